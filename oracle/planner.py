@@ -1,0 +1,411 @@
+"""Tile-size constraint checker (C0..C4) and shortlist sweep -- the oracle.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).
+
+Source: the "tile_decision.py" page (tilelang tutorial chapter 28 section 4,
+"Tile-size decision procedure"), whose module docstring lists the four
+constraints C1..C4; the "04-tile-size-decision/README.md" page, which adds the
+C0 DRAM-traffic term to the same list; and the constraint-analysis section of
+the "Tiling（分块）" page (shared-memory capacity, register pressure with an
+overhead term, occupancy).
+
+Every quantity is an integer or an exact rational (``fractions.Fraction``), so
+verdicts can be compared bit for bit with any other implementation.
+
+Two families of device model share one evaluation routine:
+
+* ``pages`` models (H100/H200 and the A100 override of the README's commands):
+  the pages' own constants and register model -- registers pooled per SM,
+  divided by registers per block -- and the pages' ranking key.
+* the ``gfx950`` model (MI355X): 256 CUs, 160 KiB LDS per CU and per
+  workgroup, wave64, 4 SIMDs per CU with a 512-entry unified VGPR file per
+  lane (256 of which can be accumulation registers), v_mfma f16/bf16 shapes.
+  The register model is per SIMD; accumulators are counted as on the pages
+  plus the fixed per-thread overhead of the Tiling page's register example;
+  the block must split into a grid of waves whose sub-tiles are whole MFMA
+  tiles; and each operand tile must be a whole number of wave-wide 16-byte
+  loads.  These additions are readings, listed with their reasons in the
+  design notes of the repository.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field, replace
+from fractions import Fraction
+from typing import List, Optional, Sequence, Tuple
+
+# ---------------------------------------------------------------------------
+# Device models
+# ---------------------------------------------------------------------------
+
+REG_POOLED = "pooled"     # regs per SM // regs per block       (tile_decision.py page)
+REG_PER_SIMD = "per_simd"  # waves per SIMD from the per-lane VGPR file (gfx950)
+
+
+@dataclass(frozen=True)
+class DeviceModel:
+    name: str
+    cores: int                      # SMs (NVIDIA) or CUs (AMD)
+    onchip_per_core: int            # shared memory / LDS bytes per SM or CU
+    onchip_per_block_max: int       # usable bytes per block (workgroup)
+    max_threads_per_core: int
+    max_threads_per_block: int
+    max_blocks_per_core: int
+    lane_count: int                 # warp (32) or wavefront (64) size
+    reg_granule_per_lane: int       # per-thread register allocation granule
+    acc_regs_max: int               # C2 cap on accumulator registers per thread
+    reg_overhead: int               # registers per thread beyond accumulators
+    reg_model: str
+    regs_per_core: int = 0          # pooled model: 32-bit registers per SM
+    simds_per_core: int = 0         # per-SIMD model
+    regs_per_lane_per_simd: int = 0  # per-SIMD model: unified VGPR file depth
+    max_waves_per_simd: int = 0     # per-SIMD model
+    instr_shapes: Tuple[Tuple[str, Tuple[int, int, int, int]], ...] = ()
+    wave_grid_rule: bool = False    # gfx950: block splits into whole MFMA tiles per wave
+    load_bytes_per_lane: int = 0    # gfx950: operand tiles are whole wave-wide loads
+    ranking: str = "pages"
+
+    def shape(self, instr: str) -> Tuple[int, int, int, int]:
+        for k, v in self.instr_shapes:
+            if k == instr:
+                return v
+        raise KeyError(f"instruction {instr!r} not known on {self.name}")
+
+
+# The pages' instruction multiples (M, N, K, threads) for the NVIDIA paths
+# (tile_decision.py page, "Instruction-shape constraints"): the warp-level mma
+# m16n8k16, the warpgroup wgmma m64nNk16 with N a multiple of 8 and 128
+# threads, and plain SIMT code.
+NVIDIA_SHAPES = (("mma", (16, 8, 16, 32)), ("simt", (1, 1, 1, 32)), ("wgmma", (64, 8, 16, 128)))
+
+# gfx950 dense f16/bf16 MFMA shapes: v_mfma_f32_32x32x16_{f16,bf16} and
+# v_mfma_f32_16x16x32_{f16,bf16}; both are issued by one 64-lane wave.
+GFX950_SHAPES = (("mfma32", (32, 32, 16, 64)), ("mfma16", (16, 16, 32, 64)))
+
+
+def device_pages(sm_count: int = 132, smem_kb: int = 228) -> DeviceModel:
+    """The H100/H200 defaults of the tile_decision.py page's Device record.
+
+    The command line of that page describes other devices only through the SM
+    count and the shared memory per SM; the per-block limit it derives is one
+    KiB less than the per-SM figure (227 KiB for the 228 KiB default).
+    """
+    return DeviceModel(
+        name="H100/H200 (sm_90)", cores=sm_count,
+        onchip_per_core=smem_kb * 1024, onchip_per_block_max=smem_kb * 1024 - 1024,
+        max_threads_per_core=2048, max_threads_per_block=1024, max_blocks_per_core=32,
+        lane_count=32, reg_granule_per_lane=256 // 32, acc_regs_max=255, reg_overhead=0,
+        reg_model=REG_POOLED, regs_per_core=65536,
+        instr_shapes=NVIDIA_SHAPES, ranking="pages")
+
+
+def device_gfx950() -> DeviceModel:
+    """MI355X (gfx950).  Values confirmed on the device through hipDeviceProp_t:
+    256 CUs, 163840 B LDS per CU and per block, 2048 threads per CU, 1024 per
+    block, 32 blocks per CU, wave64.  From the CDNA4 ISA: 4 SIMDs per CU, 8
+    waves per SIMD, a 512-deep unified VGPR file per lane with at most 256
+    accumulation registers, allocation granule 8.  The per-thread overhead of
+    32 registers is the Tiling page's register example (constraint two)."""
+    return DeviceModel(
+        name="MI355X (gfx950)", cores=256,
+        onchip_per_core=163840, onchip_per_block_max=163840,
+        max_threads_per_core=2048, max_threads_per_block=1024, max_blocks_per_core=32,
+        lane_count=64, reg_granule_per_lane=8, acc_regs_max=256, reg_overhead=32,
+        reg_model=REG_PER_SIMD, simds_per_core=4, regs_per_lane_per_simd=512,
+        max_waves_per_simd=8, instr_shapes=GFX950_SHAPES,
+        wave_grid_rule=True, load_bytes_per_lane=16, ranking="gfx950")
+
+
+# Wave grids (rows x cols of waves) a block of n waves is split into.
+WAVE_GRIDS = {1: (1, 1), 2: (1, 2), 4: (2, 2), 8: (2, 4), 16: (4, 4)}
+
+# ---------------------------------------------------------------------------
+# Records
+# ---------------------------------------------------------------------------
+
+
+@dataclass(frozen=True)
+class TileConfig:
+    block_m: int
+    block_n: int
+    block_k: int
+    stages: int = 3
+    threads: int = 128
+    instr: str = "wgmma"
+
+
+@dataclass
+class Verdict:
+    config: TileConfig
+    smem_per_stage: int = 0
+    smem_total: int = 0
+    accum_per_thread: int = 0
+    regs_per_thread: int = 0
+    regs_per_block: int = 0
+    blocks_by_regs: int = 0
+    blocks_by_smem: int = 0
+    blocks_by_threads: int = 0
+    blocks_per_core: int = 0
+    grid: int = 0
+    waves: int = 0
+    fill: Fraction = Fraction(0)
+    traffic: Fraction = Fraction(0)
+    failures: List[str] = field(default_factory=list)   # constraint codes, in check order
+    messages: List[str] = field(default_factory=list)   # human-readable FAIL text
+    warnings: List[str] = field(default_factory=list)   # C4 codes: "tail", "idle"
+    warn_text: List[str] = field(default_factory=list)
+    binding: str = ""
+
+    @property
+    def feasible(self) -> bool:
+        return not self.failures
+
+
+def _ceil_div(a: int, b: int) -> int:
+    return -(-a // b)
+
+
+# ---------------------------------------------------------------------------
+# C3, C1, C2, occupancy  (checked in this order, as the procedure prescribes:
+# the instruction shape first because it is the cheapest mistake to make)
+# ---------------------------------------------------------------------------
+
+
+def evaluate(cfg: TileConfig, dev: DeviceModel, elem_bytes: int = 2, accum_bytes: int = 4) -> Verdict:
+    v = Verdict(config=cfg)
+    bm, bn, bk, st, thr = cfg.block_m, cfg.block_n, cfg.block_k, cfg.stages, cfg.threads
+
+    # C3 -- every block dimension is a whole number of intrinsic tiles, and the
+    # thread count a whole number of the intrinsic's issuing group.
+    im, inn, ik, it = dev.shape(cfg.instr)
+    for code, dim, name, mult in (("C3_M", bm, "block_M", im), ("C3_N", bn, "block_N", inn),
+                                  ("C3_K", bk, "block_K", ik)):
+        if dim % mult:
+            v.failures.append(code)
+            v.messages.append(f"C3 {name}={dim} is not a multiple of {mult} ({cfg.instr})")
+    if thr % it:
+        v.failures.append("C3_THREADS")
+        v.messages.append(f"C3 threads={thr} is not a multiple of {it} ({cfg.instr})")
+    if thr > dev.max_threads_per_block:
+        v.failures.append("C3_MAXTHREADS")
+        v.messages.append(f"C3 threads={thr} exceeds {dev.max_threads_per_block} per block")
+    if dev.wave_grid_rule:
+        waves = thr // dev.lane_count if thr % dev.lane_count == 0 else 0
+        grid = WAVE_GRIDS.get(waves)
+        if grid is None or bm % (grid[0] * im) or bn % (grid[1] * inn):
+            v.failures.append("C3_WAVEGRID")
+            v.messages.append(f"C3 block ({bm},{bn}) does not split into whole {im}x{inn} tiles"
+                              f" over a {grid} wave grid")
+    if dev.load_bytes_per_lane:
+        unit = dev.load_bytes_per_lane * dev.lane_count
+        if (bm * bk * elem_bytes) % unit or (bk * bn * elem_bytes) % unit:
+            v.failures.append("C3_LOAD")
+            v.messages.append(f"C3 operand tiles are not whole {unit}-byte wave loads")
+
+    # C1 -- on-chip capacity: every pipeline stage holds one A tile (block_M x
+    # block_K) and one B tile (block_K x block_N).
+    v.smem_per_stage = (bm * bk + bk * bn) * elem_bytes
+    v.smem_total = v.smem_per_stage * st
+    if v.smem_total > dev.onchip_per_block_max:
+        v.failures.append("C1")
+        v.messages.append(f"C1 shared {v.smem_total} B > {dev.onchip_per_block_max} B per block"
+                          f" at stages={st}")
+
+    # C2 -- register pressure: the C tile's fp32 accumulators spread over the
+    # block's threads, rounded up to the allocation granule.
+    v.accum_per_thread = _ceil_div(bm * bn, thr)
+    raw = v.accum_per_thread * accum_bytes // 4
+    acc_regs = _ceil_div(raw, dev.reg_granule_per_lane) * dev.reg_granule_per_lane
+    v.regs_per_thread = acc_regs + dev.reg_overhead
+    if acc_regs > dev.acc_regs_max:
+        v.failures.append("C2")
+        v.messages.append(f"C2 accumulators alone need {acc_regs} registers/thread"
+                          f" (> {dev.acc_regs_max}); expect spilling to local memory")
+    v.regs_per_block = v.regs_per_thread * thr
+
+    # Occupancy: resident blocks per SM/CU allowed by registers, by on-chip
+    # memory and by threads, under the hardware block cap.
+    if dev.reg_model == REG_POOLED:
+        v.blocks_by_regs = dev.regs_per_core // max(v.regs_per_block, 1)
+    else:
+        waves_per_simd = min(dev.max_waves_per_simd, dev.regs_per_lane_per_simd // v.regs_per_thread)
+        v.blocks_by_regs = (dev.simds_per_core * waves_per_simd) // max(_ceil_div(thr, dev.lane_count), 1)
+    v.blocks_by_smem = dev.onchip_per_core // max(v.smem_total, 1)
+    v.blocks_by_threads = dev.max_threads_per_core // max(thr, 1)
+    v.blocks_per_core = max(min(v.blocks_by_regs, v.blocks_by_smem, v.blocks_by_threads,
+                                dev.max_blocks_per_core), 0)
+    if v.blocks_per_core == 0:
+        v.failures.append("OCC0")
+        v.messages.append("C1/C2 no resident block fits: blocks_per_SM = 0")
+    else:
+        # the first of (regs, smem, threads) attaining the minimum
+        pairs = (("regs", v.blocks_by_regs), ("smem", v.blocks_by_smem), ("threads", v.blocks_by_threads))
+        least = min(p[1] for p in pairs)
+        v.binding = next(name for name, val in pairs if val == least)
+    return v
+
+
+# ---------------------------------------------------------------------------
+# C4 -- parallelism: how many waves of tiles the grid takes and how full the
+# last one is.
+# ---------------------------------------------------------------------------
+
+
+def finish_parallelism(v: Verdict, m: int, n: int, dev: DeviceModel, batch: int = 1) -> Verdict:
+    cfg = v.config
+    v.grid = batch * _ceil_div(m, cfg.block_m) * _ceil_div(n, cfg.block_n)
+    resident = max(v.blocks_per_core * dev.cores, 1)
+    v.waves = _ceil_div(v.grid, resident)
+    rem = v.grid % resident
+    v.fill = Fraction(rem, resident) if rem else Fraction(1)
+    if v.waves > 1 and v.fill < Fraction(1, 2):
+        v.warnings.append("tail")
+        v.warn_text.append(f"C4 last wave only {float(v.fill) * 100:.0f}% full "
+                           f"({v.grid} tiles / {resident} resident): tail effect")
+    if v.grid < dev.cores:
+        v.warnings.append("idle")
+        v.warn_text.append(f"C4 only {v.grid} tiles for {dev.cores} SMs: more than half the machine is idle")
+    return v
+
+
+# ---------------------------------------------------------------------------
+# C0 -- DRAM traffic model: every C tile streams its A panel (block_M x K) and
+# B panel (K x block_N) once, and C is written once:
+#     b*M*N*K*(1/block_N + 1/block_M) + b*M*N,   b = bytes per element.
+# A batch of independent GEMMs multiplies the whole expression.
+# ---------------------------------------------------------------------------
+
+
+def dram_traffic(m: int, n: int, k: int, cfg: TileConfig, elem_bytes: int = 2, batch: int = 1) -> Fraction:
+    return batch * (elem_bytes * m * n * k * (Fraction(1, cfg.block_n) + Fraction(1, cfg.block_m))
+                    + elem_bytes * m * n)
+
+
+def round_half_even(x: Fraction) -> int:
+    fl = math.floor(x)
+    diff = x - fl
+    if diff > Fraction(1, 2):
+        return fl + 1
+    if diff < Fraction(1, 2):
+        return fl
+    return fl if fl % 2 == 0 else fl + 1
+
+
+# ---------------------------------------------------------------------------
+# Sweep
+# ---------------------------------------------------------------------------
+
+PAGES_SPACE = dict(bm=(16, 32, 64, 128, 256), bn=(16, 32, 64, 128, 256), bk=(16, 32, 64, 128),
+                   stages=(2, 3, 4), threads=(128, 256, 512))
+GFX950_SPACE = dict(bm=(64, 128, 256), bn=(64, 128, 256), bk=(16, 32, 64),
+                    stages=(2, 3, 4), threads=(128, 256, 512))
+
+
+def rank_key(v: Verdict, dev: DeviceModel):
+    """Order of preference among feasible candidates.
+
+    pages: least modelled DRAM traffic, then most resident blocks, then least
+    shared memory (the tile_decision.py page's shortlist order).
+    gfx950: candidates without a C4 warning first; then least traffic and most
+    resident blocks as on the pages; then, as the Tiling page's rules of thumb
+    advise when on-chip memory has room, the larger block_K and the deeper
+    pipeline; then fewer threads and less LDS.
+    """
+    t = round_half_even(v.traffic)
+    if dev.ranking == "pages":
+        return (t, -v.blocks_per_core, v.smem_total)
+    c = v.config
+    return (1 if v.warnings else 0, t, -v.blocks_per_core, -c.block_k, -c.stages, c.threads, v.smem_total)
+
+
+def candidates(dev: DeviceModel, k: int, instrs: Sequence[str]):
+    space = PAGES_SPACE if dev.ranking == "pages" else GFX950_SPACE
+    for instr in instrs:
+        it = dev.shape(instr)[3]
+        for bm in space["bm"]:
+            for bn in space["bn"]:
+                for bk in space["bk"]:
+                    if bk > k:
+                        continue
+                    for st in space["stages"]:
+                        for thr in space["threads"]:
+                            if thr % it:
+                                continue
+                            yield TileConfig(bm, bn, bk, st, thr, instr)
+
+
+def sweep(m: int, n: int, k: int, dev: DeviceModel, instrs: Sequence[str], batch: int = 1,
+          elem_bytes: int = 2) -> List[Verdict]:
+    """All feasible candidates in preference order (a stable sort over the
+    enumeration order block_M, block_N, block_K, stages, threads, with the
+    instruction shape outermost)."""
+    out = []
+    for cfg in candidates(dev, k, instrs):
+        v = evaluate(cfg, dev, elem_bytes=elem_bytes)
+        if not v.feasible:
+            continue
+        finish_parallelism(v, m, n, dev, batch)
+        v.traffic = dram_traffic(m, n, k, cfg, elem_bytes, batch)
+        out.append(v)
+    out.sort(key=lambda x: rank_key(x, dev))
+    return out
+
+
+def plan(m: int, n: int, k: int, dev: Optional[DeviceModel] = None, batch: int = 1,
+         elem_bytes: int = 2, instrs: Optional[Sequence[str]] = None) -> Tuple[Optional[Verdict], int]:
+    dev = dev or device_gfx950()
+    instrs = instrs or [s for s, _ in dev.instr_shapes]
+    res = sweep(m, n, k, dev, instrs, batch, elem_bytes)
+    return (res[0] if res else None), len(res)
+
+
+# ---------------------------------------------------------------------------
+# Text report in the pages' format (used to compare with their printed output)
+# ---------------------------------------------------------------------------
+
+
+def sweep_rows(results: Sequence[Verdict], topk: int) -> List[str]:
+    rows = []
+    for v in results[:topk]:
+        c = v.config
+        rows.append(" ".join([str(c.block_m), str(c.block_n), str(c.block_k), str(c.stages), str(c.threads),
+                              f"{float(v.traffic) / 1e6:.1f}", f"{v.smem_total / 1024:.1f}",
+                              str(v.regs_per_thread), str(v.blocks_per_core), str(v.waves),
+                              f"{float(v.fill) * 100:.0f}%", v.binding]))
+    return rows
+
+
+def sweep_summary(results: Sequence[Verdict]) -> dict:
+    best = round_half_even(results[0].traffic) if results else 0
+    tied = sum(1 for v in results if round_half_even(v.traffic) == best)
+    best_fill = max((v.fill for v in results), default=Fraction(0))
+    return {"feasible": len(results), "tied": tied, "best_fill_pct": f"{float(best_fill) * 100:.0f}%"}
+
+
+def diagnose_lines(v: Verdict) -> List[str]:
+    c = v.config
+    lines = [
+        f"C1 shared/stage {v.smem_per_stage / 1024:.1f} KB -> total {v.smem_total / 1024:.1f} KB",
+        f"C2 accumulators {v.accum_per_thread}/thread -> {v.regs_per_thread} regs/thread (warp-rounded),"
+        f" {v.regs_per_block} regs/block",
+        f"occupancy: regs -> {v.blocks_by_regs} blk/SM, smem -> {v.blocks_by_smem},"
+        f" threads -> {v.blocks_by_threads} => {v.blocks_per_core} blk/SM",
+        f"C4 grid {v.grid} tiles -> {v.waves} wave(s), last wave {float(v.fill) * 100:.1f}% full",
+    ]
+    lines += [f"FAIL {m}" for m in v.messages]
+    lines += [f"warn {w}" for w in v.warn_text]
+    if v.feasible:
+        lines.append("OK all four constraints satisfied")
+    return lines
+
+
+def diagnose(cfg: TileConfig, dev: DeviceModel, m: int, n: int, batch: int = 1) -> Verdict:
+    v = evaluate(cfg, dev)
+    finish_parallelism(v, m, n, dev, batch)
+    return v
+
+
+__all__ = ["DeviceModel", "TileConfig", "Verdict", "device_pages", "device_gfx950", "evaluate",
+           "finish_parallelism", "dram_traffic", "round_half_even", "sweep", "plan", "rank_key",
+           "sweep_rows", "sweep_summary", "diagnose_lines", "diagnose", "candidates", "WAVE_GRIDS",
+           "replace"]

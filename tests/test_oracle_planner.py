@@ -1,0 +1,180 @@
+"""Pins of the planner oracle (C0..C4, sweep) to what the pages fix.
+
+Pages-mode must reproduce the output the README page prints for its own
+commands; the gfx950 model is pinned with closed forms worked by hand.
+"""
+import os
+from fractions import Fraction
+
+import pytest
+
+from oracle import planner as P
+from oracle import intensity as I
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _lines(name):
+    with open(os.path.join(GOLD, name), encoding="utf-8") as f:
+        return [l.rstrip("\n") for l in f if l.strip() and not l.startswith("#")]
+
+
+def test_pages_sweep_matches_readme_printout():
+    gold = _lines("readme_sweep_topk8.txt")
+    dev = P.device_pages()
+    res = P.sweep(4096, 4096, 4096, dev, ["wgmma"])
+    summ = P.sweep_summary(res)
+    rows = P.sweep_rows(res, 8)
+    want_rows = [l.split()[1:] for l in gold if l.startswith("row ")]
+    for i, w in enumerate(want_rows):
+        assert rows[i].split() == w
+    for l in gold:
+        key, *val = l.split()
+        if key == "feasible":
+            assert summ["feasible"] == int(val[0])
+        elif key == "tied":
+            assert summ["tied"] == int(val[0])
+        elif key == "best_fill":
+            assert summ["best_fill_pct"] == val[0]
+
+
+def test_pages_diagnose_overbudget_matches_readme_printout():
+    gold = _lines("readme_diagnose_overbudget.txt")
+    v = P.diagnose(P.TileConfig(256, 256, 64, 4, 256, "wgmma"), P.device_pages(), 4096, 4096)
+    got = P.diagnose_lines(v)
+    assert got[0].split() == gold[0].split()
+    assert got[1].split() == gold[1].split()
+    assert got[2].split() == gold[2].split()
+    fails = [l for l in got if l.startswith("FAIL")]
+    assert [f.split() for f in fails] == [g.split() for g in gold if g.startswith("FAIL")]
+    assert v.failures == ["C1", "C2", "OCC0"]
+    # blocks/SM = 0 leaves one resident slot, so every tile is its own wave
+    assert (v.grid, v.waves, v.fill) == (256, 256, Fraction(1))
+
+
+def test_pages_other_commands_cross_checked():
+    """Outputs of the README's other commands, not printed on the pages: they
+    were obtained by executing the tile_decision.py page's listing as printed
+    (an implementation independent of this oracle)."""
+    dev = P.device_pages()
+    v = P.diagnose(P.TileConfig(128, 256, 64, 3, 256, "wgmma"), dev, 4096, 4096)
+    assert v.feasible and v.binding == "smem"
+    assert (v.smem_per_stage, v.smem_total, v.regs_per_thread, v.regs_per_block) == (49152, 147456, 128, 32768)
+    assert (v.blocks_by_regs, v.blocks_by_smem, v.blocks_by_threads, v.blocks_per_core) == (2, 1, 8, 1)
+    assert (v.grid, v.waves, f"{float(v.fill) * 100:.1f}") == (512, 4, "87.9")
+    s = P.sweep_summary(P.sweep(4096, 4096, 4096, dev, ["mma"]))
+    assert (s["feasible"], s["tied"], s["best_fill_pct"]) == (813, 8, "94%")
+    a100 = P.device_pages(sm_count=108, smem_kb=164)
+    res = P.sweep(4096, 4096, 4096, a100, ["wgmma"])
+    s = P.sweep_summary(res)
+    assert (s["feasible"], s["tied"], s["best_fill_pct"]) == (435, 7, "96%")
+    assert (res[0].waves, f"{float(res[0].fill) * 100:.0f}%") == (3, "37%")
+
+
+def test_tiling_page_constraint_examples():
+    """Constraint analysis of the Tiling page: shared-memory bytes per config
+    and the A100 block count; the register estimate with its overhead."""
+    for l in _lines("tiling_numbers.txt"):
+        key, *v = l.split()
+        if key == "smem":
+            bm, bn, bk, eb, st, want = map(int, v)
+            ver = P.evaluate(P.TileConfig(bm, bn, bk, st, 256, "mma"), P.device_pages(), elem_bytes=eb)
+            assert ver.smem_total == want
+        elif key == "smem_blocks_a100":
+            kb, tile_kb, want = map(int, v)
+            assert kb // tile_kb == want
+            a100 = P.device_pages(sm_count=108, smem_kb=164)
+            big = P.evaluate(P.TileConfig(256, 256, 64, 3, 256, "mma"), a100)
+            assert "C1" in big.failures           # 192 KB does not fit 164 KB
+        elif key == "regs":
+            bm, bn, thr, overhead, want = map(int, v)
+            g = P.device_gfx950()
+            assert g.reg_overhead == overhead
+            assert -(-bm * bn // thr) + overhead == want
+
+
+def test_traffic_closed_forms():
+    c = P.TileConfig(256, 256, 16, 2, 512, "wgmma")
+    assert P.dram_traffic(4096, 4096, 4096, c) == 2 * 4096 ** 3 * Fraction(2, 256) + 2 * 4096 ** 2
+    assert P.round_half_even(P.dram_traffic(4096, 4096, 4096, c)) == 1107296256
+    c128 = P.TileConfig(128, 128, 32, 2, 256, "mfma32")
+    t = P.dram_traffic(4096, 4096, 4096, c128)
+    assert t == 2181038080
+    # link to the Tiling page's intensity: without the C write, 2MNK / traffic
+    # is the tiled intensity 2*BM*BN/((BM+BN)*elem_bytes) = 64 FLOP/B
+    assert Fraction(2 * 4096 ** 3) / (t - 2 * 4096 ** 2) == I.intensity_tiled(128, 128, 4096) == 64
+    # a batch multiplies the whole expression
+    c64 = P.TileConfig(64, 256, 32, 2, 256, "mfma32")
+    assert P.dram_traffic(3000, 5000, 2048, c64, batch=4) == 4 * P.dram_traffic(3000, 5000, 2048, c64)
+    assert P.round_half_even(Fraction(5, 2)) == 2 and P.round_half_even(Fraction(7, 2)) == 4
+    assert P.round_half_even(Fraction(-5, 2)) == -2 and P.round_half_even(Fraction(11, 4)) == 3
+
+
+def test_grid_is_not_symmetric_in_block_dims():
+    g = P.device_gfx950()
+    v = P.finish_parallelism(P.evaluate(P.TileConfig(64, 256, 32, 2, 256, "mfma32"), g), 3000, 5000, g, batch=4)
+    assert v.grid == 4 * 47 * 20
+    v2 = P.finish_parallelism(P.evaluate(P.TileConfig(256, 64, 32, 2, 256, "mfma32"), g), 3000, 5000, g, batch=4)
+    assert v2.grid == 4 * 12 * 79
+
+
+def test_gfx950_closed_forms():
+    g = P.device_gfx950()
+    v = P.evaluate(P.TileConfig(256, 256, 64, 2, 256, "mfma32"), g)
+    assert v.feasible and v.smem_total == 131072 and v.accum_per_thread == 256
+    assert v.regs_per_thread == 288                      # 256 accumulators + 32 overhead
+    assert v.blocks_by_regs == 1                         # floor(512/288) = 1 wave/SIMD, 4 waves/block
+    assert v.blocks_by_smem == 1 and v.blocks_by_threads == 8 and v.blocks_per_core == 1
+    assert v.binding == "regs"
+    v = P.evaluate(P.TileConfig(256, 256, 64, 3, 256, "mfma32"), g)
+    assert v.failures == ["C1", "OCC0"] and v.smem_total == 196608   # no block fits either
+    v = P.evaluate(P.TileConfig(256, 256, 32, 2, 128, "mfma32"), g)
+    assert "C2" in v.failures and v.accum_per_thread == 512
+    v = P.evaluate(P.TileConfig(256, 256, 32, 2, 512, "mfma32"), g)
+    assert v.regs_per_thread == 160 and v.blocks_by_regs == (4 * (512 // 160)) // 8 == 1
+    v = P.evaluate(P.TileConfig(64, 64, 32, 2, 256, "mfma32"), g)
+    assert v.accum_per_thread == 16 and v.regs_per_thread == 48
+    assert v.blocks_by_regs == (4 * 8) // 4 == 8 and v.blocks_by_smem == 163840 // 16384 == 10
+    assert v.blocks_by_threads == 8 and v.binding == "regs"
+    # wave grid: 8 waves split 2 x 4; a 64-wide block cannot hold 4 columns of 32-wide MFMA tiles
+    assert "C3_WAVEGRID" in P.evaluate(P.TileConfig(64, 64, 32, 2, 512, "mfma32"), g).failures
+    assert P.evaluate(P.TileConfig(64, 64, 32, 2, 512, "mfma16"), g).feasible
+    # mfma16 needs block_K a multiple of 32
+    assert P.evaluate(P.TileConfig(128, 128, 16, 2, 256, "mfma16"), g).failures == ["C3_K"]
+    # C4 at the headline shape: 256 tiles of 256x256 on 256 CUs, one full wave
+    v = P.finish_parallelism(P.evaluate(P.TileConfig(256, 256, 64, 2, 256, "mfma32"), g), 4096, 4096, g)
+    assert (v.grid, v.waves, v.fill, v.warnings) == (256, 1, Fraction(1), [])
+    v = P.finish_parallelism(P.evaluate(P.TileConfig(128, 128, 64, 2, 256, "mfma32"), g), 6272, 256, g)
+    assert v.grid == 98 and v.warnings == ["idle"]
+
+
+def test_tail_warning_threshold_exact():
+    g = P.device_gfx950()
+    v = P.evaluate(P.TileConfig(256, 256, 64, 2, 256, "mfma32"), g)    # 1 block/CU -> 256 resident
+    P.finish_parallelism(v, 256 * 16, 256 * 24, g)                  # 384 tiles: fill 128/256 = 1/2 -> no warn
+    assert v.waves == 2 and v.fill == Fraction(1, 2) and v.warnings == []
+    v = P.evaluate(P.TileConfig(256, 256, 64, 2, 256, "mfma32"), g)
+    P.finish_parallelism(v, 256 * 1, 256 * 383, g)                  # 383 tiles: fill 127/256 -> tail
+    assert v.warnings == ["tail"]
+
+
+def test_sweep_is_stable_and_sorted():
+    g = P.device_gfx950()
+    res = P.sweep(4096, 4096, 4096, g, ["mfma32", "mfma16"])
+    keys = [P.rank_key(v, g) for v in res]
+    assert keys == sorted(keys)
+    order = {c: i for i, c in enumerate(P.candidates(g, 4096, ["mfma32", "mfma16"]))}
+    for a, b in zip(res, res[1:]):
+        if P.rank_key(a, g) == P.rank_key(b, g):
+            assert order[a.config] < order[b.config]
+    best = res[0].config
+    assert (best.block_m, best.block_n) == (256, 256)
+    # every feasible candidate was kept and nothing infeasible slipped in
+    n_feasible = sum(1 for c in P.candidates(g, 4096, ["mfma32", "mfma16"]) if P.evaluate(c, g).feasible)
+    assert n_feasible == len(res)
+
+
+def test_bk_larger_than_k_is_skipped():
+    g = P.device_gfx950()
+    res = P.sweep(64, 64, 32, g, ["mfma32"])
+    assert res and all(v.config.block_k <= 32 for v in res)
