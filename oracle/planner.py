@@ -23,9 +23,9 @@ Two families of device model share one evaluation routine:
   The register model is per SIMD; accumulators are counted as on the pages
   plus the fixed per-thread overhead of the Tiling page's register example;
   the block must split into a grid of waves whose sub-tiles are whole MFMA
-  tiles; and each operand tile must be a whole number of wave-wide 16-byte
-  loads.  These additions are readings, listed with their reasons in the
-  design notes of the repository.
+  tiles; and each operand tile must split into the same whole number of
+  wave-wide 16-byte-per-lane loads for every wave.  These additions are
+  readings, listed with their reasons in the design notes of the repository.
 """
 from __future__ import annotations
 
@@ -197,10 +197,13 @@ def evaluate(cfg: TileConfig, dev: DeviceModel, elem_bytes: int = 2, accum_bytes
             v.messages.append(f"C3 block ({bm},{bn}) does not split into whole {im}x{inn} tiles"
                               f" over a {grid} wave grid")
     if dev.load_bytes_per_lane:
-        unit = dev.load_bytes_per_lane * dev.lane_count
+        # every wave of the block copies the same whole number of wave-wide
+        # loads (load_bytes_per_lane per lane) of each operand tile per stage
+        waves = max(thr // dev.lane_count, 1)
+        unit = dev.load_bytes_per_lane * dev.lane_count * waves
         if (bm * bk * elem_bytes) % unit or (bk * bn * elem_bytes) % unit:
             v.failures.append("C3_LOAD")
-            v.messages.append(f"C3 operand tiles are not whole {unit}-byte wave loads")
+            v.messages.append(f"C3 operand tiles are not whole {unit}-byte block loads")
 
     # C1 -- on-chip capacity: every pipeline stage holds one A tile (block_M x
     # block_K) and one B tile (block_K x block_N).

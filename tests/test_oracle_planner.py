@@ -138,7 +138,7 @@ def test_gfx950_closed_forms():
     assert v.blocks_by_threads == 8 and v.binding == "regs"
     # wave grid: 8 waves split 2 x 4; a 64-wide block cannot hold 4 columns of 32-wide MFMA tiles
     assert "C3_WAVEGRID" in P.evaluate(P.TileConfig(64, 64, 32, 2, 512, "mfma32"), g).failures
-    assert P.evaluate(P.TileConfig(64, 64, 32, 2, 512, "mfma16"), g).feasible
+    assert P.evaluate(P.TileConfig(64, 64, 64, 2, 512, "mfma16"), g).feasible
     # mfma16 needs block_K a multiple of 32
     assert P.evaluate(P.TileConfig(128, 128, 16, 2, 256, "mfma16"), g).failures == ["C3_K"]
     # C4 at the headline shape: 256 tiles of 256x256 on 256 CUs, one full wave
@@ -178,3 +178,13 @@ def test_bk_larger_than_k_is_skipped():
     g = P.device_gfx950()
     res = P.sweep(64, 64, 32, g, ["mfma32"])
     assert res and all(v.config.block_k <= 32 for v in res)
+
+
+def test_gfx950_load_rule_per_wave():
+    """64x64x16 fp16: each operand tile is 2 KiB = two 1 KiB wave loads, so a
+    block of 2 waves passes and a block of 4 waves (0.5 load each) fails."""
+    g = P.device_gfx950()
+    assert "C3_LOAD" not in P.evaluate(P.TileConfig(64, 64, 16, 2, 128, "mfma32"), g).failures
+    assert "C3_LOAD" in P.evaluate(P.TileConfig(64, 64, 16, 2, 256, "mfma32"), g).failures
+    assert "C3_LOAD" not in P.evaluate(P.TileConfig(64, 64, 32, 2, 256, "mfma32"), g).failures
+    assert "C3_LOAD" in P.evaluate(P.TileConfig(64, 128, 16, 2, 512, "mfma16"), g).failures
