@@ -1,0 +1,239 @@
+/*
+ * tss.h -- C ABI of the tile-size-selected GEMM / convolution library for
+ * MI355X (gfx950), libtss.so.
+ *
+ * Three families of entry points:
+ *
+ *  1. The tile planner (host only, no GPU needed): the constraint check of the
+ *     "tile_decision.py" page (tilelang tutorial ch. 28 sec. 4) -- C3
+ *     instruction shape, C1 on-chip capacity, C2 register pressure, occupancy,
+ *     C4 parallelism -- and the C0 DRAM-traffic model of the
+ *     "04-tile-size-decision/README.md" page, evaluated on a device
+ *     description, plus the sweep that ranks every candidate.
+ *  2. The H-tile slice formulas of the "Tiling（分块）" page (section on the
+ *     general H/W tiling formulas).
+ *  3. The device operations: a tiled fp16/bf16 GEMM with fp32 accumulation,
+ *     and a convolution computed as an implicit GEMM over H-tiles with halo
+ *     (block -> wave -> MFMA tiling as in the Tiling page's multi-level
+ *     tiling section).
+ *
+ * Conventions for every function:
+ *  - Return value: a tss_status (0 = TSS_OK, negative = error).  No function
+ *    throws, aborts or prints.  Arguments are validated before any launch;
+ *    on error nothing is launched and output buffers are untouched.
+ *  - Device operations are asynchronous on the given stream (a hipStream_t
+ *    passed as void*, NULL = the null stream) and allocate nothing: the
+ *    caller owns every buffer and keeps it alive until the stream reaches
+ *    the work.
+ *  - Device buffers are dense, row-major, 16-byte aligned.
+ *  - Thread safety: every function may be called concurrently.
+ */
+#ifndef TSS_H_
+#define TSS_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes -------------------------------------------------------- */
+enum {
+  TSS_OK = 0,
+  TSS_E_ARG = -1,          /* null pointer, negative or oversized dimension, bad enum */
+  TSS_E_DTYPE = -2,        /* unsupported input / output dtype combination */
+  TSS_E_ALIGN = -3,        /* pointer or row stride not 16-byte aligned */
+  TSS_E_INFEASIBLE = -4,   /* the tile config fails C1..C3 or fits no block on a CU */
+  TSS_E_HIP = -5,          /* HIP runtime error (launch, device query) */
+  TSS_E_UNSUPPORTED = -6   /* feasible config with no compiled kernel */
+};
+
+/* ---- element types ------------------------------------------------------- */
+enum { TSS_F16 = 1, TSS_BF16 = 2, TSS_F32 = 3 };
+
+/* ---- instruction shapes (C3) -------------------------------------------- */
+enum {
+  TSS_INSTR_MFMA32 = 1,    /* v_mfma_f32_32x32x16_{f16,bf16}: multiples (32, 32, 16), 64 lanes */
+  TSS_INSTR_MFMA16 = 2,    /* v_mfma_f32_16x16x32_{f16,bf16}: multiples (16, 16, 32), 64 lanes */
+  /* The NVIDIA shapes of the tile_decision.py page, for the pages' own
+     device model only (no kernels): */
+  TSS_INSTR_NV_MMA = 16,   /* mma m16n8k16: (16, 8, 16), 32 threads */
+  TSS_INSTR_NV_WGMMA = 17, /* wgmma m64nNk16: (64, 8, 16), 128 threads */
+  TSS_INSTR_NV_SIMT = 18   /* (1, 1, 1), 32 threads */
+};
+
+enum { TSS_REG_POOLED = 0, TSS_REG_PER_SIMD = 1 };
+enum { TSS_RANK_PAGES = 0, TSS_RANK_GFX950 = 1 };
+
+/*
+ * Device description used by the planner.  Two register models:
+ *  POOLED   (the tile_decision.py page): blocks by registers =
+ *           regs_per_core / (regs_per_thread * threads).
+ *  PER_SIMD (gfx950): waves per SIMD = min(max_waves_per_simd,
+ *           regs_per_lane_per_simd / regs_per_thread); blocks by registers =
+ *           simds_per_core * waves per SIMD / waves per block.
+ * regs_per_thread = ceil(accumulators * 4 B / 4 B / granule) * granule +
+ * reg_overhead; C2 fails when the accumulator registers exceed acc_regs_max.
+ */
+typedef struct {
+  int32_t cores;                  /* SMs or CUs */
+  int32_t onchip_per_core;        /* shared memory / LDS bytes per SM or CU */
+  int32_t onchip_per_block_max;   /* usable bytes per block */
+  int32_t max_threads_per_core;
+  int32_t max_threads_per_block;
+  int32_t max_blocks_per_core;
+  int32_t lane_count;             /* warp or wavefront size */
+  int32_t reg_granule_per_lane;
+  int32_t acc_regs_max;
+  int32_t reg_overhead;
+  int32_t reg_model;              /* TSS_REG_* */
+  int32_t regs_per_core;          /* POOLED only */
+  int32_t simds_per_core;         /* PER_SIMD only */
+  int32_t regs_per_lane_per_simd; /* PER_SIMD only */
+  int32_t max_waves_per_simd;     /* PER_SIMD only */
+  int32_t wave_grid_rule;         /* 1: block must split into whole MFMA tiles per wave */
+  int32_t load_bytes_per_lane;    /* >0: each wave issues whole 64-lane loads per stage */
+  int32_t ranking;                /* TSS_RANK_* */
+} tss_device;
+
+/* One tile configuration (block tile BM x BN, K step BK, pipeline stages,
+   threads per block, instruction shape). */
+typedef struct {
+  int32_t bm, bn, bk, stages, threads, instr;
+} tss_tile_config;
+
+/* failure bits, in the order the constraints are checked */
+enum {
+  TSS_FAIL_C3_M = 1 << 0, TSS_FAIL_C3_N = 1 << 1, TSS_FAIL_C3_K = 1 << 2,
+  TSS_FAIL_C3_THREADS = 1 << 3, TSS_FAIL_C3_MAXTHREADS = 1 << 4,
+  TSS_FAIL_C3_WAVEGRID = 1 << 5, TSS_FAIL_C3_LOAD = 1 << 6,
+  TSS_FAIL_C1 = 1 << 7, TSS_FAIL_C2 = 1 << 8, TSS_FAIL_OCC0 = 1 << 9
+};
+enum { TSS_WARN_TAIL = 1, TSS_WARN_IDLE = 2 };
+enum { TSS_BIND_NONE = 0, TSS_BIND_REGS = 1, TSS_BIND_SMEM = 2, TSS_BIND_THREADS = 3 };
+
+/*
+ * Verdict on one configuration for one problem.  All figures are exact:
+ * last-wave fill = fill_num / fill_den; C0 traffic in bytes =
+ * (traffic_num_hi * 2^64 + traffic_num_lo) / traffic_den in lowest terms,
+ * traffic_rounded its round-half-to-even integer value.
+ */
+typedef struct {
+  tss_tile_config cfg;
+  int64_t smem_per_stage, smem_total;
+  int64_t accum_per_thread, regs_per_thread, regs_per_block;
+  int64_t blocks_by_regs, blocks_by_smem, blocks_by_threads, blocks_per_core;
+  int64_t grid, waves, fill_num, fill_den;
+  uint64_t traffic_num_hi, traffic_num_lo, traffic_den, traffic_rounded;
+  uint32_t failures;   /* TSS_FAIL_* bits; 0 = feasible */
+  uint32_t warnings;   /* TSS_WARN_* bits (C4) */
+  int32_t binding;     /* TSS_BIND_*: the first of regs, smem, threads at the minimum */
+  int32_t pad_;
+} tss_verdict;
+
+/* The MI355X (gfx950) model: 256 CUs, 160 KiB LDS per CU and per block,
+   wave64, 4 SIMDs x 8 waves, 512-deep unified VGPR file (256 accumulation
+   registers), 32 blocks per CU.  out: non-null. */
+int32_t tss_device_gfx950(tss_device *out);
+
+/* The tile_decision.py page's device model (H100/H200 defaults: sm_count
+   132, smem_kb 228; the per-block limit is smem_kb KiB minus 1 KiB).
+   sm_count, smem_kb > 0. */
+int32_t tss_device_pages(int32_t sm_count, int32_t smem_kb, tss_device *out);
+
+/* The gfx950 model with the CU count and LDS sizes read from HIP device
+   hip_device.  Needs a GPU; TSS_E_HIP otherwise. */
+int32_t tss_device_query(int32_t hip_device, tss_device *out);
+
+/*
+ * C3, C1, C2, occupancy, C4 and C0 for cfg on dev, for a batch of M x N x K
+ * GEMMs whose operands take elem_bytes per element.  dev NULL = gfx950.
+ * Infeasibility is reported in out->failures, not as an error.
+ * Errors: TSS_E_ARG (null cfg/out, dimensions < 0 or batch < 1, elem_bytes
+ * not 1..8, non-positive config fields, unknown instr for the device).
+ */
+int32_t tss_evaluate(const tss_tile_config *cfg, const tss_device *dev, int64_t batch, int64_t M,
+                     int64_t N, int64_t K, int32_t elem_bytes, tss_verdict *out);
+
+/*
+ * Sweep every candidate of the device's space, keep the feasible ones and
+ * rank them (stable over the enumeration order instr, BM, BN, BK, stages,
+ * threads).  Candidates with BK > K are skipped, unless K is below the
+ * smallest BK of the space, in which case that smallest BK is kept.
+ *   pages model : BM, BN in {16..256}, BK in {16..128}, stages 2..4,
+ *                 threads {128, 256, 512}, instr fixed by *instr_filter;
+ *                 key (round(traffic), -blocks/SM, shared memory).
+ *   gfx950 model: BM, BN in {64, 128, 256}, BK in {16, 32, 64}, stages 2..4,
+ *                 threads {128, 256, 512}, both MFMA shapes (or the one in
+ *                 instr_filter); key (C4 warning?, round(traffic), -blocks/CU,
+ *                 -BK, -stages, threads, LDS bytes).
+ * instr_filter: 0 = every shape of the device, else one TSS_INSTR_*.
+ * best (nullable) receives the top verdict; list (nullable) the first
+ * min(cap, n) verdicts in rank order; *n_feasible (nullable) the count.
+ * Returns TSS_E_INFEASIBLE when nothing is feasible (best then untouched).
+ */
+int32_t tss_tile_plan(int64_t batch, int64_t M, int64_t N, int64_t K, int32_t elem_bytes,
+                      const tss_device *dev, int32_t instr_filter, tss_verdict *best,
+                      tss_verdict *list, int32_t cap, int32_t *n_feasible);
+
+/* One H-tile of a convolution ("Tiling（分块）" page, H/W tiling formulas):
+   output rows [o0, o1) need input rows [in_start, in_end) (in_end exclusive,
+   may exceed H), sub-operator pads pt' (top) and pb' (bottom), and share
+   halo rows with the next tile. */
+typedef struct {
+  int64_t o0, o1, in_start, in_end, in_span, pt, pb, halo;
+} tss_hw_slice;
+
+/* H > 0, kh > 0, sh > 0, pt >= 0, d > 0, 0 <= o0 < o1.  TSS_E_ARG otherwise. */
+int32_t tss_hw_tile(int64_t H, int64_t kh, int64_t sh, int64_t pt, int64_t d, int64_t o0,
+                    int64_t o1, tss_hw_slice *out);
+
+/*
+ * C[b] = A[b] x B[b] for b < batch: A is M x K, B is K x N, C is M x N, all
+ * row-major and batch-major (A[b][M][K], B[b][K][N], C[b][M][N]).
+ * dtype: TSS_F16 or TSS_BF16 (A and B); fp32 accumulation; out_dtype
+ * TSS_F32, or the input dtype (rounded to nearest even).
+ * cfg: the tile configuration to use, or NULL to take the planner's choice
+ * (tss_tile_plan on the gfx950 model, cached per shape).
+ * Requirements: batch >= 1, M, N, K >= 0; K and N multiples of 8 (16-byte
+ * rows); A, B, C 16-byte aligned; each operand slice below 2 GiB.
+ * M == 0 or N == 0: nothing to do.  K == 0: C is zero-filled (A and B may
+ * then be NULL).
+ * Errors: TSS_E_ARG, TSS_E_DTYPE, TSS_E_ALIGN, TSS_E_INFEASIBLE (cfg fails
+ * C1..C3), TSS_E_UNSUPPORTED (no compiled kernel for cfg), TSS_E_HIP.
+ */
+int32_t tss_gemm(int64_t M, int64_t N, int64_t K, int32_t dtype, const void *A, const void *B,
+                 void *C, int64_t batch, int32_t out_dtype, const tss_tile_config *cfg,
+                 void *stream);
+
+/*
+ * 2-D convolution, NCHW input x[N][C][H][W], OIHW weights w[Cout][C][kh][kw],
+ * output y[N][Cout][OH][OW] with OH = (H + 2ph - (kh-1)dh - 1)/sh + 1 and OW
+ * likewise, computed as an implicit GEMM (M = Cout, N = pixels, K = C*kh*kw)
+ * over output-row tiles of tile_oh rows.  Each H-tile reads exactly its
+ * input slice [in_start, min(in_end, H)) with the sub-operator pads of the
+ * Tiling page's formulas (tss_hw_tile); the batch never crosses a tile.
+ * dtype TSS_F16 / TSS_BF16, fp32 accumulation, out_dtype TSS_F32 or dtype.
+ * tile_oh in [1, OH]; cfg NULL = planner's choice for the GEMM
+ * (Cout x N*OH*OW x C*kh*kw).  Requirements: C*kh*kw a multiple of 8;
+ * x, w, y 16-byte aligned.  Errors as tss_gemm.
+ */
+int32_t tss_conv2d(int64_t N, int64_t C, int64_t H, int64_t W, int64_t Cout, int64_t kh,
+                   int64_t kw, int64_t sh, int64_t sw, int64_t ph, int64_t pw, int64_t dh,
+                   int64_t dw, int64_t tile_oh, int32_t dtype, int32_t out_dtype, const void *x,
+                   const void *w, void *y, const tss_tile_config *cfg, void *stream);
+
+/* 1 if a kernel is compiled for cfg and dtype (op 0 = GEMM, 1 = conv), else 0. */
+int32_t tss_kernel_available(const tss_tile_config *cfg, int32_t dtype, int32_t op);
+
+/* The configuration tss_gemm / tss_conv2d would take for a NULL cfg. */
+int32_t tss_gemm_default_config(int64_t batch, int64_t M, int64_t N, int64_t K, int32_t dtype,
+                                tss_tile_config *out);
+
+/* Static text for a status code (never NULL). */
+const char *tss_status_string(int32_t status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* TSS_H_ */

@@ -323,12 +323,15 @@ def rank_key(v: Verdict, dev: DeviceModel):
 
 def candidates(dev: DeviceModel, k: int, instrs: Sequence[str]):
     space = PAGES_SPACE if dev.ranking == "pages" else GFX950_SPACE
+    # a K step longer than K is skipped -- unless K is shorter than every
+    # candidate step, when the shortest one is kept (its tail is masked)
+    bk_cap = max(k, min(space["bk"]))
     for instr in instrs:
         it = dev.shape(instr)[3]
         for bm in space["bm"]:
             for bn in space["bn"]:
                 for bk in space["bk"]:
-                    if bk > k:
+                    if bk > bk_cap:
                         continue
                     for st in space["stages"]:
                         for thr in space["threads"]:

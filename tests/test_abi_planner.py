@@ -1,0 +1,189 @@
+"""C ABI checks that need no GPU: the library loads and exports every entry
+point declared in include/tss.h; the C++ planner agrees bit for bit with the
+oracle; the H-tile formulas agree; argument errors are reported before any
+device work."""
+import ctypes
+import itertools
+import os
+import re
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+from oracle import htile as OH
+from oracle import planner as OP
+import tile_size_selection_amd as tss
+from tile_size_selection_amd import _capi as C
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_library_exports_every_declared_symbol():
+    with open(os.path.join(ROOT, "include", "tss.h")) as f:
+        hdr = f.read()
+    declared = set(re.findall(r"^(?:int32_t|const char \*)\s*(tss_\w+)\(", hdr, flags=re.M))
+    assert declared == set(C.EXPORTS)
+    L = C.lib()
+    for name in declared:
+        assert hasattr(L, name), name
+
+
+def _oracle_dev(dev_c, name):
+    if name == "gfx950":
+        return OP.device_gfx950()
+    sm, kb = name
+    return OP.device_pages(sm, kb)
+
+
+def _same(v_c: dict, v_o: OP.Verdict, name_map=None):
+    c = v_c["config"]
+    o = v_o.config
+    assert (c.bm, c.bn, c.bk, c.stages, c.threads, c.instr) == \
+        (o.block_m, o.block_n, o.block_k, o.stages, o.threads, o.instr)
+    assert v_c["smem_per_stage"] == v_o.smem_per_stage and v_c["smem_total"] == v_o.smem_total
+    assert v_c["accum_per_thread"] == v_o.accum_per_thread and v_c["regs_per_thread"] == v_o.regs_per_thread
+    assert v_c["regs_per_block"] == v_o.regs_per_block
+    assert (v_c["blocks_by_regs"], v_c["blocks_by_smem"], v_c["blocks_by_threads"], v_c["blocks_per_core"]) == \
+        (v_o.blocks_by_regs, v_o.blocks_by_smem, v_o.blocks_by_threads, v_o.blocks_per_core)
+    assert v_c["failures"] == v_o.failures
+    assert v_c["binding"] == v_o.binding
+    if not v_o.failures:
+        assert (v_c["grid"], v_c["waves"], v_c["fill"]) == (v_o.grid, v_o.waves, v_o.fill)
+        assert v_c["warnings"] == v_o.warnings
+        assert v_c["traffic"] == v_o.traffic
+        assert v_c["traffic_rounded"] == OP.round_half_even(v_o.traffic)
+
+
+DEVICES = [("gfx950", None), ((132, 228), None), ((108, 164), None)]
+
+
+def _cdev(name):
+    return tss.device_gfx950() if name == "gfx950" else tss.device_pages(*name)
+
+
+@pytest.mark.parametrize("name", ["gfx950", (132, 228), (108, 164)])
+def test_planner_sweep_bit_exact(name):
+    cd, od = _cdev(name), _oracle_dev(None, name)
+    shapes = [(1, 4096, 4096, 4096), (1, 256, 256, 256), (4, 3000, 5000, 2048), (1, 8192, 8192, 8192),
+              (1, 256, 6272, 2304), (1, 100, 37, 24)]
+    instr_sets = [None] if name == "gfx950" else ["wgmma", "mma", "simt"]
+    for (b, M, N, K), ins in itertools.product(shapes, instr_sets):
+        instrs = [s for s, _ in od.instr_shapes] if ins is None else [ins]
+        ores = OP.sweep(M, N, K, od, instrs, batch=b)
+        best, lst, n = tss.tile_plan(M, N, K, batch=b, dev=cd, instr=ins, cap=len(ores) + 5)
+        assert n == len(ores)
+        assert len(lst) == len(ores)
+        for vc, vo in zip(lst, ores):
+            _same(vc, vo)
+        if ores:
+            _same(best, ores[0])
+
+
+def test_planner_pages_printout_through_c():
+    """The README page's printed sweep figures, reproduced by the C++ planner."""
+    best, lst, n = tss.tile_plan(4096, 4096, 4096, dev=tss.device_pages(), instr="wgmma", cap=8)
+    assert n == 459
+    assert [(v["config"].bm, v["config"].bn, v["config"].bk, v["config"].stages, v["config"].threads)
+            for v in lst[:2]] == [(256, 256, 16, 2, 512), (256, 256, 16, 3, 512)]
+    assert all(f"{float(v['traffic']) / 1e6:.1f}" == "1107.3" for v in lst)
+    assert all((v["regs_per_thread"], v["blocks_per_core"], v["waves"], f"{float(v['fill']) * 100:.0f}%",
+                v["binding"]) == (128, 1, 2, "94%", "regs") for v in lst)
+
+
+def test_evaluate_random_configs_bit_exact():
+    rng = np.random.default_rng(7)
+    for _ in range(3000):
+        name = DEVICES[rng.integers(0, 3)][0]
+        cd, od = _cdev(name), _oracle_dev(None, name)
+        instrs = [s for s, _ in od.instr_shapes]
+        ins = instrs[rng.integers(0, len(instrs))]
+        cfg = OP.TileConfig(int(rng.choice([8, 16, 24, 32, 48, 64, 96, 128, 192, 256, 512])),
+                            int(rng.choice([8, 16, 32, 40, 64, 128, 256, 512])),
+                            int(rng.choice([8, 16, 32, 48, 64, 128])), int(rng.integers(1, 6)),
+                            int(rng.choice([32, 64, 96, 100, 128, 192, 256, 512, 1024, 2048])), ins)
+        b, M, N, K = int(rng.integers(1, 5)), int(rng.integers(0, 20000)), int(rng.integers(0, 20000)), \
+            int(rng.integers(0, 20000))
+        eb = int(rng.choice([1, 2, 4]))
+        vo = OP.evaluate(cfg, od, elem_bytes=eb)
+        OP.finish_parallelism(vo, M, N, od, b)
+        vo.traffic = OP.dram_traffic(M, N, K, cfg, eb, b)
+        vc = tss.evaluate(tss.TileConfig(cfg.block_m, cfg.block_n, cfg.block_k, cfg.stages, cfg.threads, ins),
+                          M, N, K, batch=b, elem_bytes=eb, dev=cd)
+        # compare C4/C0 even for infeasible configs
+        assert (vc["grid"], vc["waves"], vc["fill"], vc["warnings"]) == (vo.grid, vo.waves, vo.fill, vo.warnings)
+        assert vc["traffic"] == vo.traffic
+        _same(vc, vo)
+
+
+def test_hw_tile_matches_oracle():
+    for H, kh, sh, pt, d in itertools.product((1, 5, 9, 56), (1, 3, 5), (1, 2, 3), (0, 1, 2), (1, 2)):
+        OHt = OH.out_size(H, kh, sh, pt, pt, d)
+        if OHt <= 0:
+            continue
+        for toh in (1, 2, 3, 8):
+            for t in OH.tile_table(H, kh, sh, pt, d, OHt, toh):
+                c = tss.hw_tile(H, kh, sh, pt, d, t.o0, t.o1)
+                assert (c["in_start"], c["in_end"], c["in_span"], c["pt"], c["pb"], c["halo"]) == \
+                    (t.in_start, t.in_end, t.in_span, t.pt, t.pb, t.halo)
+
+
+def test_hw_tile_worked_example():
+    a = tss.hw_tile(9, 3, 2, 1, 1, 0, 2)
+    b = tss.hw_tile(9, 3, 2, 1, 1, 2, 4)
+    assert (a["in_start"], a["in_end"], a["in_span"], a["pt"], a["pb"]) == (0, 4, 4, 1, 0)
+    assert (b["in_start"], b["in_end"], b["in_span"], b["pt"], b["pb"]) == (3, 8, 5, 0, 0)
+    assert a["halo"] == b["halo"] == 1
+
+
+def test_argument_errors_before_device_work():
+    L = C.lib()
+    cfg = C.TileConfig(256, 256, 64, 2, 256, C.INSTR["mfma32"])
+    g = lambda *a: L.tss_gemm(*a)
+    assert g(64, 64, 64, 7, 16, 16, 16, 1, C.TSS_F32, None, None) == C.TSS_E_DTYPE
+    assert g(64, 64, 64, C.TSS_F16, 16, 16, 16, 1, C.TSS_BF16, None, None) == C.TSS_E_DTYPE
+    assert g(64, 64, 60, C.TSS_F16, 16, 16, 16, 1, C.TSS_F32, None, None) == C.TSS_E_ALIGN   # K % 8
+    assert g(64, 36, 64, C.TSS_F16, 16, 16, 16, 1, C.TSS_F32, None, None) == C.TSS_E_ALIGN   # N % 8
+    assert g(64, 64, 64, C.TSS_F16, 24, 16, 16, 1, C.TSS_F32, None, None) == C.TSS_E_ALIGN   # A misaligned
+    assert g(64, 64, 64, C.TSS_F16, None, 16, 16, 1, C.TSS_F32, None, None) == C.TSS_E_ARG
+    assert g(-1, 64, 64, C.TSS_F16, 16, 16, 16, 1, C.TSS_F32, None, None) == C.TSS_E_ARG
+    assert g(64, 64, 64, C.TSS_F16, 16, 16, 16, 0, C.TSS_F32, None, None) == C.TSS_E_ARG
+    assert g(0, 64, 64, C.TSS_F16, None, None, None, 1, C.TSS_F32, None, None) == C.TSS_OK  # empty: no-op
+    assert g(1 << 17, 1 << 14, 1 << 14, C.TSS_F16, 16, 16, 16, 1, C.TSS_F32, None, None) == C.TSS_E_ARG  # >2 GiB
+    bad = C.TileConfig(256, 256, 64, 3, 256, C.INSTR["mfma32"])       # 192 KiB of LDS: C1
+    assert g(64, 64, 64, C.TSS_F16, 16, 16, 16, 1, C.TSS_F32, ctypes.byref(bad), None) == C.TSS_E_INFEASIBLE
+    nv = C.TileConfig(128, 128, 32, 2, 256, C.INSTR["wgmma"])
+    assert g(64, 64, 64, C.TSS_F16, 16, 16, 16, 1, C.TSS_F32, ctypes.byref(nv), None) == C.TSS_E_ARG
+    cv = lambda *a: L.tss_conv2d(*a)
+    base = [8, 256, 56, 56, 256, 3, 3, 2, 2, 1, 1, 1, 1]
+    assert cv(*base, 0, C.TSS_F16, C.TSS_F32, 16, 16, 16, None, None) == C.TSS_E_ARG        # tile_oh 0
+    assert cv(*base, 29, C.TSS_F16, C.TSS_F32, 16, 16, 16, None, None) == C.TSS_E_ARG       # tile_oh > OH
+    assert cv(*[8, 3, 56, 56, 256, 3, 3, 2, 2, 1, 1, 1, 1], 8, C.TSS_F16, C.TSS_F32, 16, 16, 16, None,
+              None) == C.TSS_E_ALIGN                                                         # C*kh*kw = 27
+    assert cv(*base, 8, C.TSS_F32, C.TSS_F32, 16, 16, 16, None, None) == C.TSS_E_DTYPE
+    assert cv(*base, 8, C.TSS_F16, C.TSS_F32, 16, 24, 16, None, None) == C.TSS_E_ALIGN
+    assert cv(*[8, 256, 1, 56, 256, 3, 3, 2, 2, 0, 1, 1, 1], 1, C.TSS_F16, C.TSS_F32, 16, 16, 16, None,
+              None) == C.TSS_E_ARG                                                           # window > input
+    assert L.tss_evaluate(ctypes.byref(cfg), None, 0, 1, 1, 1, 2, ctypes.byref(C.Verdict())) == C.TSS_E_ARG
+    assert L.tss_hw_tile(9, 3, 2, 1, 1, 2, 2, ctypes.byref(C.HwSlice())) == C.TSS_E_ARG
+    assert L.tss_tile_plan(1, 64, 64, 64, 2, None, 99, None, None, 0, None) == C.TSS_E_ARG
+    assert L.tss_status_string(-4).decode() == "tile configuration infeasible"
+
+
+def test_every_feasible_gfx950_config_has_a_kernel():
+    g = OP.device_gfx950()
+    n = 0
+    for c in OP.candidates(g, 1 << 20, ["mfma32", "mfma16"]):
+        ok = OP.evaluate(c, g).feasible
+        for dt in ("f16", "bf16"):
+            for op in ("gemm", "conv"):
+                assert tss.kernel_available(tss.TileConfig(c.block_m, c.block_n, c.block_k, c.stages, c.threads,
+                                                           c.instr), dt, op) == ok
+        n += ok
+    assert n == 292
+
+
+def test_default_config_is_planner_best():
+    for (b, M, N, K) in [(1, 4096, 4096, 4096), (4, 3000, 5000, 2048), (1, 256, 256, 256), (1, 8192, 8192, 8192)]:
+        best, _, _ = tss.tile_plan(M, N, K, batch=b)
+        assert tss.default_config(M, N, K, batch=b) == best["config"]

@@ -188,3 +188,12 @@ def test_gfx950_load_rule_per_wave():
     assert "C3_LOAD" in P.evaluate(P.TileConfig(64, 64, 16, 2, 256, "mfma32"), g).failures
     assert "C3_LOAD" not in P.evaluate(P.TileConfig(64, 64, 32, 2, 256, "mfma32"), g).failures
     assert "C3_LOAD" in P.evaluate(P.TileConfig(64, 128, 16, 2, 512, "mfma16"), g).failures
+
+
+def test_short_k_keeps_the_shortest_step():
+    g = P.device_gfx950()
+    res = P.sweep(64, 64, 8, g, ["mfma32"])
+    assert res and {v.config.block_k for v in res} == {16}
+    assert P.sweep(64, 64, 0, g, ["mfma32"])
+    pages = P.sweep(4096, 4096, 8, P.device_pages(), ["wgmma"])
+    assert {v.config.block_k for v in pages} == {16}

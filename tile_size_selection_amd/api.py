@@ -1,0 +1,185 @@
+"""Python front end of libtss: argument marshalling only.  Every step of the
+GEMM / convolution runs in the HIP kernels; torch supplies device memory and
+the stream."""
+from __future__ import annotations
+
+import ctypes
+from dataclasses import dataclass
+from fractions import Fraction
+from typing import List, Optional, Sequence, Tuple, Union
+
+from . import _capi as C
+
+try:
+    import torch
+except ImportError:  # the planner needs no torch
+    torch = None
+
+
+@dataclass(frozen=True)
+class TileConfig:
+    bm: int
+    bn: int
+    bk: int
+    stages: int
+    threads: int
+    instr: str = "mfma32"
+
+    def c(self) -> C.TileConfig:
+        if self.instr not in C.INSTR:
+            raise ValueError(f"unknown instruction shape {self.instr!r}")
+        return C.TileConfig(self.bm, self.bn, self.bk, self.stages, self.threads, C.INSTR[self.instr])
+
+    @staticmethod
+    def from_c(c: C.TileConfig) -> "TileConfig":
+        return TileConfig(c.bm, c.bn, c.bk, c.stages, c.threads, C.INSTR_NAME.get(c.instr, str(c.instr)))
+
+
+def device_gfx950() -> C.Device:
+    d = C.Device()
+    C.check(C.lib().tss_device_gfx950(ctypes.byref(d)), "tss_device_gfx950")
+    return d
+
+
+def device_pages(sm_count: int = 132, smem_kb: int = 228) -> C.Device:
+    d = C.Device()
+    C.check(C.lib().tss_device_pages(sm_count, smem_kb, ctypes.byref(d)), "tss_device_pages")
+    return d
+
+
+def device_query(hip_device: int = 0) -> C.Device:
+    d = C.Device()
+    C.check(C.lib().tss_device_query(hip_device, ctypes.byref(d)), "tss_device_query")
+    return d
+
+
+def verdict_dict(v: C.Verdict) -> dict:
+    num = (v.traffic_num_hi << 64) | v.traffic_num_lo
+    return {
+        "config": TileConfig.from_c(v.cfg),
+        "smem_per_stage": v.smem_per_stage, "smem_total": v.smem_total,
+        "accum_per_thread": v.accum_per_thread, "regs_per_thread": v.regs_per_thread,
+        "regs_per_block": v.regs_per_block, "blocks_by_regs": v.blocks_by_regs,
+        "blocks_by_smem": v.blocks_by_smem, "blocks_by_threads": v.blocks_by_threads,
+        "blocks_per_core": v.blocks_per_core, "grid": v.grid, "waves": v.waves,
+        "fill": Fraction(v.fill_num, v.fill_den) if v.fill_den else Fraction(0),
+        "traffic": Fraction(num, v.traffic_den) if v.traffic_den else Fraction(0),
+        "traffic_rounded": v.traffic_rounded,
+        "failures": [n for i, n in enumerate(C.FAIL_BITS) if v.failures >> i & 1],
+        "warnings": [n for i, n in enumerate(C.WARN_BITS) if v.warnings >> i & 1],
+        "binding": C.BINDING.get(v.binding, "?"),
+    }
+
+
+def evaluate(cfg: TileConfig, M: int, N: int, K: int, batch: int = 1, elem_bytes: int = 2,
+             dev: Optional[C.Device] = None) -> dict:
+    v = C.Verdict()
+    C.check(C.lib().tss_evaluate(ctypes.byref(cfg.c()), ctypes.byref(dev) if dev is not None else None,
+                                 batch, M, N, K, elem_bytes, ctypes.byref(v)), "tss_evaluate")
+    return verdict_dict(v)
+
+
+def tile_plan(M: int, N: int, K: int, batch: int = 1, elem_bytes: int = 2, dev: Optional[C.Device] = None,
+              instr: Optional[str] = None, cap: int = 0) -> Tuple[Optional[dict], List[dict], int]:
+    """(best verdict or None, the first `cap` ranked verdicts, number feasible)."""
+    best = C.Verdict()
+    lst = (C.Verdict * max(cap, 1))()
+    n = C.i32(0)
+    st = C.lib().tss_tile_plan(batch, M, N, K, elem_bytes, ctypes.byref(dev) if dev is not None else None,
+                               C.INSTR[instr] if instr else 0, ctypes.byref(best), lst if cap else None, cap,
+                               ctypes.byref(n))
+    if st == C.TSS_E_INFEASIBLE:
+        return None, [], 0
+    C.check(st, "tss_tile_plan")
+    return verdict_dict(best), [verdict_dict(lst[i]) for i in range(min(cap, n.value))], n.value
+
+
+def hw_tile(H: int, kh: int, sh: int, pt: int, d: int, o0: int, o1: int) -> dict:
+    s = C.HwSlice()
+    C.check(C.lib().tss_hw_tile(H, kh, sh, pt, d, o0, o1, ctypes.byref(s)), "tss_hw_tile")
+    return {f: getattr(s, f) for f, _ in C.HwSlice._fields_}
+
+
+def kernel_available(cfg: TileConfig, dtype: str = "f16", op: str = "gemm") -> bool:
+    return bool(C.lib().tss_kernel_available(ctypes.byref(cfg.c()), _DT[dtype], 0 if op == "gemm" else 1))
+
+
+def default_config(M: int, N: int, K: int, batch: int = 1, dtype: str = "f16") -> TileConfig:
+    c = C.TileConfig()
+    C.check(C.lib().tss_gemm_default_config(batch, M, N, K, _DT[dtype], ctypes.byref(c)), "tss_gemm_default_config")
+    return TileConfig.from_c(c)
+
+
+_DT = {"f16": C.TSS_F16, "bf16": C.TSS_BF16, "f32": C.TSS_F32}
+
+
+def _dt_of(t) -> str:
+    return {torch.float16: "f16", torch.bfloat16: "bf16", torch.float32: "f32"}[t.dtype]
+
+
+def _stream_ptr(stream) -> Optional[int]:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return getattr(stream, "cuda_stream", stream)
+
+
+def gemm(A, B, out_dtype: Optional[str] = None, cfg: Optional[TileConfig] = None, out=None, stream=None):
+    """C = A @ B for row-major fp16/bf16 device tensors, A [b,] M x K and
+    B [b,] K x N; fp32 accumulation; out_dtype 'f32' or the input dtype
+    (default: the input dtype)."""
+    if A.dim() not in (2, 3) or B.dim() != A.dim():
+        raise ValueError("A and B must both be 2-D or both 3-D")
+    if A.dtype != B.dtype:
+        raise ValueError("A and B must share a dtype")
+    if not (A.is_cuda and B.is_cuda and A.is_contiguous() and B.is_contiguous()):
+        raise ValueError("A and B must be contiguous device tensors")
+    batched = A.dim() == 3
+    bt = A.shape[0] if batched else 1
+    M, K = A.shape[-2], A.shape[-1]
+    K2, N = B.shape[-2], B.shape[-1]
+    if K != K2 or (batched and B.shape[0] != bt):
+        raise ValueError(f"shape mismatch {tuple(A.shape)} x {tuple(B.shape)}")
+    dt = _dt_of(A)
+    od = out_dtype or dt
+    shape = (bt, M, N) if batched else (M, N)
+    tdt = {"f16": torch.float16, "bf16": torch.bfloat16, "f32": torch.float32}[od]
+    if out is None:
+        out = torch.empty(shape, dtype=tdt, device=A.device)
+    elif tuple(out.shape) != shape or out.dtype != tdt or not out.is_contiguous():
+        raise ValueError("out has the wrong shape, dtype or layout")
+    st = C.lib().tss_gemm(M, N, K, _DT[dt], A.data_ptr(), B.data_ptr(), out.data_ptr(), bt, _DT[od],
+                          ctypes.byref(cfg.c()) if cfg else None, _stream_ptr(stream))
+    C.check(st, "tss_gemm")
+    return out
+
+
+def conv2d(x, w, stride: Union[int, Sequence[int]] = 1, padding: Union[int, Sequence[int]] = 0,
+           dilation: Union[int, Sequence[int]] = 1, tile_oh: Optional[int] = None, out_dtype: Optional[str] = None,
+           cfg: Optional[TileConfig] = None, out=None, stream=None):
+    """NCHW convolution as an implicit GEMM over output-row tiles of tile_oh
+    rows (default: the whole output height)."""
+    pair = lambda v: (v, v) if isinstance(v, int) else tuple(v)
+    (sh, sw), (ph, pw), (dh, dw) = pair(stride), pair(padding), pair(dilation)
+    if x.dim() != 4 or w.dim() != 4 or x.dtype != w.dtype:
+        raise ValueError("x must be NCHW and w OIHW, same dtype")
+    if not (x.is_cuda and w.is_cuda and x.is_contiguous() and w.is_contiguous()):
+        raise ValueError("x and w must be contiguous device tensors")
+    N, Ci, H, W = x.shape
+    Co, Ci2, kh, kw = w.shape
+    if Ci != Ci2:
+        raise ValueError("channel mismatch")
+    OH = (H + 2 * ph - (kh - 1) * dh - 1) // sh + 1
+    OW = (W + 2 * pw - (kw - 1) * dw - 1) // sw + 1
+    dt = _dt_of(x)
+    od = out_dtype or dt
+    tdt = {"f16": torch.float16, "bf16": torch.bfloat16, "f32": torch.float32}[od]
+    shape = (N, Co, OH, OW)
+    if out is None:
+        out = torch.empty(shape, dtype=tdt, device=x.device)
+    elif tuple(out.shape) != shape or out.dtype != tdt or not out.is_contiguous():
+        raise ValueError("out has the wrong shape, dtype or layout")
+    st = C.lib().tss_conv2d(N, Ci, H, W, Co, kh, kw, sh, sw, ph, pw, dh, dw, tile_oh or OH, _DT[dt], _DT[od],
+                            x.data_ptr(), w.data_ptr(), out.data_ptr(), ctypes.byref(cfg.c()) if cfg else None,
+                            _stream_ptr(stream))
+    C.check(st, "tss_conv2d")
+    return out

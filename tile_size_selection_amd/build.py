@@ -1,0 +1,100 @@
+"""Build libtss.so (planner, C ABI and every gfx950 kernel) in-tree.
+
+    python -m tile_size_selection_amd.build [--incremental] [--jobs N]
+
+Each instantiation unit under csrc/inst is compiled by its own hipcc process
+for --offload-arch=gfx950; the objects are linked into
+tile_size_selection_amd/libtss.so, which is what the Python binding loads.
+"""
+from __future__ import annotations
+
+import argparse
+import concurrent.futures as cf
+import glob
+import os
+import shutil
+import subprocess
+import sys
+import time
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+OUT_DIR = os.path.join(ROOT, "_build")
+LIB = os.path.join(PKG, "libtss.so")
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+
+# -packed-fp32-ops off: compiler-made v_pk_{add,mul,fma}_f32 are avoided.
+FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++20", "-fPIC", "-Wall", "-Wno-unused-variable",
+         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         "-I", os.path.join(ROOT, "include")]
+
+
+def sources():
+    return ([os.path.join(CSRC, "planner.cpp"), os.path.join(CSRC, "api.cpp")]
+            + sorted(glob.glob(os.path.join(CSRC, "inst", "*.hip"))))
+
+
+def _headers_mtime():
+    hs = glob.glob(os.path.join(CSRC, "*.h")) + glob.glob(os.path.join(CSRC, "*.inc")) + \
+        glob.glob(os.path.join(ROOT, "include", "*.h"))
+    return max(os.path.getmtime(h) for h in hs)
+
+
+def _obj(src):
+    rel = os.path.relpath(src, CSRC).replace(os.sep, "_")
+    return os.path.join(OUT_DIR, rel + ".o")
+
+
+def _compile(src, obj):
+    t0 = time.time()
+    cmd = [HIPCC, *FLAGS, "-x", "hip", "-c", src, "-o", obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    errs = "\n".join(l for l in (r.stderr or "").splitlines() if "packed-fp32-ops" not in l)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for {src}:\n{errs}")
+    return src, time.time() - t0
+
+
+def build(incremental: bool = False, jobs: int = 0, verbose: bool = True) -> str:
+    os.makedirs(OUT_DIR, exist_ok=True)
+    hm = _headers_mtime()
+    todo = []
+    for s in sources():
+        o = _obj(s)
+        if incremental and os.path.exists(o) and os.path.getmtime(o) > max(os.path.getmtime(s), hm):
+            continue
+        todo.append((s, o))
+    jobs = jobs or min(16, os.cpu_count() or 4)
+    t0 = time.time()
+    with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
+        for src, dt in ex.map(lambda so: _compile(*so), todo):
+            if verbose:
+                print(f"  compiled {os.path.relpath(src, ROOT)} in {dt:.1f}s", flush=True)
+    objs = [_obj(s) for s in sources()]
+    tmp = LIB + ".tmp"
+    r = subprocess.run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs],
+                       capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{r.stderr}")
+    os.replace(tmp, LIB)
+    if verbose:
+        print(f"built {os.path.relpath(LIB, ROOT)} ({len(todo)} units compiled) in {time.time() - t0:.1f}s",
+              flush=True)
+    return LIB
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--incremental", action="store_true")
+    ap.add_argument("--jobs", type=int, default=0)
+    ap.add_argument("--clean", action="store_true")
+    a = ap.parse_args()
+    if a.clean and os.path.isdir(OUT_DIR):
+        shutil.rmtree(OUT_DIR)
+    build(a.incremental, a.jobs)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,240 @@
+// C ABI of the device operations: tss_gemm, tss_conv2d and their helpers.
+// Argument checks happen before any launch; nothing here allocates device
+// memory.
+#include <hip/hip_runtime.h>
+
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <tuple>
+#include <vector>
+
+#include "planner.h"
+#include "registry.h"
+
+using namespace tss;
+
+namespace {
+
+struct Key {
+  int32_t bm, bn, bk, stages, threads, instr, dtype, op;
+  bool operator<(const Key &o) const {
+    return std::tie(bm, bn, bk, stages, threads, instr, dtype, op) <
+           std::tie(o.bm, o.bn, o.bk, o.stages, o.threads, o.instr, o.dtype, o.op);
+  }
+};
+
+const std::map<Key, KernelEntry> &registry() {
+  static const std::map<Key, KernelEntry> reg = [] {
+    std::map<Key, KernelEntry> m;
+    KernelTable (*tables[])() = {table_gemm_f16_bm64,  table_gemm_f16_bm128,  table_gemm_f16_bm256,
+                                 table_gemm_bf16_bm64, table_gemm_bf16_bm128, table_gemm_bf16_bm256,
+                                 table_conv_f16_bm64,  table_conv_f16_bm128,  table_conv_f16_bm256,
+                                 table_conv_bf16_bm64, table_conv_bf16_bm128, table_conv_bf16_bm256};
+    for (auto fn : tables) {
+      KernelTable t = fn();
+      for (int i = 0; i < t.n; ++i) {
+        const KernelEntry &e = t.entries[i];
+        if (!e.launch) continue;
+        m[Key{e.bm, e.bn, e.bk, e.stages, e.threads, e.instr, e.dtype, e.op}] = e;
+      }
+    }
+    return m;
+  }();
+  return reg;
+}
+
+const KernelEntry *find_kernel(const tss_tile_config &c, int32_t dtype, int32_t op) {
+  const auto &r = registry();
+  auto it = r.find(Key{c.bm, c.bn, c.bk, c.stages, c.threads, c.instr, dtype, op});
+  return it == r.end() ? nullptr : &it->second;
+}
+
+// Planner choice per problem, cached (planning evaluates every candidate).
+int32_t planned_config(int64_t batch, int64_t M, int64_t N, int64_t K, tss_tile_config *out) {
+  using PKey = std::tuple<int64_t, int64_t, int64_t, int64_t>;
+  static std::mutex mu;
+  static std::map<PKey, tss_tile_config> cache;
+  PKey key{batch, M, N, K};
+  {
+    std::lock_guard<std::mutex> g(mu);
+    auto it = cache.find(key);
+    if (it != cache.end()) {
+      *out = it->second;
+      return TSS_OK;
+    }
+  }
+  tss_verdict best{};
+  int32_t st = tss_tile_plan(batch, M, N, K, 2, nullptr, 0, &best, nullptr, 0, nullptr);
+  if (st != TSS_OK) return st;
+  {
+    std::lock_guard<std::mutex> g(mu);
+    cache[key] = best.cfg;
+  }
+  *out = best.cfg;
+  return TSS_OK;
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int32_t check_config(const tss_tile_config &c) {
+  const tss_device d = gfx950_device();
+  if (c.bm <= 0 || c.bn <= 0 || c.bk <= 0 || c.stages <= 0 || c.threads <= 0 || !instr_on_device(c.instr, d))
+    return TSS_E_ARG;
+  if (evaluate_block(c, d, 2).failures) return TSS_E_INFEASIBLE;
+  return TSS_OK;
+}
+
+int group_m_for(int tiles_m) {
+  int g = 4;
+  return tiles_m < g ? (tiles_m > 0 ? tiles_m : 1) : g;
+}
+
+constexpr int64_t kTwoGiB = int64_t(1) << 31;
+
+}  // namespace
+
+extern "C" {
+
+int32_t tss_device_query(int32_t hip_device, tss_device *out) {
+  if (!out) return TSS_E_ARG;
+  hipDeviceProp_t pr;
+  if (hipGetDeviceProperties(&pr, hip_device) != hipSuccess) return TSS_E_HIP;
+  if (std::strncmp(pr.gcnArchName, "gfx950", 6) != 0) return TSS_E_UNSUPPORTED;
+  tss_device d = gfx950_device();
+  d.cores = pr.multiProcessorCount;
+  d.onchip_per_core = int32_t(pr.maxSharedMemoryPerMultiProcessor);
+  d.onchip_per_block_max = int32_t(pr.sharedMemPerBlock);
+  d.max_threads_per_core = pr.maxThreadsPerMultiProcessor;
+  d.max_threads_per_block = pr.maxThreadsPerBlock;
+  if (pr.maxBlocksPerMultiProcessor > 0) d.max_blocks_per_core = pr.maxBlocksPerMultiProcessor;
+  *out = d;
+  return TSS_OK;
+}
+
+int32_t tss_kernel_available(const tss_tile_config *cfg, int32_t dtype, int32_t op) {
+  if (!cfg || (op != 0 && op != 1)) return 0;
+  return find_kernel(*cfg, dtype, op) ? 1 : 0;
+}
+
+int32_t tss_gemm_default_config(int64_t batch, int64_t M, int64_t N, int64_t K, int32_t dtype,
+                                tss_tile_config *out) {
+  if (!out || batch < 1 || M < 0 || N < 0 || K < 0) return TSS_E_ARG;
+  if (dtype != TSS_F16 && dtype != TSS_BF16) return TSS_E_DTYPE;
+  return planned_config(batch, M, N, K, out);
+}
+
+int32_t tss_gemm(int64_t M, int64_t N, int64_t K, int32_t dtype, const void *A, const void *B, void *C,
+                 int64_t batch, int32_t out_dtype, const tss_tile_config *cfg, void *stream) {
+  if (batch < 1 || M < 0 || N < 0 || K < 0) return TSS_E_ARG;
+  if (M > INT32_MAX || N > INT32_MAX || K > INT32_MAX || batch > INT32_MAX) return TSS_E_ARG;
+  if (dtype != TSS_F16 && dtype != TSS_BF16) return TSS_E_DTYPE;
+  if (out_dtype != TSS_F32 && out_dtype != dtype) return TSS_E_DTYPE;
+  if (K % 8 || N % 8) return TSS_E_ALIGN;
+  if (M * K * 2 >= kTwoGiB || K * N * 2 >= kTwoGiB) return TSS_E_ARG;
+  if (M == 0 || N == 0) return TSS_OK;
+  if (!C || (K > 0 && (!A || !B))) return TSS_E_ARG;  // with K == 0, A and B are never read
+  if (!aligned16(A) || !aligned16(B) || !aligned16(C)) return TSS_E_ALIGN;
+  tss_tile_config c{};
+  if (cfg) {
+    c = *cfg;
+    int32_t st = check_config(c);
+    if (st != TSS_OK) return st;
+  } else {
+    int32_t st = planned_config(batch, M, N, K, &c);
+    if (st != TSS_OK) return st;
+  }
+  const KernelEntry *e = find_kernel(c, dtype, 0);
+  if (!e) return TSS_E_UNSUPPORTED;
+  KernelArgs a{};
+  a.A = A;
+  a.B = B;
+  a.C = C;
+  a.M = int32_t(M);
+  a.N = int32_t(N);
+  a.K = int32_t(K);
+  a.tiles_m = int32_t((M + c.bm - 1) / c.bm);
+  a.tiles_n = int32_t((N + c.bn - 1) / c.bn);
+  a.group_m = group_m_for(a.tiles_m);
+  a.out_dtype = out_dtype;
+  a.batch_stride_a = M * K;
+  a.batch_stride_b = K * N;
+  a.batch_stride_c = M * N;
+  const int64_t blocks = batch * a.tiles_m * a.tiles_n;
+  if (blocks * c.threads > int64_t(UINT32_MAX)) return TSS_E_ARG;
+  hipError_t err = e->launch(a, dim3(uint32_t(blocks)), e->stage_bytes * c.stages, (hipStream_t)stream);
+  return err == hipSuccess ? TSS_OK : TSS_E_HIP;
+}
+
+int32_t tss_conv2d(int64_t N, int64_t C, int64_t H, int64_t W, int64_t Cout, int64_t kh, int64_t kw, int64_t sh,
+                   int64_t sw, int64_t ph, int64_t pw, int64_t dh, int64_t dw, int64_t tile_oh, int32_t dtype,
+                   int32_t out_dtype, const void *x, const void *w, void *y, const tss_tile_config *cfg,
+                   void *stream) {
+  const int64_t lim = int64_t(1) << 30;
+  if (N < 1 || C < 1 || H < 1 || W < 1 || Cout < 1 || kh < 1 || kw < 1 || sh < 1 || sw < 1 || ph < 0 || pw < 0 ||
+      dh < 1 || dw < 1)
+    return TSS_E_ARG;
+  if (N > lim || C > lim || H > lim || W > lim || Cout > lim || kh > lim || kw > lim || sh > lim || sw > lim ||
+      ph > lim || pw > lim || dh > lim || dw > lim)
+    return TSS_E_ARG;
+  if (dtype != TSS_F16 && dtype != TSS_BF16) return TSS_E_DTYPE;
+  if (out_dtype != TSS_F32 && out_dtype != dtype) return TSS_E_DTYPE;
+  const int64_t OH = (H + 2 * ph - (kh - 1) * dh - 1) / sh + 1;
+  const int64_t OW = (W + 2 * pw - (kw - 1) * dw - 1) / sw + 1;
+  if (H + 2 * ph < (kh - 1) * dh + 1 || W + 2 * pw < (kw - 1) * dw + 1) return TSS_E_ARG;
+  if (tile_oh < 1 || tile_oh > OH) return TSS_E_ARG;
+  const int64_t Kc = C * kh * kw;
+  if (Kc % 8) return TSS_E_ALIGN;
+  if (N * C * H * W * 2 >= kTwoGiB || Cout * Kc * 2 >= kTwoGiB || Kc > INT32_MAX) return TSS_E_ARG;
+  const int64_t out_bytes = out_dtype == TSS_F32 ? 4 : 2;
+  if (N * Cout * OH * OW * out_bytes >= (int64_t(1) << 40)) return TSS_E_ARG;
+  const int64_t tile_pixels = N * tile_oh * OW;
+  if (tile_pixels > INT32_MAX) return TSS_E_ARG;
+  if (!x || !w || !y) return TSS_E_ARG;
+  if (!aligned16(x) || !aligned16(w) || !aligned16(y)) return TSS_E_ALIGN;
+  tss_tile_config c{};
+  if (cfg) {
+    c = *cfg;
+    int32_t st = check_config(c);
+    if (st != TSS_OK) return st;
+  } else {
+    // The implicit GEMM: M = Cout, N = every output pixel, K = C*kh*kw.
+    int32_t st = planned_config(1, Cout, N * OH * OW, Kc, &c);
+    if (st != TSS_OK) return st;
+  }
+  const KernelEntry *e = find_kernel(c, dtype, 1);
+  if (!e) return TSS_E_UNSUPPORTED;
+  KernelArgs a{};
+  a.A = w;
+  a.B = x;
+  a.C = y;
+  a.M = int32_t(Cout);
+  a.N = int32_t(tile_pixels);
+  a.K = int32_t(Kc);
+  a.tiles_m = int32_t((Cout + c.bm - 1) / c.bm);
+  a.tiles_n = int32_t((tile_pixels + c.bn - 1) / c.bn);
+  a.group_m = group_m_for(a.tiles_m);
+  a.out_dtype = out_dtype;
+  a.Nb = int32_t(N);
+  a.Cin = int32_t(C);
+  a.H = int32_t(H);
+  a.W = int32_t(W);
+  a.kh = int32_t(kh);
+  a.kw = int32_t(kw);
+  a.sh = int32_t(sh);
+  a.sw = int32_t(sw);
+  a.ph = int32_t(ph);
+  a.pw = int32_t(pw);
+  a.dh = int32_t(dh);
+  a.dw = int32_t(dw);
+  a.OH = int32_t(OH);
+  a.OW = int32_t(OW);
+  a.tile_oh = int32_t(tile_oh);
+  const int64_t n_htiles = (OH + tile_oh - 1) / tile_oh;
+  const int64_t blocks = n_htiles * a.tiles_m * a.tiles_n;
+  if (blocks * c.threads > int64_t(UINT32_MAX)) return TSS_E_ARG;
+  hipError_t err = e->launch(a, dim3(uint32_t(blocks)), e->stage_bytes * c.stages, (hipStream_t)stream);
+  return err == hipSuccess ? TSS_OK : TSS_E_HIP;
+}
+
+}  // extern "C"

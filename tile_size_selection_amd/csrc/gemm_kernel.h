@@ -1,0 +1,511 @@
+// Multi-level tiled GEMM for gfx950:  C[b] = A[b] x B[b], fp16/bf16 inputs,
+// fp32 accumulation.
+//
+// The hierarchy is the one of the "Tiling（分块）" page's multi-level tiling
+// section, mapped onto CDNA4:
+//   block  : a BM x BN tile of C per workgroup; A (BM x BK) and B (BK x BN)
+//            slices staged HBM -> LDS once per K step and reused by every wave
+//   wave   : the block splits into WM x WN waves, each owning a
+//            (BM/WM) x (BN/WN) sub-tile held in accumulation registers
+//   MFMA   : v_mfma_f32_32x32x16 or v_mfma_f32_16x16x32 on LDS fragments
+//
+// Memory-hierarchy techniques of the same page, in their gfx950 form:
+//   * staging with a multi-stage pipeline: `stages` LDS buffers in a ring;
+//     K tile t+stages-1 is in flight while tile t is computed.  The copy is a
+//     direct HBM->LDS buffer load (buffer_load_dwordx4 ... lds) that bypasses
+//     registers, the analogue of the page's asynchronous copy;
+//   * coalescing: each load instruction moves 64 lanes x 16 B = 1 KiB of whole
+//     rows;
+//   * bank-conflict-free LDS: 16-byte chunks are XOR-swizzled per row (the
+//     page's row-xor-column remapping) for 64 banks of 4 bytes;
+//   * B is row-major K x N: its fragments are read with the gfx950 LDS
+//     transpose read (ds_read_b64_tr_b16) instead of being transposed on the
+//     way in.
+// Ragged edges: a 16-byte chunk outside the operand is given an offset past
+// the buffer's range, so the hardware range check writes zeros into LDS; the
+// epilogue masks rows >= M and columns >= N.
+//
+// The same kernel computes a convolution as an implicit GEMM (CONV = true):
+// A is the OIHW weight matrix (Cout x C*kh*kw, K-contiguous, loaded exactly as
+// the GEMM's A); B is the im2col matrix of one H-tile, gathered element by
+// element from the NCHW input into the B layout of the GEMM; the batch index
+// of the GEMM is the H-tile.  Each block derives its input slice and the
+// sub-operator pads from the Tiling page's H/W tiling formulas; rows of the
+// slice's pads read as zero.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/tss.h"
+
+namespace tss {
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef __attribute__((address_space(3))) i16x8 lds_i16x8;
+
+struct KernelArgs {
+  const void *A;  // GEMM: A[batch][M][K].       conv: weights [Cout][C*kh*kw]
+  const void *B;  // GEMM: B[batch][K][N].       conv: input x[Nb][C][H][W]
+  void *C;        // GEMM: C[batch][M][N].       conv: output y[Nb][Cout][OH][OW]
+  int32_t M, N, K;  // conv: M = Cout, K = C*kh*kw, N = pixels of a full H-tile
+  int32_t tiles_m, tiles_n;
+  int32_t group_m;    // tile rows per group of the L2-friendly tile order
+  int32_t out_dtype;  // TSS_F32 / TSS_F16 / TSS_BF16
+  int64_t batch_stride_a, batch_stride_b, batch_stride_c;  // GEMM only, elements
+  // convolution geometry (CONV only); the GEMM batch index is the H-tile
+  int32_t Nb, Cin, H, W, kh, kw, sh, sw, ph, pw, dh, dw, OH, OW, tile_oh;
+};
+
+// ---- small device helpers --------------------------------------------------
+
+constexpr uint32_t kOOB = 0x80000000u;  // voffset beyond any accepted buffer range
+
+// s_waitcnt with vmcnt = n and the other counters left alone (gfx9 encoding:
+// vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] in bits [15:14]).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// s_waitcnt vmcnt(n) lgkmcnt(0): the LDS writes of this wave are done too.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_lgkm0() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (0 << 8) | ((N >> 4) << 14));
+}
+
+// Workgroup barrier without the release/acquire fence of __syncthreads (which
+// would wait for every outstanding HBM->LDS copy, prefetches included).  The
+// memory clobber keeps the compiler from moving LDS accesses across it; the
+// needed waits are issued explicitly.
+__device__ __forceinline__ void block_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = __builtin_bit_cast(uint32_t, f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return uint16_t((u >> 16) | 0x40);  // quiet NaN
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return uint16_t(u >> 16);
+}
+
+template <typename T>
+struct Mfma;
+
+template <>
+struct Mfma<_Float16> {
+  static __device__ __forceinline__ f32x16 m32(i16x8 a, i16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ f32x4 m16(i16x8 a, i16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  }
+};
+
+template <>
+struct Mfma<__bf16> {
+  static __device__ __forceinline__ f32x16 m32(i16x8 a, i16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ f32x4 m16(i16x8 a, i16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  }
+};
+
+template <int MF>
+struct AccType;
+template <>
+struct AccType<32> { using type = f32x16; static constexpr int n = 16; };
+template <>
+struct AccType<16> { using type = f32x4; static constexpr int n = 4; };
+
+// ---- compile-time tile geometry ----------------------------------------------
+
+template <int BM_, int BN_, int BK_, int ST_, int NW_, int MF_>
+struct Geometry {
+  static constexpr int BM = BM_, BN = BN_, BK = BK_, ST = ST_, NW = NW_, MF = MF_;
+  static constexpr int THREADS = NW * 64;
+  static constexpr int WM = NW == 1 ? 1 : NW == 2 ? 1 : NW == 4 ? 2 : NW == 8 ? 2 : 4;
+  static constexpr int WN = NW / WM;
+  static constexpr int WTM = BM / WM, WTN = BN / WN;   // wave sub-tile
+  static constexpr int FK = MF == 32 ? 16 : 32;        // K per MFMA
+  static constexpr int TM = WTM / MF, TN = WTN / MF;   // MFMA tiles per wave
+  static constexpr int KSUB = BK / FK;                 // MFMA K steps per stage
+  static constexpr int CA = BK / 8;                    // 16-byte chunks per A row
+  static constexpr int CB = BN / 8;                    // 16-byte chunks per B row
+  static constexpr int A_BYTES = BM * BK * 2, B_BYTES = BK * BN * 2;
+  static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
+  static constexpr int A_LOADS = A_BYTES / 1024 / NW;  // 1 KiB wave loads per wave per stage
+  static constexpr int B_LOADS = B_BYTES / 1024 / NW;
+  static constexpr int LPW = A_LOADS + B_LOADS;
+  static_assert(WTM % MF == 0 && WTN % MF == 0, "wave tile must hold whole MFMA tiles");
+  static_assert(BK % FK == 0, "BK must hold whole MFMA K steps");
+  static_assert(A_BYTES % (1024 * NW) == 0 && B_BYTES % (1024 * NW) == 0, "whole wave loads");
+  static_assert(CA >= 2 && CA <= 16 && CB >= 8, "swizzle assumes 2..16 chunks per A row, >= 8 per B row");
+  static_assert(ST >= 2 && ST <= 4, "2..4 pipeline stages");
+  static_assert((ST - 2) * LPW < 64, "outstanding loads must fit the 6-bit vmcnt");
+
+  // A rows (K-contiguous, BK*2 bytes): chunk c of row r lives at chunk
+  // c ^ swz_a(r).  16 consecutive rows read at one logical chunk land in 16
+  // distinct 16-byte bank groups of the 256-byte bank space.
+  static __device__ __forceinline__ int swz_a(int r) { return (r / (16 / CA)) % CA; }
+  // B rows (N-contiguous, BN*2 bytes): a transpose read touches 4 consecutive
+  // rows (k % 4 == 0) in each 16-lane group, rows 8 apart across groups; the
+  // swizzle spreads those rows over distinct 64-byte quarters and 32-byte
+  // halves of the bank space.
+  static __device__ __forceinline__ int swz_b(int k) {
+    int q = CB >= 16 ? 4 * (k % 4) : 4 * ((k / 2) % 2);
+    return q ^ (2 * ((k / 8) % 2));
+  }
+};
+
+// Convert and store one wave's accumulators (row-major C, masked edges).
+template <typename O>
+__device__ __forceinline__ O convert_out(float v) {
+  if constexpr (__is_same(O, float)) return v;
+  else if constexpr (__is_same(O, _Float16)) return (_Float16)v;
+  else return __builtin_bit_cast(__bf16, f32_to_bf16_rne(v));
+}
+
+template <typename G, typename O, typename Acc>
+__device__ __forceinline__ void store_tile(const Acc (&acc)[G::TM][G::TN], O *C, int m0, int n0, int wr, int wc,
+                                           int lane, int M, int N) {
+  constexpr int MF = G::MF;
+  constexpr int NACC = AccType<MF>::n;
+#pragma unroll
+  for (int i = 0; i < G::TM; ++i)
+#pragma unroll
+    for (int j = 0; j < G::TN; ++j) {
+      const int col = n0 + wc * G::WTN + j * MF + lane % MF;
+      const int rbase = m0 + wr * G::WTM + i * MF + (MF == 32 ? (lane / 32) * 4 : (lane / 16) * 4);
+      if (col < N) {
+#pragma unroll
+        for (int e = 0; e < NACC; ++e) {
+          const int row = rbase + (MF == 32 ? (e / 4) * 8 + (e % 4) : e);
+          if (row < M) C[int64_t(row) * N + col] = convert_out<O>(acc[i][j][e]);
+        }
+      }
+    }
+}
+
+
+// Convolution epilogue: row = output channel, column = pixel of the H-tile
+// (image n, output row o0 + oh_l, output column ow); y is NCHW.
+template <typename G, typename O, typename Acc>
+__device__ __forceinline__ void store_conv(const Acc (&acc)[G::TM][G::TN], O *y, const KernelArgs &p, int m0, int n0,
+                                           int wr, int wc, int lane, int o0, int rows_t, int npix) {
+  constexpr int MF = G::MF;
+  constexpr int NACC = AccType<MF>::n;
+  const int plane = rows_t * p.OW;
+  const int64_t chan = int64_t(p.OH) * p.OW;
+#pragma unroll
+  for (int j = 0; j < G::TN; ++j) {
+    const int pix = n0 + wc * G::WTN + j * MF + lane % MF;
+    if (pix >= npix) continue;
+    const int n = pix / plane, rem = pix - n * plane;
+    const int oh = o0 + rem / p.OW, ow = rem % p.OW;
+    O *base = y + (int64_t(n) * p.M) * chan + int64_t(oh) * p.OW + ow;
+#pragma unroll
+    for (int i = 0; i < G::TM; ++i) {
+      const int rbase = m0 + wr * G::WTM + i * MF + (MF == 32 ? (lane / 32) * 4 : (lane / 16) * 4);
+#pragma unroll
+      for (int e = 0; e < NACC; ++e) {
+        const int co = rbase + (MF == 32 ? (e / 4) * 8 + (e % 4) : e);
+        if (co < p.M) base[int64_t(co) * chan] = convert_out<O>(acc[i][j][e]);
+      }
+    }
+  }
+}
+
+// ---- the kernel ----------------------------------------------------------------
+
+template <typename G, typename T, bool CONV>
+__global__ __launch_bounds__(G::THREADS) void tiled_gemm_kernel(KernelArgs p) {
+  extern __shared__ __attribute__((aligned(1024))) char smem[];
+  using Acc = typename AccType<G::MF>::type;
+  constexpr int MF = G::MF;
+  constexpr int S = G::ST;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wr = wave / G::WN, wc = wave % G::WN;
+
+  // -- block -> tile.  Workgroups are dealt to the 8 XCDs round-robin; remap
+  // so that each XCD gets a contiguous run of tiles, ordered in groups of
+  // group_m tile rows so that the run shares A and B panels in its L2.
+  const int nblk = gridDim.x, bid = blockIdx.x;
+  const int xcd = bid & 7, local = bid >> 3;
+  const int per = nblk >> 3, extra = nblk & 7;
+  const int t = xcd < extra ? xcd * (per + 1) + local : extra * (per + 1) + (xcd - extra) * per + local;
+  const int tiles_mn = p.tiles_m * p.tiles_n;
+  const int bz = t / tiles_mn;
+  const int tt = t - bz * tiles_mn;
+  const int span = p.group_m * p.tiles_n;
+  const int first_m = (tt / span) * p.group_m;
+  const int gm = min(p.tiles_m - first_m, p.group_m);
+  const int in_g = tt - (tt / span) * span;
+  const int tm = first_m + in_g % gm, tn = in_g / gm;
+  const int m0 = tm * G::BM, n0 = tn * G::BN;
+  const int M = p.M, K = p.K;
+
+  // -- convolution: this block's H-tile, its input slice and sub-operator pads
+  int N = p.N;
+  int o0 = 0, rows_t = 0, in_start = 0, pt_sub = 0, rows_in = 0;
+  if constexpr (CONV) {
+    o0 = bz * p.tile_oh;
+    const int o1 = min(o0 + p.tile_oh, p.OH);
+    rows_t = o1 - o0;
+    N = p.Nb * rows_t * p.OW;        // pixels of this H-tile, over the batch
+    if (n0 >= N) return;             // ragged last H-tile: whole block idle
+    in_start = max(0, o0 * p.sh - p.ph);                          // (1)
+    const int in_end = (o1 - 1) * p.sh - p.ph + (p.kh - 1) * p.dh + 1;  // (2), exclusive
+    pt_sub = max(0, p.ph - o0 * p.sh);                            // (3)
+    rows_in = min(in_end, p.H) - in_start;                        // slice rows; (4) pads the rest
+  }
+
+  const T *Ab = reinterpret_cast<const T *>(p.A) + (CONV ? 0 : int64_t(bz) * p.batch_stride_a) + int64_t(m0) * K;
+  const uint32_t a_range = uint32_t(min(G::BM, M - m0)) * uint32_t(K) * 2u;  // rows [m0, M)
+  __amdgpu_buffer_rsrc_t rsA = __builtin_amdgcn_make_buffer_rsrc((void *)Ab, (short)0, (int)a_range, 0x00020000);
+  __amdgpu_buffer_rsrc_t rsB;
+  if constexpr (CONV) {
+    const uint32_t x_range = uint32_t(p.Nb) * uint32_t(p.Cin) * uint32_t(p.H) * uint32_t(p.W) * 2u;
+    rsB = __builtin_amdgcn_make_buffer_rsrc((void *)p.B, (short)0, (int)x_range, 0x00020000);
+  } else {
+    const T *Bb = reinterpret_cast<const T *>(p.B) + int64_t(bz) * p.batch_stride_b + n0;
+    const uint32_t b_range = (uint32_t(K) * uint32_t(N) - uint32_t(n0)) * 2u;  // elements [n0, K*N)
+    rsB = __builtin_amdgcn_make_buffer_rsrc((void *)Bb, (short)0, (int)b_range, 0x00020000);
+  }
+
+  // -- A copy plan: wave load j of a stage covers LDS chunks (j*NW+wave)*64 + lane
+  uint32_t a_off[G::A_LOADS];
+  int a_kc[G::A_LOADS];  // first K element of the lane's chunk within the stage
+#pragma unroll
+  for (int j = 0; j < G::A_LOADS; ++j) {
+    int pchunk = (j * G::NW + wave) * 64 + lane;
+    int r = pchunk / G::CA, pc = pchunk % G::CA;
+    int lc = pc ^ G::swz_a(r);
+    a_off[j] = uint32_t(r) * uint32_t(K) * 2u + uint32_t(lc) * 16u;
+    a_kc[j] = lc * 8;
+  }
+  // -- B copy plan (GEMM): the same for the K x N operand
+  uint32_t b_off[CONV ? 1 : G::B_LOADS];
+  int b_k[CONV ? 1 : G::B_LOADS];
+  if constexpr (!CONV) {
+#pragma unroll
+    for (int j = 0; j < G::B_LOADS; ++j) {
+      int pchunk = (j * G::NW + wave) * 64 + lane;
+      int k = pchunk / G::CB, pc = pchunk % G::CB;
+      int lc = pc ^ G::swz_b(k);
+      bool col_ok = n0 + lc * 8 < N;
+      b_off[j] = col_ok ? uint32_t(k) * uint32_t(N) * 2u + uint32_t(lc) * 16u : kOOB;
+      b_k[j] = col_ok ? k : (1 << 30);
+    }
+  }
+  // -- B gather plan (conv): the thread fills logical pixel chunk g_lc (8
+  // consecutive pixels) of B rows g_k0 + j*(THREADS/CB)
+  const int g_lc = threadIdx.x % G::CB;
+  const int g_k0 = threadIdx.x / G::CB;
+  int px_img[CONV ? 8 : 1], px_sr[CONV ? 8 : 1], px_iw[CONV ? 8 : 1];
+  if constexpr (CONV) {
+    const int plane = rows_t * p.OW;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int pix = n0 + g_lc * 8 + e;
+      const int n = pix / plane, rem = pix - n * plane;
+      const int oh_l = rem / p.OW, ow = rem - oh_l * p.OW;
+      const bool ok = pix < N;
+      px_img[e] = ok ? n * p.Cin * p.H * p.W : -1;
+      px_sr[e] = oh_l * p.sh;            // slice row of the window's first tap
+      px_iw[e] = ow * p.sw - p.pw;
+    }
+  }
+  i16x8 g_reg[CONV ? G::B_LOADS : 1];
+
+  const int nk = (K + G::BK - 1) / G::BK;
+
+  auto issue = [&](int kt, int stage) {
+    const int k0 = kt * G::BK;
+    char *sa = smem + stage * G::STAGE_BYTES;
+#pragma unroll
+    for (int j = 0; j < G::A_LOADS; ++j) {
+      uint32_t off = (k0 + a_kc[j] < K) ? a_off[j] + uint32_t(k0) * 2u : kOOB;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsA, (lds_void *)(sa + (j * G::NW + wave) * 1024), 16, off, 0, 0, 0);
+    }
+    if constexpr (!CONV) {
+      char *sb = sa + G::A_BYTES;
+#pragma unroll
+      for (int j = 0; j < G::B_LOADS; ++j) {
+        uint32_t off = (k0 + b_k[j] < K) ? b_off[j] + uint32_t(k0) * uint32_t(N) * 2u : kOOB;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsB, (lds_void *)(sb + (j * G::NW + wave) * 1024), 16, off, 0, 0, 0);
+      }
+    } else {
+      const int khw = p.kh * p.kw;
+      const int HW = p.H * p.W;
+      const int sr_lo = pt_sub, sr_hi = pt_sub + rows_in;   // slice rows holding data
+      const int row0 = in_start - pt_sub;                   // input row of slice row 0
+#pragma unroll
+      for (int j = 0; j < G::B_LOADS; ++j) {
+        const int k = k0 + g_k0 + j * (G::THREADS / G::CB);
+        const bool kok = k < K;
+        const int ci = kok ? k / khw : 0;
+        const int rs = k - ci * khw;
+        const int r = rs / p.kw, s = rs - r * p.kw;
+        const int kbase = ci * HW;
+        const int dr = r * p.dh, ds = s * p.dw;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int sr = px_sr[e] + dr;
+          const int iw = px_iw[e] + ds;
+          const bool ok = kok && px_img[e] >= 0 && sr >= sr_lo && sr < sr_hi && iw >= 0 && iw < p.W;
+          const uint32_t off = ok ? uint32_t(px_img[e] + kbase + (row0 + sr) * p.W + iw) * 2u : kOOB;
+          g_reg[j][e] = (short)__builtin_amdgcn_raw_buffer_load_b16(rsB, off, 0, 0);
+        }
+      }
+    }
+  };
+  // conv: write the gathered B rows of a stage (after its loads returned)
+  auto store_gather = [&](int stage) {
+    if constexpr (CONV) {
+      char *sb = smem + stage * G::STAGE_BYTES + G::A_BYTES;
+#pragma unroll
+      for (int j = 0; j < G::B_LOADS; ++j) {
+        const int kk = g_k0 + j * (G::THREADS / G::CB);
+        *(lds_i16x8 *)(sb + kk * G::BN * 2 + ((g_lc ^ G::swz_b(kk)) * 16)) = g_reg[j];
+      }
+    }
+  };
+
+  // -- per-lane fragment addresses (bytes within a stage)
+  // A: lane reads row (lane % MF) of each MFMA tile, logical chunk
+  //    q*(FK/8) + lane/MF; the swizzle depends only on lane % MF.
+  uint32_t fa[G::KSUB];
+  {
+    const int r = lane % MF;
+    const int x = G::swz_a(r);
+#pragma unroll
+    for (int q = 0; q < G::KSUB; ++q) {
+      int lc = q * (G::FK / 8) + lane / MF;
+      fa[q] = uint32_t((wr * G::WTM + r) * G::BK * 2 + ((lc ^ x) * 16));
+    }
+  }
+  // B (transpose read, 4 k-rows x 16 columns per 16-lane group): source lane
+  // s = lane % 16 points at row kbase + s/4, columns cbase + 4*(s%4) .. +3.
+  uint32_t fb[G::TN];
+  {
+    const int g = lane / 16, s = lane % 16;
+    int krow, ncol;
+    if (MF == 32) {
+      krow = (g / 2) * 8 + s / 4;
+      ncol = (g % 2) * 16 + 4 * (s % 4);
+    } else {
+      krow = g * 8 + s / 4;
+      ncol = 4 * (s % 4);
+    }
+    const int x = G::swz_b(krow);
+#pragma unroll
+    for (int nt = 0; nt < G::TN; ++nt) {
+      int n = wc * G::WTN + nt * MF + ncol;
+      int lc = n / 8;
+      fb[nt] = uint32_t(G::A_BYTES + krow * G::BN * 2 + ((lc ^ x) * 16) + (n % 8) * 2);
+    }
+  }
+
+  Acc acc[G::TM][G::TN];
+#pragma unroll
+  for (int i = 0; i < G::TM; ++i)
+#pragma unroll
+    for (int j = 0; j < G::TN; ++j) acc[i][j] = Acc{};
+
+  auto load_frags = [&](const char *st, int q, i16x8(&af)[G::TM], i16x8(&bf)[G::TN]) {
+#pragma unroll
+    for (int i = 0; i < G::TM; ++i) af[i] = *(const lds_i16x8 *)(st + fa[q] + i * MF * G::BK * 2);
+#pragma unroll
+    for (int j = 0; j < G::TN; ++j) {
+      const char *bp = st + fb[j] + q * G::FK * G::BN * 2;
+      i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(bp));
+      i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(bp + 4 * G::BN * 2));
+      bf[j] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+  };
+  auto mfmas = [&](const i16x8(&af)[G::TM], const i16x8(&bf)[G::TN]) {
+#pragma unroll
+    for (int i = 0; i < G::TM; ++i)
+#pragma unroll
+      for (int j = 0; j < G::TN; ++j) {
+        if constexpr (MF == 32) acc[i][j] = Mfma<T>::m32(af[i], bf[j], acc[i][j]);
+        else acc[i][j] = Mfma<T>::m16(af[i], bf[j], acc[i][j]);
+      }
+  };
+  // fragments of K step q+1 are read while the MFMAs of step q run
+  auto compute = [&](int stage) {
+    const char *st = smem + stage * G::STAGE_BYTES;
+    i16x8 af0[G::TM], bf0[G::TN], af1[G::TM], bf1[G::TN];
+    load_frags(st, 0, af0, bf0);
+#pragma unroll
+    for (int q = 0; q < G::KSUB; q += 2) {
+      if (q + 1 < G::KSUB) load_frags(st, q + 1, af1, bf1);
+      mfmas(af0, bf0);
+      if (q + 2 < G::KSUB) load_frags(st, q + 2, af0, bf0);
+      if (q + 1 < G::KSUB) mfmas(af1, bf1);
+    }
+  };
+
+  // -- prologue: stages 0 .. S-2 in flight
+#pragma unroll
+  for (int s = 0; s < S - 1; ++s)
+    if (s < nk) {
+      issue(s, s);
+      store_gather(s);
+    }
+
+  int kt = 0, cs = 0, ls = S - 1;
+  // steady state: tile kt has landed once only the S-2 younger tiles' loads
+  // are outstanding; the barrier publishes every wave's copy and frees stage
+  // ls (computed in the previous iteration) for tile kt+S-1.
+  for (; kt + S - 1 < nk; ++kt) {
+    wait_vmcnt_lgkm0<(S - 2) * G::LPW>();
+    block_barrier();
+    issue(kt + S - 1, ls);
+    compute(cs);
+    store_gather(ls);
+    cs = cs + 1 == S ? 0 : cs + 1;
+    ls = ls + 1 == S ? 0 : ls + 1;
+  }
+  // drain: nothing more to load; nk-1-kt younger tiles remain outstanding
+  for (; kt < nk; ++kt) {
+    const int pend = nk - 1 - kt;
+    if (S >= 4 && pend >= 2) wait_vmcnt_lgkm0<(S >= 4 ? 2 : 0) * G::LPW>();
+    else if (S >= 3 && pend >= 1) wait_vmcnt_lgkm0<(S >= 3 ? 1 : 0) * G::LPW>();
+    else wait_vmcnt_lgkm0<0>();
+    block_barrier();
+    compute(cs);
+    cs = cs + 1 == S ? 0 : cs + 1;
+  }
+
+  // -- epilogue
+  if constexpr (!CONV) {
+    const int64_t cbase = int64_t(bz) * p.batch_stride_c;
+    if (p.out_dtype == TSS_F32)
+      store_tile<G, float>(acc, reinterpret_cast<float *>(p.C) + cbase, m0, n0, wr, wc, lane, M, N);
+    else if (p.out_dtype == TSS_F16)
+      store_tile<G, _Float16>(acc, reinterpret_cast<_Float16 *>(p.C) + cbase, m0, n0, wr, wc, lane, M, N);
+    else
+      store_tile<G, __bf16>(acc, reinterpret_cast<__bf16 *>(p.C) + cbase, m0, n0, wr, wc, lane, M, N);
+  } else {
+    if (p.out_dtype == TSS_F32)
+      store_conv<G, float>(acc, reinterpret_cast<float *>(p.C), p, m0, n0, wr, wc, lane, o0, rows_t, N);
+    else if (p.out_dtype == TSS_F16)
+      store_conv<G, _Float16>(acc, reinterpret_cast<_Float16 *>(p.C), p, m0, n0, wr, wc, lane, o0, rows_t, N);
+    else
+      store_conv<G, __bf16>(acc, reinterpret_cast<__bf16 *>(p.C), p, m0, n0, wr, wc, lane, o0, rows_t, N);
+  }
+}
+
+}  // namespace tss

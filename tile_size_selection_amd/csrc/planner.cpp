@@ -1,0 +1,132 @@
+// C ABI of the tile planner (host only).  The arithmetic lives in planner.h.
+#include <algorithm>
+#include <vector>
+
+#include "planner.h"
+
+using namespace tss;
+
+namespace {
+
+bool valid_device(const tss_device &d) {
+  if (d.cores <= 0 || d.onchip_per_core <= 0 || d.onchip_per_block_max <= 0 || d.max_threads_per_core <= 0 ||
+      d.max_threads_per_block <= 0 || d.max_blocks_per_core <= 0 || d.lane_count <= 0 ||
+      d.reg_granule_per_lane <= 0 || d.acc_regs_max <= 0 || d.reg_overhead < 0)
+    return false;
+  if (d.reg_model == TSS_REG_POOLED) return d.regs_per_core > 0;
+  if (d.reg_model == TSS_REG_PER_SIMD)
+    return d.simds_per_core > 0 && d.regs_per_lane_per_simd > 0 && d.max_waves_per_simd > 0;
+  return false;
+}
+
+bool valid_config(const tss_tile_config &c, const tss_device &d) {
+  return c.bm > 0 && c.bn > 0 && c.bk > 0 && c.stages > 0 && c.threads > 0 && instr_on_device(c.instr, d);
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t tss_device_gfx950(tss_device *out) {
+  if (!out) return TSS_E_ARG;
+  *out = gfx950_device();
+  return TSS_OK;
+}
+
+int32_t tss_device_pages(int32_t sm_count, int32_t smem_kb, tss_device *out) {
+  if (!out || sm_count <= 0 || smem_kb <= 1 || smem_kb > (1 << 20)) return TSS_E_ARG;
+  *out = pages_device(sm_count, smem_kb);
+  return TSS_OK;
+}
+
+int32_t tss_evaluate(const tss_tile_config *cfg, const tss_device *dev, int64_t batch, int64_t M, int64_t N,
+                     int64_t K, int32_t elem_bytes, tss_verdict *out) {
+  const tss_device d = dev ? *dev : gfx950_device();
+  if (!cfg || !out || batch < 1 || M < 0 || N < 0 || K < 0 || elem_bytes < 1 || elem_bytes > 8) return TSS_E_ARG;
+  if (!valid_device(d) || !valid_config(*cfg, d)) return TSS_E_ARG;
+  if (M > (int64_t(1) << 40) || N > (int64_t(1) << 40) || K > (int64_t(1) << 40) || batch > (int64_t(1) << 20))
+    return TSS_E_ARG;
+  tss_verdict v = evaluate_block(*cfg, d, elem_bytes);
+  finish(v, d, batch, M, N, K, elem_bytes);
+  *out = v;
+  return TSS_OK;
+}
+
+int32_t tss_tile_plan(int64_t batch, int64_t M, int64_t N, int64_t K, int32_t elem_bytes, const tss_device *dev,
+                      int32_t instr_filter, tss_verdict *best, tss_verdict *list, int32_t cap,
+                      int32_t *n_feasible) {
+  const tss_device d = dev ? *dev : gfx950_device();
+  if (batch < 1 || M < 0 || N < 0 || K < 0 || elem_bytes < 1 || elem_bytes > 8 || cap < 0) return TSS_E_ARG;
+  if (M > (int64_t(1) << 40) || N > (int64_t(1) << 40) || K > (int64_t(1) << 40) || batch > (int64_t(1) << 20))
+    return TSS_E_ARG;
+  if (!valid_device(d)) return TSS_E_ARG;
+  if (instr_filter && !instr_on_device(instr_filter, d)) return TSS_E_ARG;
+  const Space s = space_for(d, instr_filter);
+  // A K step longer than K is skipped, unless K is shorter than every
+  // candidate step: then the shortest one is kept (its tail is masked).
+  const int64_t bk_cap = K > s.bk[0] ? K : s.bk[0];
+  std::vector<tss_verdict> feas;
+  feas.reserve(512);
+  for (int ii = 0; ii < s.ninstr; ++ii) {
+    Shape sh{};
+    instr_shape(s.instr[ii], sh);
+    for (int a = 0; a < s.nbm; ++a)
+      for (int b = 0; b < s.nbn; ++b)
+        for (int c = 0; c < s.nbk; ++c) {
+          if (s.bk[c] > bk_cap) continue;
+          for (int e = 0; e < s.nst; ++e)
+            for (int f = 0; f < s.nthr; ++f) {
+              if (s.threads[f] % sh.threads) continue;
+              tss_tile_config cfg{s.bm[a], s.bn[b], s.bk[c], s.stages[e], s.threads[f], s.instr[ii]};
+              tss_verdict v = evaluate_block(cfg, d, elem_bytes);
+              if (v.failures) continue;
+              finish(v, d, batch, M, N, K, elem_bytes);
+              feas.push_back(v);
+            }
+        }
+  }
+  std::stable_sort(feas.begin(), feas.end(), [&](const tss_verdict &x, const tss_verdict &y) {
+    return key_less(rank_key(x, d), rank_key(y, d));
+  });
+  if (n_feasible) *n_feasible = int32_t(feas.size());
+  if (list)
+    for (int32_t i = 0; i < cap && i < int32_t(feas.size()); ++i) list[i] = feas[i];
+  if (feas.empty()) return TSS_E_INFEASIBLE;
+  if (best) *best = feas[0];
+  return TSS_OK;
+}
+
+int32_t tss_hw_tile(int64_t H, int64_t kh, int64_t sh, int64_t pt, int64_t d, int64_t o0, int64_t o1,
+                    tss_hw_slice *out) {
+  if (!out || H <= 0 || kh <= 0 || sh <= 0 || pt < 0 || d <= 0 || o0 < 0 || o1 <= o0) return TSS_E_ARG;
+  const int64_t lim = int64_t(1) << 40;
+  if (H > lim || kh > lim || sh > lim || pt > lim || d > lim || o1 > lim) return TSS_E_ARG;
+  // "Tiling（分块）" page, H/W tiling formulas (1)..(5)
+  const int64_t window = (kh - 1) * d + 1;
+  tss_hw_slice s{};
+  s.o0 = o0;
+  s.o1 = o1;
+  s.in_start = std::max<int64_t>(0, o0 * sh - pt);
+  s.in_end = (o1 - 1) * sh - pt + window;
+  s.in_span = s.in_end - s.in_start;
+  s.pt = std::max<int64_t>(0, pt - o0 * sh);
+  s.pb = std::max<int64_t>(0, s.in_end - H);
+  s.halo = window - sh;
+  *out = s;
+  return TSS_OK;
+}
+
+const char *tss_status_string(int32_t status) {
+  switch (status) {
+    case TSS_OK: return "ok";
+    case TSS_E_ARG: return "invalid argument";
+    case TSS_E_DTYPE: return "unsupported dtype";
+    case TSS_E_ALIGN: return "pointer or row stride not 16-byte aligned";
+    case TSS_E_INFEASIBLE: return "tile configuration infeasible";
+    case TSS_E_HIP: return "HIP runtime error";
+    case TSS_E_UNSUPPORTED: return "no compiled kernel for this configuration";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,50 @@
+// Table of compiled kernels.  Each instantiation unit contributes the kernels
+// of one (input dtype, operation, BM) slice of the gfx950 candidate space;
+// a shape is compiled exactly when the planner's C3/C1/C2/occupancy checks
+// pass for it at the lightest pipeline depth (planner.h,
+// kernel_shape_needed), so every feasible configuration has a kernel.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "gemm_kernel.h"
+
+namespace tss {
+
+using Launch = hipError_t (*)(const KernelArgs &, dim3 grid, int lds_bytes, hipStream_t s);
+
+struct KernelEntry {
+  int32_t bm, bn, bk, stages, threads, instr, dtype, op;  // op 0 = GEMM, 1 = conv
+  Launch launch;
+  int32_t stage_bytes;
+};
+
+struct KernelTable {
+  const KernelEntry *entries;
+  int n;
+};
+
+// Defined by the instantiation units.
+KernelTable table_gemm_f16_bm64();
+KernelTable table_gemm_f16_bm128();
+KernelTable table_gemm_f16_bm256();
+KernelTable table_gemm_bf16_bm64();
+KernelTable table_gemm_bf16_bm128();
+KernelTable table_gemm_bf16_bm256();
+KernelTable table_conv_f16_bm64();
+KernelTable table_conv_f16_bm128();
+KernelTable table_conv_f16_bm256();
+KernelTable table_conv_bf16_bm64();
+KernelTable table_conv_bf16_bm128();
+KernelTable table_conv_bf16_bm256();
+
+template <typename G, typename T, bool CONV>
+hipError_t launch_kernel(const KernelArgs &a, dim3 grid, int lds_bytes, hipStream_t s) {
+  static const hipError_t attr = hipFuncSetAttribute((const void *)tiled_gemm_kernel<G, T, CONV>,
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize, 163840);
+  if (attr != hipSuccess) return attr;
+  hipLaunchKernelGGL((tiled_gemm_kernel<G, T, CONV>), grid, dim3(G::THREADS), lds_bytes, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace tss
