@@ -1,0 +1,184 @@
+#!/usr/bin/env python3
+"""Headline benchmark: fp16 GEMM at M = N = K = 4096 on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+One step is one pass of the hot path over the resident synthetic operands:
+the tile decision (the planner's choice, cached per shape after its first
+evaluation) and the tiled GEMM kernel it selects, launched through the C ABI
+on the current stream.  Prints one JSON line.
+
+The timed region holds exactly `steps` launches, bracketed by
+torch.cuda.synchronize(); HIP events recorded on the launch stream give the
+average kernel duration the roofline figure uses.  Beside it: the convolution
+workload (8x256x56x56, 3x3, stride 2, pad 1, H-tiles of 8 output rows) timed
+the same way, and the oracle timed on the host cores on a bounded sample.
+"""
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_F16_TFLOPS = 2516.6      # MI355X dense fp16/bf16 MFMA: 256 CU x 4096 FLOP/clk x 2.4 GHz
+COUNTER_PROFILE = os.path.join(ROOT, "profiles", "gemm_f16_4096_counters.md")
+KERNEL_SOURCES = [os.path.join(ROOT, "tile_size_selection_amd", "csrc", f)
+                  for f in ("gemm_kernel.h", "registry.h", "instances.inc")]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def profiled_traffic(cfg_str: str):
+    """HBM bytes per launch from the committed counter summary, if it was
+    taken on the current kernel source and tile configuration."""
+    if not os.path.exists(COUNTER_PROFILE):
+        return None
+    txt = open(COUNTER_PROFILE, encoding="utf-8").read()
+    kv = dict(re.findall(r"^(\w+):\s*(\S+)\s*$", txt, flags=re.M))
+    if kv.get("kernel_source_hash") != kernel_source_hash() or kv.get("config") != cfg_str:
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(A, B, budget_s: float = 12.0):
+    """The fp64 oracle on the host cores, on the first rows of the same
+    problem: a short calibration run sizes the sample to about budget_s."""
+    from oracle import gemm_conv as G
+    Ad = A.double().numpy()
+    Bd = B.double().numpy()
+    K, N = Bd.shape
+    t0 = time.perf_counter()
+    G.gemm(Ad[:4], Bd)
+    dt = max(time.perf_counter() - t0, 1e-6)
+    rows = int(min(A.shape[0], max(4, budget_s / dt * 4)))
+    t0 = time.perf_counter()
+    G.gemm(Ad[:rows], Bd)
+    dt = time.perf_counter() - t0
+    flops = 2.0 * rows * N * K
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": G.threads(), "kind": "oracle",
+            "sample": f"first {rows} of {A.shape[0]} rows of the 4096^3 problem (C and sum|a*b| in fp64), "
+                      f"{dt:.1f} s wall"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=30)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for {args.gpus}); the GEMM shards by output tiles "
+              "with no exchange, so a multi-GPU figure is N independent single-GPU runs.", file=sys.stderr)
+        return 2
+
+    import torch
+    import tile_size_selection_amd as tss
+    from tile_size_selection_amd.inputs import WORKLOADS
+
+    w = WORKLOADS[2]
+    A, B = w.make()
+    dA, dB = A.to("cuda:0"), B.to("cuda:0")
+    out = torch.empty((w.M, w.N), dtype=torch.float16, device="cuda:0")
+    cfg = tss.default_config(w.M, w.N, w.K, w.batch, w.dtype)
+    stream = torch.cuda.current_stream()
+
+    # warm-up (also brings the clocks up)
+    for _ in range(args.warmup):
+        tss.gemm(dA, dB, out=out)
+    torch.cuda.synchronize()
+
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        tss.gemm(dA, dB, out=out)          # planner choice (cached) + kernel
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ev_ms = e0.elapsed_time(e1)
+    ms_per_step = ev_ms / args.steps
+    flops = w.flops()
+    tflops = flops / (ms_per_step * 1e-3) / 1e12
+
+    # a few sampled entries against the oracle (outside the timed region)
+    from oracle import gemm_conv as G
+    import numpy as np
+    rng = np.random.default_rng(0)
+    i, j = rng.integers(0, w.M, 64), rng.integers(0, w.N, 64)
+    ref, S = G.gemm_entries(A.double().numpy(), B.double().numpy(), np.zeros(64, np.int64), i, j)
+    got = out[torch.from_numpy(i).cuda(), torch.from_numpy(j).cuda()].double().cpu().numpy()
+    parity_ok = bool(np.all(np.abs(got - ref) <= 5e-3 * S + 1e-3))
+
+    # the convolution workload, same timing method
+    cw = WORKLOADS[5]
+    x, wt = cw.make()
+    dx, dwt = x.to("cuda:0"), wt.to("cuda:0")
+    y = tss.conv2d(dx, dwt, cw.stride, cw.pad, cw.dil, tile_oh=cw.tile_oh, out_dtype=cw.out_dtype)
+    for _ in range(10):
+        tss.conv2d(dx, dwt, cw.stride, cw.pad, cw.dil, tile_oh=cw.tile_oh, out_dtype=cw.out_dtype, out=y)
+    torch.cuda.synchronize()
+    c0 = torch.cuda.Event(enable_timing=True)
+    c1 = torch.cuda.Event(enable_timing=True)
+    nconv = 100
+    c0.record(stream)
+    for _ in range(nconv):
+        tss.conv2d(dx, dwt, cw.stride, cw.pad, cw.dil, tile_oh=cw.tile_oh, out_dtype=cw.out_dtype, out=y)
+    c1.record(stream)
+    torch.cuda.synchronize()
+    conv_us = c0.elapsed_time(c1) / nconv * 1e3
+    OH = OW = 28
+    conv_flops = 2 * cw.N * cw.Co * OH * OW * cw.C * cw.kh * cw.kw
+    conv_cfg = tss.default_config(cw.Co, cw.N * OH * OW, cw.C * cw.kh * cw.kw)
+
+    cfg_str = f"{cfg.bm}x{cfg.bn}x{cfg.bk}/s{cfg.stages}/t{cfg.threads}/{cfg.instr}"
+    achieved = flops / (ms_per_step * 1e-3) / 1e12
+    line = {
+        "metric": "fp16 GEMM TFLOP/s at 4096^3 and % of MI355X dense MFMA peak",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": "gemm_f16_4096: C = A x B, M=N=K=4096, fp16 row-major operands U[-1,1] "
+                               "(seeds 2000/2001), fp32 accumulation, fp16 output",
+                   "tile": cfg_str, "parallelism": "single GPU", "wall_s": round(wall, 4),
+                   "sampled_parity_ok": parity_ok},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_F16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_F16_TFLOPS, 4),
+                     "traffic": profiled_traffic(cfg_str)},
+        "conv": {"workload": "conv_f16_n8c256h56_k3s2p1 (tileOh 8, fp32 out)", "us": round(conv_us, 2),
+                 "tflops": round(conv_flops / (conv_us * 1e-6) / 1e12, 2),
+                 "tile": f"{conv_cfg.bm}x{conv_cfg.bn}x{conv_cfg.bk}/s{conv_cfg.stages}/t{conv_cfg.threads}/"
+                         f"{conv_cfg.instr}"},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(A, B)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

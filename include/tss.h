@@ -166,7 +166,7 @@ int32_t tss_evaluate(const tss_tile_config *cfg, const tss_device *dev, int64_t 
  *   gfx950 model: BM, BN in {64, 128, 256}, BK in {16, 32, 64}, stages 2..4,
  *                 threads {128, 256, 512}, both MFMA shapes (or the one in
  *                 instr_filter); key (C4 warning?, round(traffic), -blocks/CU,
- *                 -BK, -stages, threads, LDS bytes).
+ *                 -resident waves/CU, -BK, -stages, LDS bytes).
  * instr_filter: 0 = every shape of the device, else one TSS_INSTR_*.
  * best (nullable) receives the top verdict; list (nullable) the first
  * min(cap, n) verdicts in rank order; *n_feasible (nullable) the count.

@@ -29,6 +29,9 @@
  */
 #include <math.h>
 #include <stdint.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
 #include <stdlib.h>
 #include <string.h>
 
@@ -147,4 +150,13 @@ int oracle_conv2d_htiled(int64_t N, int64_t Ci, int64_t H, int64_t W, int64_t Co
     free(xs);
   }
   return 0;
+}
+
+/* Threads the OpenMP loops above run on. */
+int oracle_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
 }

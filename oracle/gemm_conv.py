@@ -47,6 +47,8 @@ def lib():
         L.oracle_conv2d.restype = None
         L.oracle_conv2d_htiled.argtypes = [i64] * 14 + [ip, dp, dp, dp]
         L.oracle_conv2d_htiled.restype = ctypes.c_int
+        L.oracle_threads.argtypes = []
+        L.oracle_threads.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -124,3 +126,8 @@ def conv2d_htiled(x, w, stride=(1, 1), pad=(0, 0), dil=(1, 1), tile_oh: int = 8)
     if rc != 0:
         raise RuntimeError(f"H-tile slice table is inconsistent (rc={rc})")
     return y
+
+
+def threads() -> int:
+    """OpenMP threads the oracle loops use."""
+    return int(lib().oracle_threads())

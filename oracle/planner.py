@@ -310,15 +310,18 @@ def rank_key(v: Verdict, dev: DeviceModel):
     pages: least modelled DRAM traffic, then most resident blocks, then least
     shared memory (the tile_decision.py page's shortlist order).
     gfx950: candidates without a C4 warning first; then least traffic and most
-    resident blocks as on the pages; then, as the Tiling page's rules of thumb
-    advise when on-chip memory has room, the larger block_K and the deeper
-    pipeline; then fewer threads and less LDS.
+    resident blocks as on the pages; then the most resident waves per CU
+    (occupancy, the Tiling page's third constraint: low occupancy leaves the
+    compute units idle while waves wait on memory); then, as that page's
+    rules of thumb advise when on-chip memory has room, the larger block_K and
+    the deeper pipeline; then less LDS.
     """
     t = round_half_even(v.traffic)
     if dev.ranking == "pages":
         return (t, -v.blocks_per_core, v.smem_total)
     c = v.config
-    return (1 if v.warnings else 0, t, -v.blocks_per_core, -c.block_k, -c.stages, c.threads, v.smem_total)
+    resident_waves = v.blocks_per_core * (c.threads // dev.lane_count)
+    return (1 if v.warnings else 0, t, -v.blocks_per_core, -resident_waves, -c.block_k, -c.stages, v.smem_total)
 
 
 def candidates(dev: DeviceModel, k: int, instrs: Sequence[str]):

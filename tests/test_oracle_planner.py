@@ -197,3 +197,14 @@ def test_short_k_keeps_the_shortest_step():
     assert P.sweep(64, 64, 0, g, ["mfma32"])
     pages = P.sweep(4096, 4096, 8, P.device_pages(), ["wgmma"])
     assert {v.config.block_k for v in pages} == {16}
+
+
+def test_gfx950_rank_prefers_occupancy_then_bigger_k_step():
+    """4096^3: every 256x256 tile ties on traffic and on one block per CU;
+    512 threads keep 8 waves resident (25% of 32) against 4 for 256 threads,
+    and among those the 64-deep K step wins."""
+    g = P.device_gfx950()
+    res = P.sweep(4096, 4096, 4096, g, ["mfma32", "mfma16"])
+    c = res[0].config
+    assert (c.block_m, c.block_n, c.block_k, c.stages, c.threads, c.instr) == (256, 256, 64, 2, 512, "mfma32")
+    assert P.rank_key(res[0], g)[3] == -8

@@ -1,0 +1,109 @@
+"""Measured sweep over the planner's candidate tiles (the autotuning loop of
+the "Tiling（分块）" page: enumerate the candidates, drop the ones that break
+a hardware constraint, time every survivor on the device, keep the fastest).
+
+    python -m tile_size_selection_amd.autotune --m 4096 --n 4096 --k 4096 [--out report.md]
+
+Prints, for every feasible configuration, its measured time and TFLOP/s, its
+rank in the planner's order, and how the planner's first choice compares with
+the fastest measured one.
+"""
+from __future__ import annotations
+
+import argparse
+import sys
+import time
+from typing import List, Optional, Tuple
+
+import torch
+
+from . import api
+from .inputs import draw
+
+
+def time_config(A, B, out, cfg, iters: int, warmup: int) -> float:
+    for _ in range(warmup):
+        api.gemm(A, B, cfg=cfg, out=out)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(iters):
+        api.gemm(A, B, cfg=cfg, out=out)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / iters * 1e3  # microseconds
+
+
+def sweep(M: int, N: int, K: int, batch: int = 1, dtype: str = "f16", out_dtype: Optional[str] = None,
+          iters: int = 20, warmup: int = 5, rounds: int = 2) -> Tuple[List[dict], dict]:
+    best, ranked, n = api.tile_plan(M, N, K, batch=batch, cap=1024)
+    shapeA = (batch, M, K) if batch > 1 else (M, K)
+    shapeB = (batch, K, N) if batch > 1 else (K, N)
+    A = draw(shapeA, "uniform", -1, 1, dtype, 2000).cuda()
+    B = draw(shapeB, "uniform", -1, 1, dtype, 2001).cuda()
+    od = out_dtype or dtype
+    tdt = {"f16": torch.float16, "bf16": torch.bfloat16, "f32": torch.float32}[od]
+    out = torch.empty(((batch,) if batch > 1 else ()) + (M, N), dtype=tdt, device="cuda")
+    # bring the clocks up before the first measurement
+    t_end = time.time() + 1.0
+    while time.time() < t_end:
+        api.gemm(A, B, cfg=ranked[0]["config"], out=out)
+    torch.cuda.synchronize()
+    rows = []
+    for rank, v in enumerate(ranked):
+        rows.append({"rank": rank, "config": v["config"], "verdict": v, "us": float("inf")})
+    # several rounds, interleaved, keep each config's best round
+    for _ in range(rounds):
+        for r in rows:
+            r["us"] = min(r["us"], time_config(A, B, out, r["config"], iters, warmup))
+    flops = 2.0 * batch * M * N * K
+    for r in rows:
+        r["tflops"] = flops / (r["us"] * 1e-6) / 1e12
+    fastest = min(rows, key=lambda r: r["us"])
+    summary = {"n_feasible": n, "planner": rows[0], "fastest": fastest,
+               "planner_over_fastest": rows[0]["us"] / fastest["us"]}
+    return rows, summary
+
+
+def report(M, N, K, batch, rows, summary) -> str:
+    c = lambda cfg: f"{cfg.bm}x{cfg.bn}x{cfg.bk} s{cfg.stages} t{cfg.threads} {cfg.instr}"
+    lines = [f"# Measured tile sweep: GEMM {batch}x{M}x{N}x{K}", "",
+             f"feasible candidates: {summary['n_feasible']}",
+             f"planner's choice: {c(summary['planner']['config'])}: {summary['planner']['us']:.1f} us "
+             f"({summary['planner']['tflops']:.1f} TFLOP/s)",
+             f"fastest measured: {c(summary['fastest']['config'])} (planner rank {summary['fastest']['rank']}): "
+             f"{summary['fastest']['us']:.1f} us ({summary['fastest']['tflops']:.1f} TFLOP/s)",
+             f"planner time / fastest time: {summary['planner_over_fastest']:.4f}", "",
+             "| planner rank | config | us | TFLOP/s | LDS KiB | blocks/CU | waves | C4 warnings |",
+             "|---|---|---|---|---|---|---|---|"]
+    for r in sorted(rows, key=lambda r: r["us"]):
+        v = r["verdict"]
+        lines.append(f"| {r['rank']} | {c(r['config'])} | {r['us']:.1f} | {r['tflops']:.1f} | "
+                     f"{v['smem_total'] / 1024:.0f} | {v['blocks_per_core']} | {v['waves']} | "
+                     f"{','.join(v['warnings']) or '-'} |")
+    return "\n".join(lines) + "\n"
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--m", type=int, default=4096)
+    ap.add_argument("--n", type=int, default=4096)
+    ap.add_argument("--k", type=int, default=4096)
+    ap.add_argument("--batch", type=int, default=1)
+    ap.add_argument("--dtype", default="f16")
+    ap.add_argument("--out-dtype", default=None)
+    ap.add_argument("--iters", type=int, default=20)
+    ap.add_argument("--out", default=None)
+    a = ap.parse_args()
+    rows, summary = sweep(a.m, a.n, a.k, a.batch, a.dtype, a.out_dtype, a.iters)
+    txt = report(a.m, a.n, a.k, a.batch, rows, summary)
+    if a.out:
+        with open(a.out, "w") as f:
+            f.write(txt)
+    print("\n".join(txt.splitlines()[:8]), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -11,9 +11,15 @@
 //
 // Memory-hierarchy techniques of the same page, in their gfx950 form:
 //   * staging with a multi-stage pipeline: `stages` LDS buffers in a ring;
-//     K tile t+stages-1 is in flight while tile t is computed.  The copy is a
-//     direct HBM->LDS buffer load (buffer_load_dwordx4 ... lds) that bypasses
-//     registers, the analogue of the page's asynchronous copy;
+//     K tile t+stages-1 is in flight while tile t is computed.  With three or
+//     four stages the copy is a direct HBM->LDS buffer load
+//     (buffer_load_dwordx4 ... lds) that bypasses registers, the analogue of
+//     the page's asynchronous copy, so several tiles are in flight without
+//     holding registers.  With two stages (double buffering) the tile goes
+//     through registers (buffer_load_dwordx4, then ds_write_b128 once the
+//     current tile's MFMAs are issued), the page's older HBM -> register ->
+//     shared-memory path: on gfx950 it measured faster than the direct copy
+//     for this depth;
 //   * coalescing: each load instruction moves 64 lanes x 16 B = 1 KiB of whole
 //     rows;
 //   * bank-conflict-free LDS: 16-byte chunks are XOR-swizzled per row (the
@@ -174,27 +180,92 @@ __device__ __forceinline__ O convert_out(float v) {
   else return __builtin_bit_cast(__bf16, f32_to_bf16_rne(v));
 }
 
-template <typename G, typename O, typename Acc>
-__device__ __forceinline__ void store_tile(const Acc (&acc)[G::TM][G::TN], O *C, int m0, int n0, int wr, int wc,
-                                           int lane, int M, int N) {
-  constexpr int MF = G::MF;
-  constexpr int NACC = AccType<MF>::n;
-#pragma unroll
-  for (int i = 0; i < G::TM; ++i)
-#pragma unroll
-    for (int j = 0; j < G::TN; ++j) {
-      const int col = n0 + wc * G::WTN + j * MF + lane % MF;
-      const int rbase = m0 + wr * G::WTM + i * MF + (MF == 32 ? (lane / 32) * 4 : (lane / 16) * 4);
-      if (col < N) {
-#pragma unroll
-        for (int e = 0; e < NACC; ++e) {
-          const int row = rbase + (MF == 32 ? (e / 4) * 8 + (e % 4) : e);
-          if (row < M) C[int64_t(row) * N + col] = convert_out<O>(acc[i][j][e]);
-        }
-      }
-    }
+// Accumulator layout (B fragment as the MFMA row operand): register e of
+// MFMA tile (i, j) holds C[row][col] with
+//   row = wave row base + i*MF + lane % MF
+//   col = wave col base + j*MF + c4(e, lane) + e % 4,
+//   c4  = (e/4)*8 + (lane/32)*4 for 32x32 tiles, (lane/16)*4 for 16x16 tiles,
+// so every group of 4 registers is 4 consecutive columns of one row.
+template <int MF>
+__device__ __forceinline__ int acc_col4(int e4, int lane) {
+  return MF == 32 ? e4 * 8 + (lane / 32) * 4 : (lane / 16) * 4;
 }
 
+template <typename O>
+struct Vec4 {
+  typedef O type __attribute__((ext_vector_type(4)));
+};
+
+// Epilogue staged through LDS: each wave converts one MFMA row of its
+// sub-tile (MF rows x WTN columns) into a private LDS area, then stores it
+// with 16-byte, row-contiguous global writes.  The row pitch is padded by
+// 16 bytes so the 4-column writes of 32 consecutive rows hit distinct banks.
+template <typename G, typename O>
+struct LdsEpilogue {
+  static constexpr int PITCH = G::WTN * int(sizeof(O)) + 16;
+  static constexpr int WAVE_BYTES = G::MF * PITCH;
+  static constexpr bool fits = G::NW * WAVE_BYTES <= G::ST * G::STAGE_BYTES;
+};
+
+template <typename G, typename O, typename Acc>
+__device__ __forceinline__ void store_tile(const Acc (&acc)[G::TM][G::TN], O *C, char *smem, int m0, int n0,
+                                           int wave, int wr, int wc, int lane, int M, int N) {
+  constexpr int MF = G::MF;
+  constexpr int NACC = AccType<MF>::n;
+  using V4 = typename Vec4<O>::type;
+  if constexpr (LdsEpilogue<G, O>::fits) {
+    using E = LdsEpilogue<G, O>;
+    char *area = smem + wave * E::WAVE_BYTES;
+    constexpr int ELEMS16 = 16 / int(sizeof(O));        // elements per 16-byte chunk
+    constexpr int CPR = G::WTN / ELEMS16;                // chunks per row
+    constexpr int CHUNKS = MF * CPR;
+    block_barrier();  // every wave is done with the last stage's fragments
+#pragma unroll
+    for (int i = 0; i < G::TM; ++i) {
+#pragma unroll
+      for (int j = 0; j < G::TN; ++j)
+#pragma unroll
+        for (int e4 = 0; e4 < NACC / 4; ++e4) {
+          V4 v;
+          v[0] = convert_out<O>(acc[i][j][e4 * 4 + 0]);
+          v[1] = convert_out<O>(acc[i][j][e4 * 4 + 1]);
+          v[2] = convert_out<O>(acc[i][j][e4 * 4 + 2]);
+          v[3] = convert_out<O>(acc[i][j][e4 * 4 + 3]);
+          const int col = j * MF + acc_col4<MF>(e4, lane);
+          *(__attribute__((address_space(3))) V4 *)(area + (lane % MF) * E::PITCH + col * int(sizeof(O))) = v;
+        }
+#pragma unroll
+      for (int c = 0; c < (CHUNKS + 63) / 64; ++c) {
+        const int chunk = c * 64 + lane;
+        if (CHUNKS % 64 && chunk >= CHUNKS) break;
+        const int r = chunk / CPR, cc = chunk % CPR;
+        const i16x8 v = *(const lds_i16x8 *)(area + r * E::PITCH + cc * 16);
+        const int row = m0 + wr * G::WTM + i * MF + r;
+        const int col = n0 + wc * G::WTN + cc * ELEMS16;
+        if (row < M && col < N) *(i16x8 *)(C + int64_t(row) * N + col) = v;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < G::TM; ++i) {
+      const int row = m0 + wr * G::WTM + i * MF + lane % MF;
+      if (row >= M) continue;
+#pragma unroll
+      for (int j = 0; j < G::TN; ++j)
+#pragma unroll
+        for (int e4 = 0; e4 < NACC / 4; ++e4) {
+          const int col = n0 + wc * G::WTN + j * MF + acc_col4<MF>(e4, lane);
+          if (col >= N) continue;  // N % 4 == 0: the 4 columns are all in or all out
+          V4 v;
+          v[0] = convert_out<O>(acc[i][j][e4 * 4 + 0]);
+          v[1] = convert_out<O>(acc[i][j][e4 * 4 + 1]);
+          v[2] = convert_out<O>(acc[i][j][e4 * 4 + 2]);
+          v[3] = convert_out<O>(acc[i][j][e4 * 4 + 3]);
+          *(V4 *)(C + int64_t(row) * N + col) = v;
+        }
+    }
+  }
+}
 
 // Convolution epilogue: row = output channel, column = pixel of the H-tile
 // (image n, output row o0 + oh_l, output column ow); y is NCHW.
@@ -206,21 +277,19 @@ __device__ __forceinline__ void store_conv(const Acc (&acc)[G::TM][G::TN], O *y,
   const int plane = rows_t * p.OW;
   const int64_t chan = int64_t(p.OH) * p.OW;
 #pragma unroll
-  for (int j = 0; j < G::TN; ++j) {
-    const int pix = n0 + wc * G::WTN + j * MF + lane % MF;
-    if (pix >= npix) continue;
-    const int n = pix / plane, rem = pix - n * plane;
-    const int oh = o0 + rem / p.OW, ow = rem % p.OW;
-    O *base = y + (int64_t(n) * p.M) * chan + int64_t(oh) * p.OW + ow;
+  for (int i = 0; i < G::TM; ++i) {
+    const int co = m0 + wr * G::WTM + i * MF + lane % MF;
+    if (co >= p.M) continue;
 #pragma unroll
-    for (int i = 0; i < G::TM; ++i) {
-      const int rbase = m0 + wr * G::WTM + i * MF + (MF == 32 ? (lane / 32) * 4 : (lane / 16) * 4);
+    for (int j = 0; j < G::TN; ++j)
 #pragma unroll
       for (int e = 0; e < NACC; ++e) {
-        const int co = rbase + (MF == 32 ? (e / 4) * 8 + (e % 4) : e);
-        if (co < p.M) base[int64_t(co) * chan] = convert_out<O>(acc[i][j][e]);
+        const int pix = n0 + wc * G::WTN + j * MF + acc_col4<MF>(e / 4, lane) + e % 4;
+        if (pix >= npix) continue;
+        const int n = pix / plane, rem = pix - n * plane;
+        const int oh = o0 + rem / p.OW, ow = rem - (rem / p.OW) * p.OW;
+        y[(int64_t(n) * p.M + co) * chan + int64_t(oh) * p.OW + ow] = convert_out<O>(acc[i][j][e]);
       }
-    }
   }
 }
 
@@ -327,6 +396,9 @@ __global__ __launch_bounds__(G::THREADS) void tiled_gemm_kernel(KernelArgs p) {
     }
   }
   i16x8 g_reg[CONV ? G::B_LOADS : 1];
+  // two-stage ring: the next tile's copy is staged in registers
+  constexpr bool REG_COPY = S == 2;
+  i16x8 ra[REG_COPY ? G::A_LOADS : 1], rb[(REG_COPY && !CONV) ? G::B_LOADS : 1];
 
   const int nk = (K + G::BK - 1) / G::BK;
 
@@ -336,14 +408,21 @@ __global__ __launch_bounds__(G::THREADS) void tiled_gemm_kernel(KernelArgs p) {
 #pragma unroll
     for (int j = 0; j < G::A_LOADS; ++j) {
       uint32_t off = (k0 + a_kc[j] < K) ? a_off[j] + uint32_t(k0) * 2u : kOOB;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsA, (lds_void *)(sa + (j * G::NW + wave) * 1024), 16, off, 0, 0, 0);
+      if constexpr (REG_COPY)
+        ra[j] = __builtin_bit_cast(i16x8, __builtin_amdgcn_raw_buffer_load_b128(rsA, off, 0, 0));
+      else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsA, (lds_void *)(sa + (j * G::NW + wave) * 1024), 16, off, 0, 0, 0);
     }
     if constexpr (!CONV) {
       char *sb = sa + G::A_BYTES;
 #pragma unroll
       for (int j = 0; j < G::B_LOADS; ++j) {
         uint32_t off = (k0 + b_k[j] < K) ? b_off[j] + uint32_t(k0) * uint32_t(N) * 2u : kOOB;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsB, (lds_void *)(sb + (j * G::NW + wave) * 1024), 16, off, 0, 0, 0);
+        if constexpr (REG_COPY)
+          rb[j] = __builtin_bit_cast(i16x8, __builtin_amdgcn_raw_buffer_load_b128(rsB, off, 0, 0));
+        else
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rsB, (lds_void *)(sb + (j * G::NW + wave) * 1024), 16, off, 0, 0,
+                                                   0);
       }
     } else {
       const int khw = p.kh * p.kw;
@@ -370,8 +449,20 @@ __global__ __launch_bounds__(G::THREADS) void tiled_gemm_kernel(KernelArgs p) {
       }
     }
   };
-  // conv: write the gathered B rows of a stage (after its loads returned)
-  auto store_gather = [&](int stage) {
+  // write the register-staged part of a stage (after its loads returned):
+  // the two-stage ring's A and B chunks at the positions the direct copy
+  // would use, and the convolution's gathered B rows
+  auto store_staged = [&](int stage) {
+    if constexpr (REG_COPY) {
+      char *sa = smem + stage * G::STAGE_BYTES;
+#pragma unroll
+      for (int j = 0; j < G::A_LOADS; ++j) *(lds_i16x8 *)(sa + (j * G::NW + wave) * 1024 + lane * 16) = ra[j];
+      if constexpr (!CONV) {
+        char *sb = sa + G::A_BYTES;
+#pragma unroll
+        for (int j = 0; j < G::B_LOADS; ++j) *(lds_i16x8 *)(sb + (j * G::NW + wave) * 1024 + lane * 16) = rb[j];
+      }
+    }
     if constexpr (CONV) {
       char *sb = smem + stage * G::STAGE_BYTES + G::A_BYTES;
 #pragma unroll
@@ -439,11 +530,16 @@ __global__ __launch_bounds__(G::THREADS) void tiled_gemm_kernel(KernelArgs p) {
     for (int i = 0; i < G::TM; ++i)
 #pragma unroll
       for (int j = 0; j < G::TN; ++j) {
-        if constexpr (MF == 32) acc[i][j] = Mfma<T>::m32(af[i], bf[j], acc[i][j]);
-        else acc[i][j] = Mfma<T>::m16(af[i], bf[j], acc[i][j]);
+        // B fragment as the MFMA's row operand: the accumulator then holds
+        // C^T, i.e. each lane owns 4 consecutive columns of one C row
+        if constexpr (MF == 32) acc[i][j] = Mfma<T>::m32(bf[j], af[i], acc[i][j]);
+        else acc[i][j] = Mfma<T>::m16(bf[j], af[i], acc[i][j]);
       }
   };
-  // fragments of K step q+1 are read while the MFMAs of step q run
+  // Fragments of K step q+1 are read while the MFMAs of step q run.  The
+  // schedule is pinned: each LDS fragment read is issued right after an
+  // MFMA, spread evenly over the step, so the reads overlap the matrix
+  // pipeline instead of stalling it just before each MFMA.
   auto compute = [&](int stage) {
     const char *st = smem + stage * G::STAGE_BYTES;
     i16x8 af0[G::TM], bf0[G::TN], af1[G::TM], bf1[G::TN];
@@ -455,6 +551,19 @@ __global__ __launch_bounds__(G::THREADS) void tiled_gemm_kernel(KernelArgs p) {
       if (q + 2 < G::KSUB) load_frags(st, q + 2, af0, bf0);
       if (q + 1 < G::KSUB) mfmas(af1, bf1);
     }
+    constexpr int NMF = G::TM * G::TN, NDS = G::TM + 2 * G::TN;
+    __builtin_amdgcn_sched_group_barrier(0x100, NDS, 0);  // first step's fragments
+#pragma unroll
+    for (int q = 0; q + 1 < G::KSUB; ++q) {
+#pragma unroll
+      for (int i = 0; i < NMF; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+        const int nds = (i + 1) * NDS / NMF - i * NDS / NMF;
+#pragma unroll
+        for (int d = 0; d < nds; ++d) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+      }
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, NMF, 0);  // last step
   };
 
   // -- prologue: stages 0 .. S-2 in flight
@@ -462,7 +571,7 @@ __global__ __launch_bounds__(G::THREADS) void tiled_gemm_kernel(KernelArgs p) {
   for (int s = 0; s < S - 1; ++s)
     if (s < nk) {
       issue(s, s);
-      store_gather(s);
+      store_staged(s);
     }
 
   int kt = 0, cs = 0, ls = S - 1;
@@ -474,7 +583,7 @@ __global__ __launch_bounds__(G::THREADS) void tiled_gemm_kernel(KernelArgs p) {
     block_barrier();
     issue(kt + S - 1, ls);
     compute(cs);
-    store_gather(ls);
+    store_staged(ls);
     cs = cs + 1 == S ? 0 : cs + 1;
     ls = ls + 1 == S ? 0 : ls + 1;
   }
@@ -493,11 +602,11 @@ __global__ __launch_bounds__(G::THREADS) void tiled_gemm_kernel(KernelArgs p) {
   if constexpr (!CONV) {
     const int64_t cbase = int64_t(bz) * p.batch_stride_c;
     if (p.out_dtype == TSS_F32)
-      store_tile<G, float>(acc, reinterpret_cast<float *>(p.C) + cbase, m0, n0, wr, wc, lane, M, N);
+      store_tile<G, float>(acc, reinterpret_cast<float *>(p.C) + cbase, smem, m0, n0, wave, wr, wc, lane, M, N);
     else if (p.out_dtype == TSS_F16)
-      store_tile<G, _Float16>(acc, reinterpret_cast<_Float16 *>(p.C) + cbase, m0, n0, wr, wc, lane, M, N);
+      store_tile<G, _Float16>(acc, reinterpret_cast<_Float16 *>(p.C) + cbase, smem, m0, n0, wave, wr, wc, lane, M, N);
     else
-      store_tile<G, __bf16>(acc, reinterpret_cast<__bf16 *>(p.C) + cbase, m0, n0, wr, wc, lane, M, N);
+      store_tile<G, __bf16>(acc, reinterpret_cast<__bf16 *>(p.C) + cbase, smem, m0, n0, wave, wr, wc, lane, M, N);
   } else {
     if (p.out_dtype == TSS_F32)
       store_conv<G, float>(acc, reinterpret_cast<float *>(p.C), p, m0, n0, wr, wc, lane, o0, rows_t, N);

@@ -262,12 +262,14 @@ constexpr Key rank_key(const tss_verdict &v, const tss_device &d) {
     r.k[1] = -v.blocks_per_core;
     r.k[2] = v.smem_total;
   } else {
+    // C4-clean first, then least traffic, most resident blocks, most resident
+    // waves (occupancy), larger BK, deeper pipeline, less LDS
     r.k[0] = v.warnings ? 1 : 0;
     r.k[1] = t;
     r.k[2] = -v.blocks_per_core;
-    r.k[3] = -v.cfg.bk;
-    r.k[4] = -v.cfg.stages;
-    r.k[5] = v.cfg.threads;
+    r.k[3] = -v.blocks_per_core * (v.cfg.threads / d.lane_count);
+    r.k[4] = -v.cfg.bk;
+    r.k[5] = -v.cfg.stages;
     r.k[6] = v.smem_total;
   }
   return r;
