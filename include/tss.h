@@ -164,8 +164,8 @@ int32_t tss_evaluate(const tss_tile_config *cfg, const tss_device *dev, int64_t 
  *                 threads {128, 256, 512}, instr fixed by *instr_filter;
  *                 key (round(traffic), -blocks/SM, shared memory).
  *   gfx950 model: BM, BN in {64, 128, 256}, BK in {16, 32, 64}, stages 2..4,
- *                 threads {128, 256, 512}, both MFMA shapes (or the one in
- *                 instr_filter); key (C4 warning?, round(traffic), -blocks/CU,
+ *                 threads {128, 256, 512}, both MFMA shapes, 16x16x32 first
+ *                 (or the one in instr_filter); key (C4 warning?, round(traffic), -blocks/CU,
  *                 -resident waves/CU, -BK, -stages, LDS bytes).
  * instr_filter: 0 = every shape of the device, else one TSS_INSTR_*.
  * best (nullable) receives the top verdict; list (nullable) the first

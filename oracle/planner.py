@@ -78,9 +78,11 @@ class DeviceModel:
 # threads, and plain SIMT code.
 NVIDIA_SHAPES = (("mma", (16, 8, 16, 32)), ("simt", (1, 1, 1, 32)), ("wgmma", (64, 8, 16, 128)))
 
-# gfx950 dense f16/bf16 MFMA shapes: v_mfma_f32_32x32x16_{f16,bf16} and
-# v_mfma_f32_16x16x32_{f16,bf16}; both are issued by one 64-lane wave.
-GFX950_SHAPES = (("mfma32", (32, 32, 16, 64)), ("mfma16", (16, 16, 32, 64)))
+# gfx950 dense f16/bf16 MFMA shapes: v_mfma_f32_16x16x32_{f16,bf16} and
+# v_mfma_f32_32x32x16_{f16,bf16}; both are issued by one 64-lane wave.  The
+# 16x16 one is listed first, so it wins ties: it keeps the 16x16 output tile
+# of the MMA level in the Tiling page's multi-level tiling section.
+GFX950_SHAPES = (("mfma16", (16, 16, 32, 64)), ("mfma32", (32, 32, 16, 64)))
 
 
 def device_pages(sm_count: int = 132, smem_kb: int = 228) -> DeviceModel:

@@ -202,9 +202,12 @@ def test_short_k_keeps_the_shortest_step():
 def test_gfx950_rank_prefers_occupancy_then_bigger_k_step():
     """4096^3: every 256x256 tile ties on traffic and on one block per CU;
     512 threads keep 8 waves resident (25% of 32) against 4 for 256 threads,
-    and among those the 64-deep K step wins."""
+    among those the 64-deep K step wins, and the 16x16x32 shape wins the tie
+    with 32x32x16 by coming first."""
     g = P.device_gfx950()
-    res = P.sweep(4096, 4096, 4096, g, ["mfma32", "mfma16"])
+    res = P.sweep(4096, 4096, 4096, g, [s for s, _ in g.instr_shapes])
     c = res[0].config
-    assert (c.block_m, c.block_n, c.block_k, c.stages, c.threads, c.instr) == (256, 256, 64, 2, 512, "mfma32")
+    assert (c.block_m, c.block_n, c.block_k, c.stages, c.threads, c.instr) == (256, 256, 64, 2, 512, "mfma16")
+    d = res[1].config    # the 32x32x16 twin ties on every key and follows it
+    assert (d.block_m, d.block_n, d.block_k, d.stages, d.threads, d.instr) == (256, 256, 64, 2, 512, "mfma32")
     assert P.rank_key(res[0], g)[3] == -8

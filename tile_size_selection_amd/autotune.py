@@ -21,15 +21,15 @@ from . import api
 from .inputs import draw
 
 
-def time_config(A, B, out, cfg, iters: int, warmup: int) -> float:
+def time_config(A, B, out, cfg, iters: int, warmup: int, out_dtype: str) -> float:
     for _ in range(warmup):
-        api.gemm(A, B, cfg=cfg, out=out)
+        api.gemm(A, B, out_dtype=out_dtype, cfg=cfg, out=out)
     torch.cuda.synchronize()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     e0.record()
     for _ in range(iters):
-        api.gemm(A, B, cfg=cfg, out=out)
+        api.gemm(A, B, out_dtype=out_dtype, cfg=cfg, out=out)
     e1.record()
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) / iters * 1e3  # microseconds
@@ -48,7 +48,7 @@ def sweep(M: int, N: int, K: int, batch: int = 1, dtype: str = "f16", out_dtype:
     # bring the clocks up before the first measurement
     t_end = time.time() + 1.0
     while time.time() < t_end:
-        api.gemm(A, B, cfg=ranked[0]["config"], out=out)
+        api.gemm(A, B, out_dtype=od, cfg=ranked[0]["config"], out=out)
     torch.cuda.synchronize()
     rows = []
     for rank, v in enumerate(ranked):
@@ -56,7 +56,7 @@ def sweep(M: int, N: int, K: int, batch: int = 1, dtype: str = "f16", out_dtype:
     # several rounds, interleaved, keep each config's best round
     for _ in range(rounds):
         for r in rows:
-            r["us"] = min(r["us"], time_config(A, B, out, r["config"], iters, warmup))
+            r["us"] = min(r["us"], time_config(A, B, out, r["config"], iters, warmup, od))
     flops = 2.0 * batch * M * N * K
     for r in rows:
         r["tflops"] = flops / (r["us"] * 1e-6) / 1e12

@@ -1,0 +1,157 @@
+"""HBM traffic of the headline GEMM kernel from hardware counters.
+
+Two steps, each under its own rocprofv3 run (one counter per pass):
+
+    rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir>/fetch -o run -- python3 -m tile_size_selection_amd.counters run
+    rocprofv3 --pmc WRITE_SIZE --output-format csv -d <dir>/write -o run -- python3 -m tile_size_selection_amd.counters run
+    python3 -m tile_size_selection_amd.counters summarize <dir> [--trace <kernel_stats.csv>] > summary.md
+
+`run` launches a plain elementwise pass over 256 MiB (y = -x: known bytes
+read and written) and then the 4096^3 fp16 GEMM in the configuration the
+benchmark times.  That pass calibrates the counters: the GEMM's FETCH_SIZE / WRITE_SIZE (KiB per
+dispatch, summed over the L2 channels) are scaled by bytes_known / bytes_read
+of the copy.  `summarize` writes the figures the benchmark reads back
+(kernel_source_hash, config, hbm_bytes_per_launch).
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import os
+import sys
+from collections import defaultdict
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+COPY_BYTES = 256 << 20
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in ("gemm_kernel.h", "registry.h", "instances.inc"):
+        with open(os.path.join(PKG, "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def run(launches: int = 5):
+    import torch
+    from . import api
+    from .inputs import WORKLOADS
+    src = torch.ones(COPY_BYTES // 2, dtype=torch.float16, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.neg(src, out=dst)      # reads and writes COPY_BYTES
+    torch.cuda.synchronize()
+    w = WORKLOADS[2]
+    A, B = w.make()
+    dA, dB = A.cuda(), B.cuda()
+    out = torch.empty((w.M, w.N), dtype=torch.float16, device="cuda")
+    for _ in range(launches):
+        api.gemm(dA, dB, out=out)
+    torch.cuda.synchronize()
+    cfg = api.default_config(w.M, w.N, w.K)
+    print(f"config {cfg.bm}x{cfg.bn}x{cfg.bk}/s{cfg.stages}/t{cfg.threads}/{cfg.instr}", flush=True)
+
+
+def per_dispatch(csv_path: str, counter: str):
+    """{kernel name: [value per dispatch]} (rows of one dispatch summed)."""
+    acc = defaultdict(float)
+    names = {}
+    with open(csv_path) as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] != counter:
+                continue
+            d = r["Dispatch_Id"]
+            acc[d] += float(r["Counter_Value"])
+            names[d] = r["Kernel_Name"]
+    out = defaultdict(list)
+    for d, v in acc.items():
+        out[names[d]].append(v)
+    return out
+
+
+def _mean(v):
+    return sum(v) / len(v)
+
+
+def summarize(d: str, trace: str = None) -> str:
+    from . import api
+    fetch = per_dispatch(glob.glob(os.path.join(d, "fetch", "**", "*counter_collection.csv"), recursive=True)[0],
+                         "FETCH_SIZE")
+    write = per_dispatch(glob.glob(os.path.join(d, "write", "**", "*counter_collection.csv"), recursive=True)[0],
+                         "WRITE_SIZE")
+    # the calibration pass is the non-GEMM kernel that reads the most
+    copy_k = sorted((k for k in fetch if "tiled_gemm_kernel" not in k), key=lambda k: -_mean(fetch[k]))
+    gemm_k = [k for k in fetch if "tiled_gemm_kernel" in k]
+    if not copy_k or not gemm_k:
+        raise SystemExit("calibration or GEMM dispatches missing from the counter files")
+    ck, gk = copy_k[0], gemm_k[0]
+    f_copy = _mean(fetch[ck]) * 1024.0
+    w_copy = _mean(write[ck]) * 1024.0
+    f_scale = COPY_BYTES / f_copy
+    w_scale = COPY_BYTES / w_copy
+    f_gemm = _mean(fetch[gk]) * 1024.0 * f_scale
+    w_gemm = _mean(write[gk]) * 1024.0 * w_scale
+    cfg = api.default_config(4096, 4096, 4096)
+    cfg_s = f"{cfg.bm}x{cfg.bn}x{cfg.bk}/s{cfg.stages}/t{cfg.threads}/{cfg.instr}"
+    algo = 3 * 4096 * 4096 * 2
+    lines = [
+        "# HBM traffic of the 4096^3 fp16 GEMM kernel (rocprofv3 counters)",
+        "",
+        "Commands (from the repository root, on the MI355X):",
+        "",
+        "    rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir>/fetch -o run -- "
+        "python3 -m tile_size_selection_amd.counters run",
+        "    rocprofv3 --pmc WRITE_SIZE --output-format csv -d <dir>/write -o run -- "
+        "python3 -m tile_size_selection_amd.counters run",
+        "    python3 -m tile_size_selection_amd.counters summarize <dir>",
+        "",
+        f"copy calibration: {COPY_BYTES} B copied; FETCH_SIZE read {f_copy:.0f} B (scale {f_scale:.4f}), "
+        f"WRITE_SIZE read {w_copy:.0f} B (scale {w_scale:.4f}); kernel `{ck[:60]}`",
+        f"GEMM kernel `{gk[:90]}`: {len(fetch[gk])} dispatches",
+        f"GEMM FETCH_SIZE {_mean(fetch[gk]):.0f} KiB/dispatch raw -> {f_gemm:.0f} B scaled",
+        f"GEMM WRITE_SIZE {_mean(write[gk]):.0f} KiB/dispatch raw -> {w_gemm:.0f} B scaled",
+        f"algorithmic bytes (A and B read once, C written once): {algo} B; measured / algorithmic = "
+        f"{(f_gemm + w_gemm) / algo:.3f}",
+        "",
+        "Values read by bench.py:",
+        "",
+        f"kernel_source_hash: {kernel_source_hash()}",
+        f"config: {cfg_s}",
+        f"hbm_bytes_per_launch: {f_gemm + w_gemm:.0f}",
+        f"fetch_bytes_per_launch: {f_gemm:.0f}",
+        f"write_bytes_per_launch: {w_gemm:.0f}",
+    ]
+    if trace and os.path.exists(trace):
+        lines += ["", "Kernel trace of the benchmark, same build:", "",
+                  "    rocprofv3 --kernel-trace --stats --output-format csv -d <dir>/ktrace -o bench -- "
+                  "python3 bench.py --no-cpu-baseline"]
+        with open(trace) as f:
+            for r in csv.DictReader(f):
+                if "tiled_gemm_kernel" in r["Name"]:
+                    lines += ["", f"kernel trace (same build): {r['Name'][:90]} calls {r['Calls']} "
+                                  f"average {float(r['AverageNs']) / 1e3:.2f} us, min {float(r['MinNs']) / 1e3:.2f} us"]
+    return "\n".join(lines) + "\n"
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    r = sub.add_parser("run")
+    r.add_argument("--launches", type=int, default=5)
+    s = sub.add_parser("summarize")
+    s.add_argument("dir")
+    s.add_argument("--trace", default=None)
+    a = ap.parse_args()
+    if a.cmd == "run":
+        run(a.launches)
+    else:
+        sys.stdout.write(summarize(a.dir, a.trace))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -236,8 +236,10 @@ constexpr Space space_for(const tss_device &d, int32_t instr_filter) {
     int32_t ks[3] = {16, 32, 64};
     for (int i = 0; i < 3; ++i) s.bk[i] = ks[i];
     s.nbk = 3;
-    s.instr[0] = TSS_INSTR_MFMA32;
-    s.instr[1] = TSS_INSTR_MFMA16;
+    // 16x16x32 first: it wins ties, keeping the 16x16 output tile of the
+    // MMA level of the Tiling page's multi-level tiling
+    s.instr[0] = TSS_INSTR_MFMA16;
+    s.instr[1] = TSS_INSTR_MFMA32;
     s.ninstr = 2;
   }
   if (instr_filter) {
