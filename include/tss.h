@@ -163,10 +163,12 @@ int32_t tss_evaluate(const tss_tile_config *cfg, const tss_device *dev, int64_t 
  *   pages model : BM, BN in {16..256}, BK in {16..128}, stages 2..4,
  *                 threads {128, 256, 512}, instr fixed by *instr_filter;
  *                 key (round(traffic), -blocks/SM, shared memory).
- *   gfx950 model: BM, BN in {64, 128, 256}, BK in {16, 32, 64}, stages 2..4,
- *                 threads {128, 256, 512}, both MFMA shapes, 16x16x32 first
- *                 (or the one in instr_filter); key (C4 warning?, round(traffic), -blocks/CU,
- *                 -resident waves/CU, -BK, -stages, LDS bytes).
+ *   gfx950 model: BM, BN in {256, 128, 64} (largest first), BK in
+ *                 {16, 32, 64}, stages 2..4, threads {128, 256, 512}, both
+ *                 MFMA shapes, 16x16x32 first (or the one in instr_filter);
+ *                 key (ceil(grid / CUs) * (BM + BN), round(traffic), -BK,
+ *                 -blocks/CU, -resident waves/CU, -stages, LDS bytes): the
+ *                 first term is the C0 panel traffic of the busiest CU.
  * instr_filter: 0 = every shape of the device, else one TSS_INSTR_*.
  * best (nullable) receives the top verdict; list (nullable) the first
  * min(cap, n) verdicts in rank order; *n_feasible (nullable) the count.

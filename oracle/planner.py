@@ -302,8 +302,22 @@ def round_half_even(x: Fraction) -> int:
 
 PAGES_SPACE = dict(bm=(16, 32, 64, 128, 256), bn=(16, 32, 64, 128, 256), bk=(16, 32, 64, 128),
                    stages=(2, 3, 4), threads=(128, 256, 512))
-GFX950_SPACE = dict(bm=(64, 128, 256), bn=(64, 128, 256), bk=(16, 32, 64),
+# gfx950: tile sides largest first, so that of two otherwise equal tiles the
+# taller one comes first (its B panel -- the operand the convolution gathers
+# element by element -- is reused over more rows).
+GFX950_SPACE = dict(bm=(256, 128, 64), bn=(256, 128, 64), bk=(16, 32, 64),
                     stages=(2, 3, 4), threads=(128, 256, 512))
+
+
+def busiest_core_traffic(v: Verdict, dev: DeviceModel) -> int:
+    """C0's per-tile traffic (BM + BN) * K * b, times the number of tiles the
+    busiest SM/CU streams once C4 has dealt the grid out in waves over the
+    cores: ceil(grid / cores) * (BM + BN), in units of K * b bytes.  Every
+    candidate tile's intensity 2*BM*BN / ((BM + BN) * b) (Tiling page) is below
+    the device's ridge (gfx950: 2516.6 TFLOP/s over 8 TB/s, about 315 FLOP/B),
+    so this is the time the busiest core needs."""
+    c = v.config
+    return _ceil_div(v.grid, dev.cores) * (c.block_m + c.block_n)
 
 
 def rank_key(v: Verdict, dev: DeviceModel):
@@ -311,19 +325,19 @@ def rank_key(v: Verdict, dev: DeviceModel):
 
     pages: least modelled DRAM traffic, then most resident blocks, then least
     shared memory (the tile_decision.py page's shortlist order).
-    gfx950: candidates without a C4 warning first; then least traffic and most
-    resident blocks as on the pages; then the most resident waves per CU
-    (occupancy, the Tiling page's third constraint: low occupancy leaves the
-    compute units idle while waves wait on memory); then, as that page's
-    rules of thumb advise when on-chip memory has room, the larger block_K and
-    the deeper pipeline; then less LDS.
+    gfx950: least traffic through the busiest CU (C0 per tile under C4's wave
+    quantization), then least total traffic (C0); then, as the Tiling page's
+    rules of thumb advise when on-chip memory has room, the larger block_K;
+    then most resident blocks and most resident waves per CU (occupancy, that
+    page's third constraint); then the deeper pipeline; then less LDS.
     """
     t = round_half_even(v.traffic)
     if dev.ranking == "pages":
         return (t, -v.blocks_per_core, v.smem_total)
     c = v.config
     resident_waves = v.blocks_per_core * (c.threads // dev.lane_count)
-    return (1 if v.warnings else 0, t, -v.blocks_per_core, -resident_waves, -c.block_k, -c.stages, v.smem_total)
+    return (busiest_core_traffic(v, dev), t, -c.block_k, -v.blocks_per_core, -resident_waves, -c.stages,
+            v.smem_total)
 
 
 def candidates(dev: DeviceModel, k: int, instrs: Sequence[str]):
@@ -419,4 +433,5 @@ def diagnose(cfg: TileConfig, dev: DeviceModel, m: int, n: int, batch: int = 1) 
 __all__ = ["DeviceModel", "TileConfig", "Verdict", "device_pages", "device_gfx950", "evaluate",
            "finish_parallelism", "dram_traffic", "round_half_even", "sweep", "plan", "rank_key",
            "sweep_rows", "sweep_summary", "diagnose_lines", "diagnose", "candidates", "WAVE_GRIDS",
+           "busiest_core_traffic",
            "replace"]

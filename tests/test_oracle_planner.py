@@ -200,14 +200,50 @@ def test_short_k_keeps_the_shortest_step():
 
 
 def test_gfx950_rank_prefers_occupancy_then_bigger_k_step():
-    """4096^3: every 256x256 tile ties on traffic and on one block per CU;
-    512 threads keep 8 waves resident (25% of 32) against 4 for 256 threads,
-    among those the 64-deep K step wins, and the 16x16x32 shape wins the tie
-    with 32x32x16 by coming first."""
+    """4096^3: every 256x256 tile streams 512 panel rows through its CU (one
+    tile per CU) and ties on C0; the 64-deep K step wins, then 512 threads
+    (8 resident waves against 4), and the 16x16x32 shape wins the tie with
+    32x32x16 by coming first."""
     g = P.device_gfx950()
     res = P.sweep(4096, 4096, 4096, g, [s for s, _ in g.instr_shapes])
     c = res[0].config
     assert (c.block_m, c.block_n, c.block_k, c.stages, c.threads, c.instr) == (256, 256, 64, 2, 512, "mfma16")
+    assert P.rank_key(res[0], g)[:1] == (512,) and P.rank_key(res[0], g)[4] == -8
     d = res[1].config    # the 32x32x16 twin ties on every key and follows it
     assert (d.block_m, d.block_n, d.block_k, d.stages, d.threads, d.instr) == (256, 256, 64, 2, 512, "mfma32")
-    assert P.rank_key(res[0], g)[3] == -8
+
+
+def test_gfx950_busiest_core_traffic_closed_forms():
+    g = P.device_gfx950()
+    ev = lambda bm, bn, M, N, b=1: P.finish_parallelism(P.evaluate(P.TileConfig(bm, bn, 64, 2, 256, "mfma32"), g),
+                                                        M, N, g, b)
+    # conv workload as a GEMM (256 x 6272): 128x64 tiles -> 196 tiles, one per
+    # CU at most: 1 * (128 + 64); 64x64 -> 392 tiles, two on some CUs: 2 * 128
+    assert P.busiest_core_traffic(ev(128, 64, 256, 6272), g) == 192
+    assert P.busiest_core_traffic(ev(64, 64, 256, 6272), g) == 256
+    assert P.busiest_core_traffic(ev(256, 256, 256, 6272), g) == 512     # 25 tiles, one CU each
+    # ragged batch: 4 x 12 x 20 = 960 tiles of 256x256 -> 4 per CU
+    assert P.busiest_core_traffic(ev(256, 256, 3000, 5000, 4), g) == 4 * 512
+    assert P.busiest_core_traffic(ev(128, 128, 3000, 5000, 4), g) == 15 * 256   # 3840 tiles
+
+
+def test_gfx950_conv_and_small_shape_choices():
+    g = P.device_gfx950()
+    ins = [s for s, _ in g.instr_shapes]
+    c = P.sweep(256, 6272, 2304, g, ins)[0].config
+    # 128x64 and 64x128 tie on every key but order: the taller tile comes first
+    assert (c.block_m, c.block_n, c.block_k, c.stages, c.threads, c.instr) == (128, 64, 64, 2, 512, "mfma16")
+    c = P.sweep(256, 256, 256, g, ins)[0].config
+    assert (c.block_m, c.block_n) == (64, 64)     # 16 tiles over 16 CUs beat one 256x256 tile
+    c = P.sweep(3000, 5000, 2048, g, ins, batch=4)[0].config
+    assert (c.block_m, c.block_n, c.block_k, c.stages, c.threads) == (256, 256, 64, 2, 512)
+
+
+def test_pages_register_granule_closed_form():
+    """tile_decision.py page, C2: 256 registers per warp of 32 threads, so
+    8 accumulators per thread take 8 registers and 9 take 16."""
+    dev = P.device_pages()
+    v = P.evaluate(P.TileConfig(32, 32, 16, 2, 128, "mma"), dev)
+    assert (v.accum_per_thread, v.regs_per_thread, v.regs_per_block, v.blocks_by_regs) == (8, 8, 1024, 64)
+    v = P.evaluate(P.TileConfig(48, 24, 16, 2, 128, "simt"), dev)      # 1152 / 128 = 9 accumulators
+    assert (v.accum_per_thread, v.regs_per_thread) == (9, 16)

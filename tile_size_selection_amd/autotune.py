@@ -3,6 +3,7 @@ the "Tiling（分块）" page: enumerate the candidates, drop the ones that brea
 a hardware constraint, time every survivor on the device, keep the fastest).
 
     python -m tile_size_selection_amd.autotune --m 4096 --n 4096 --k 4096 [--out report.md]
+    python -m tile_size_selection_amd.autotune --conv [--out report.md]     (the conv workload)
 
 Prints, for every feasible configuration, its measured time and TFLOP/s, its
 rank in the planner's order, and how the planner's first choice compares with
@@ -66,6 +67,46 @@ def sweep(M: int, N: int, K: int, batch: int = 1, dtype: str = "f16", out_dtype:
     return rows, summary
 
 
+def sweep_conv(iters: int = 20, warmup: int = 3, rounds: int = 2) -> Tuple[List[dict], dict]:
+    """The conv workload (8x256x56x56, 3x3, stride 2, pad 1, H-tiles of 8
+    rows, fp32 out) under every feasible tile of its implicit GEMM."""
+    from .inputs import WORKLOADS
+    cw = WORKLOADS[5]
+    OH = (cw.H + 2 * cw.pad[0] - cw.kh) // cw.stride[0] + 1
+    OW = (cw.W + 2 * cw.pad[1] - cw.kw) // cw.stride[1] + 1
+    M, N, K = cw.Co, cw.N * OH * OW, cw.C * cw.kh * cw.kw
+    best, ranked, n = api.tile_plan(M, N, K, cap=1024)
+    x, w = cw.make()
+    x, w = x.cuda(), w.cuda()
+    y = torch.empty((cw.N, cw.Co, OH, OW), dtype=torch.float32, device="cuda")
+    run = lambda cfg: api.conv2d(x, w, cw.stride, cw.pad, cw.dil, tile_oh=cw.tile_oh, out_dtype="f32", cfg=cfg,
+                                 out=y)
+    t_end = time.time() + 1.0
+    while time.time() < t_end:
+        run(ranked[0]["config"])
+    torch.cuda.synchronize()
+    rows = [{"rank": i, "config": v["config"], "verdict": v, "us": float("inf")} for i, v in enumerate(ranked)]
+    for _ in range(rounds):
+        for r in rows:
+            for _ in range(warmup):
+                run(r["config"])
+            torch.cuda.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(iters):
+                run(r["config"])
+            e1.record()
+            torch.cuda.synchronize()
+            r["us"] = min(r["us"], e0.elapsed_time(e1) / iters * 1e3)
+    flops = 2.0 * M * N * K
+    for r in rows:
+        r["tflops"] = flops / (r["us"] * 1e-6) / 1e12
+    fastest = min(rows, key=lambda r: r["us"])
+    return rows, {"n_feasible": n, "planner": rows[0], "fastest": fastest,
+                  "planner_over_fastest": rows[0]["us"] / fastest["us"], "shape": (M, N, K)}
+
+
 def report(M, N, K, batch, rows, summary) -> str:
     c = lambda cfg: f"{cfg.bm}x{cfg.bn}x{cfg.bk} s{cfg.stages} t{cfg.threads} {cfg.instr}"
     lines = [f"# Measured tile sweep: GEMM {batch}x{M}x{N}x{K}", "",
@@ -95,9 +136,16 @@ def main():
     ap.add_argument("--out-dtype", default=None)
     ap.add_argument("--iters", type=int, default=20)
     ap.add_argument("--out", default=None)
+    ap.add_argument("--conv", action="store_true")
     a = ap.parse_args()
-    rows, summary = sweep(a.m, a.n, a.k, a.batch, a.dtype, a.out_dtype, a.iters)
-    txt = report(a.m, a.n, a.k, a.batch, rows, summary)
+    if a.conv:
+        rows, summary = sweep_conv(a.iters)
+        M, N, K = summary["shape"]
+        txt = report(M, N, K, 1, rows, summary).replace("# Measured tile sweep: GEMM",
+                                                        "# Measured tile sweep: conv workload as implicit GEMM")
+    else:
+        rows, summary = sweep(a.m, a.n, a.k, a.batch, a.dtype, a.out_dtype, a.iters)
+        txt = report(a.m, a.n, a.k, a.batch, rows, summary)
     if a.out:
         with open(a.out, "w") as f:
             f.write(txt)

@@ -378,31 +378,42 @@ __global__ __launch_bounds__(G::THREADS) void tiled_gemm_kernel(KernelArgs p) {
     }
   }
   // -- B gather plan (conv): the thread fills logical pixel chunk g_lc (8
-  // consecutive pixels) of B rows g_k0 + j*(THREADS/CB)
+  // consecutive pixels) of B rows g_k0 + j*(THREADS/CB).  Per pixel it keeps
+  // the byte offset of the window's first tap and the tap's slice row and
+  // input column, so each gathered element costs two range checks and an add.
   const int g_lc = threadIdx.x % G::CB;
   const int g_k0 = threadIdx.x / G::CB;
-  int px_img[CONV ? 8 : 1], px_sr[CONV ? 8 : 1], px_iw[CONV ? 8 : 1];
+  int px_off[CONV ? 8 : 1], px_row[CONV ? 8 : 1], px_col[CONV ? 8 : 1];
   if constexpr (CONV) {
     const int plane = rows_t * p.OW;
+    const int row0 = in_start - pt_sub;  // input row of slice row 0 (= o0*sh - ph)
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int pix = n0 + g_lc * 8 + e;
       const int n = pix / plane, rem = pix - n * plane;
       const int oh_l = rem / p.OW, ow = rem - oh_l * p.OW;
-      const bool ok = pix < N;
-      px_img[e] = ok ? n * p.Cin * p.H * p.W : -1;
-      px_sr[e] = oh_l * p.sh;            // slice row of the window's first tap
-      px_iw[e] = ow * p.sw - p.pw;
+      const int sr = oh_l * p.sh;        // slice row of the window's first tap
+      const int iw = ow * p.sw - p.pw;   // input column of the window's first tap
+      px_off[e] = ((n * p.Cin * p.H + row0 + sr) * p.W + iw) * 2;
+      px_row[e] = pix < N ? sr - pt_sub : (1 << 30);  // rows [pt', pt' + rows_in) hold data
+      px_col[e] = iw;
     }
   }
-  i16x8 g_reg[CONV ? G::B_LOADS : 1];
+  // The gather of tile t is issued S-1 iterations before tile t is computed
+  // and written to LDS at the end of the iteration before; S-1 register sets
+  // keep those gathers in flight.
+  constexpr int NSET = CONV ? (S > 2 ? S - 1 : 1) : 1;
+  i16x8 g_reg[NSET][CONV ? G::B_LOADS : 1];
   // two-stage ring: the next tile's copy is staged in registers
   constexpr bool REG_COPY = S == 2;
   i16x8 ra[REG_COPY ? G::A_LOADS : 1], rb[(REG_COPY && !CONV) ? G::B_LOADS : 1];
+  // vector-memory instructions one iteration issues per thread
+  constexpr int VPI = G::A_LOADS + (CONV ? 8 * G::B_LOADS : G::B_LOADS);
 
   const int nk = (K + G::BK - 1) / G::BK;
 
-  auto issue = [&](int kt, int stage) {
+  auto issue = [&](int kt, int stage, auto set_c) __attribute__((always_inline)) {
+    constexpr int SET = decltype(set_c)::value;
     const int k0 = kt * G::BK;
     char *sa = smem + stage * G::STAGE_BYTES;
 #pragma unroll
@@ -427,8 +438,6 @@ __global__ __launch_bounds__(G::THREADS) void tiled_gemm_kernel(KernelArgs p) {
     } else {
       const int khw = p.kh * p.kw;
       const int HW = p.H * p.W;
-      const int sr_lo = pt_sub, sr_hi = pt_sub + rows_in;   // slice rows holding data
-      const int row0 = in_start - pt_sub;                   // input row of slice row 0
 #pragma unroll
       for (int j = 0; j < G::B_LOADS; ++j) {
         const int k = k0 + g_k0 + j * (G::THREADS / G::CB);
@@ -436,15 +445,14 @@ __global__ __launch_bounds__(G::THREADS) void tiled_gemm_kernel(KernelArgs p) {
         const int ci = kok ? k / khw : 0;
         const int rs = k - ci * khw;
         const int r = rs / p.kw, s = rs - r * p.kw;
-        const int kbase = ci * HW;
         const int dr = r * p.dh, ds = s * p.dw;
+        const int delta = (ci * HW + dr * p.W + ds) * 2;
+        const uint32_t rows_ok = kok ? uint32_t(rows_in) : 0u;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const int sr = px_sr[e] + dr;
-          const int iw = px_iw[e] + ds;
-          const bool ok = kok && px_img[e] >= 0 && sr >= sr_lo && sr < sr_hi && iw >= 0 && iw < p.W;
-          const uint32_t off = ok ? uint32_t(px_img[e] + kbase + (row0 + sr) * p.W + iw) * 2u : kOOB;
-          g_reg[j][e] = (short)__builtin_amdgcn_raw_buffer_load_b16(rsB, off, 0, 0);
+          const bool ok = uint32_t(px_row[e] + dr) < rows_ok && uint32_t(px_col[e] + ds) < uint32_t(p.W);
+          const uint32_t off = ok ? uint32_t(px_off[e] + delta) : kOOB;
+          g_reg[SET][j][e] = (short)__builtin_amdgcn_raw_buffer_load_b16(rsB, off, 0, 0);
         }
       }
     }
@@ -452,7 +460,8 @@ __global__ __launch_bounds__(G::THREADS) void tiled_gemm_kernel(KernelArgs p) {
   // write the register-staged part of a stage (after its loads returned):
   // the two-stage ring's A and B chunks at the positions the direct copy
   // would use, and the convolution's gathered B rows
-  auto store_staged = [&](int stage) {
+  auto store_staged = [&](int stage, auto set_c) __attribute__((always_inline)) {
+    constexpr int SET = decltype(set_c)::value;
     if constexpr (REG_COPY) {
       char *sa = smem + stage * G::STAGE_BYTES;
 #pragma unroll
@@ -468,7 +477,7 @@ __global__ __launch_bounds__(G::THREADS) void tiled_gemm_kernel(KernelArgs p) {
 #pragma unroll
       for (int j = 0; j < G::B_LOADS; ++j) {
         const int kk = g_k0 + j * (G::THREADS / G::CB);
-        *(lds_i16x8 *)(sb + kk * G::BN * 2 + ((g_lc ^ G::swz_b(kk)) * 16)) = g_reg[j];
+        *(lds_i16x8 *)(sb + kk * G::BN * 2 + ((g_lc ^ G::swz_b(kk)) * 16)) = g_reg[SET][j];
       }
     }
   };
@@ -540,7 +549,7 @@ __global__ __launch_bounds__(G::THREADS) void tiled_gemm_kernel(KernelArgs p) {
   // schedule is pinned: each LDS fragment read is issued right after an
   // MFMA, spread evenly over the step, so the reads overlap the matrix
   // pipeline instead of stalling it just before each MFMA.
-  auto compute = [&](int stage) {
+  auto compute = [&](int stage) __attribute__((always_inline)) {
     const char *st = smem + stage * G::STAGE_BYTES;
     i16x8 af0[G::TM], bf0[G::TN], af1[G::TM], bf1[G::TN];
     load_frags(st, 0, af0, bf0);
@@ -566,36 +575,75 @@ __global__ __launch_bounds__(G::THREADS) void tiled_gemm_kernel(KernelArgs p) {
     __builtin_amdgcn_sched_group_barrier(0x008, NMF, 0);  // last step
   };
 
-  // -- prologue: stages 0 .. S-2 in flight
-#pragma unroll
-  for (int s = 0; s < S - 1; ++s)
-    if (s < nk) {
-      issue(s, s);
-      store_staged(s);
-    }
-
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, (NSET > 1 ? 1 : 0)>;
+  using I2 = std::integral_constant<int, (NSET > 2 ? 2 : 0)>;
   int kt = 0, cs = 0, ls = S - 1;
-  // steady state: tile kt has landed once only the S-2 younger tiles' loads
-  // are outstanding; the barrier publishes every wave's copy and frees stage
-  // ls (computed in the previous iteration) for tile kt+S-1.
-  for (; kt + S - 1 < nk; ++kt) {
-    wait_vmcnt_lgkm0<(S - 2) * G::LPW>();
-    block_barrier();
-    issue(kt + S - 1, ls);
-    compute(cs);
-    store_staged(ls);
-    cs = cs + 1 == S ? 0 : cs + 1;
-    ls = ls + 1 == S ? 0 : ls + 1;
-  }
-  // drain: nothing more to load; nk-1-kt younger tiles remain outstanding
-  for (; kt < nk; ++kt) {
-    const int pend = nk - 1 - kt;
-    if (S >= 4 && pend >= 2) wait_vmcnt_lgkm0<(S >= 4 ? 2 : 0) * G::LPW>();
-    else if (S >= 3 && pend >= 1) wait_vmcnt_lgkm0<(S >= 3 ? 1 : 0) * G::LPW>();
-    else wait_vmcnt_lgkm0<0>();
-    block_barrier();
-    compute(cs);
-    cs = cs + 1 == S ? 0 : cs + 1;
+
+  if constexpr (NSET == 1) {
+    // -- prologue: stages 0 .. S-2 in flight
+#pragma unroll
+    for (int s = 0; s < S - 1; ++s)
+      if (s < nk) {
+        issue(s, s, I0{});
+        store_staged(s, I0{});
+      }
+    // steady state: tile kt has landed once only the S-2 younger tiles'
+    // loads are outstanding; the barrier publishes every wave's copy and
+    // frees stage ls (computed in the previous iteration) for tile kt+S-1.
+    for (; kt + S - 1 < nk; ++kt) {
+      wait_vmcnt_lgkm0<(S - 2) * G::LPW>();
+      block_barrier();
+      issue(kt + S - 1, ls, I0{});
+      compute(cs);
+      store_staged(ls, I0{});
+      cs = cs + 1 == S ? 0 : cs + 1;
+      ls = ls + 1 == S ? 0 : ls + 1;
+    }
+    // drain: nothing more to load; nk-1-kt younger tiles remain outstanding
+    for (; kt < nk; ++kt) {
+      const int pend = nk - 1 - kt;
+      if (S >= 4 && pend >= 2) wait_vmcnt_lgkm0<(S >= 4 ? 2 : 0) * G::LPW>();
+      else if (S >= 3 && pend >= 1) wait_vmcnt_lgkm0<(S >= 3 ? 1 : 0) * G::LPW>();
+      else wait_vmcnt_lgkm0<0>();
+      block_barrier();
+      compute(cs);
+      cs = cs + 1 == S ? 0 : cs + 1;
+    }
+  } else {
+    // Convolution with 3 or 4 stages: A goes HBM -> LDS directly, the
+    // gathered B of tile t is issued S-1 iterations ahead into register set
+    // t % NSET and written to its stage at the end of iteration t-1.
+    constexpr int W1 = VPI < 63 ? VPI : 63;
+    constexpr int W2 = 2 * VPI < 63 ? 2 * VPI : 63;
+    if (0 < nk) issue(0, 0, I0{});
+    if (1 < nk) issue(1, 1, I1{});
+    if (S > 3 && 2 < nk) issue(2, 2 % S, I2{});
+    if (0 < nk) store_staged(0, I0{});
+    // one iteration; unrolled NSET times so every register set index is
+    // static (iteration kt issues into set kt % NSET, stores set (kt+1) % NSET)
+    auto step = [&](auto set_c) __attribute__((always_inline)) {
+      constexpr int J = decltype(set_c)::value;
+      if (kt >= nk) return;
+      // tile kt's direct copy is complete once only the younger tiles'
+      // instructions (at most S-2 iterations' worth) are outstanding
+      const int pend = nk - 1 - kt < S - 2 ? nk - 1 - kt : S - 2;
+      if (pend >= 2) wait_vmcnt_lgkm0<W2>();
+      else if (pend == 1) wait_vmcnt_lgkm0<W1>();
+      else wait_vmcnt_lgkm0<0>();
+      block_barrier();
+      if (kt + S - 1 < nk) issue(kt + S - 1, ls, std::integral_constant<int, J>{});
+      compute(cs);
+      if (kt + 1 < nk) store_staged(cs + 1 == S ? 0 : cs + 1, std::integral_constant<int, (J + 1) % NSET>{});
+      cs = cs + 1 == S ? 0 : cs + 1;
+      ls = ls + 1 == S ? 0 : ls + 1;
+      ++kt;
+    };
+    while (kt < nk) {
+      step(I0{});
+      step(I1{});
+      if constexpr (NSET > 2) step(I2{});
+    }
   }
 
   // -- epilogue

@@ -230,7 +230,10 @@ constexpr Space space_for(const tss_device &d, int32_t instr_filter) {
     for (int i = 0; i < 3; ++i) s.instr[i] = nv[i];
     s.ninstr = 3;
   } else {
-    int32_t sizes[3] = {64, 128, 256};
+    // largest first: of two otherwise equal tiles the taller one comes first
+    // (its B panel, the operand the convolution gathers element by element,
+    // is reused over more rows)
+    int32_t sizes[3] = {256, 128, 64};
     for (int i = 0; i < 3; ++i) s.bm[i] = s.bn[i] = sizes[i];
     s.nbm = s.nbn = 3;
     int32_t ks[3] = {16, 32, 64};
@@ -264,13 +267,16 @@ constexpr Key rank_key(const tss_verdict &v, const tss_device &d) {
     r.k[1] = -v.blocks_per_core;
     r.k[2] = v.smem_total;
   } else {
-    // C4-clean first, then least traffic, most resident blocks, most resident
-    // waves (occupancy), larger BK, deeper pipeline, less LDS
-    r.k[0] = v.warnings ? 1 : 0;
+    // least traffic through the busiest CU: C0's per-tile panels (BM + BN)
+    // times the tiles a CU streams once the grid is dealt out in waves (every
+    // candidate's intensity is below the device ridge, ~315 FLOP/B); then
+    // total C0, larger BK, most resident blocks, most resident waves, deeper
+    // pipeline, less LDS
+    r.k[0] = cdiv(v.grid, d.cores) * (v.cfg.bm + v.cfg.bn);
     r.k[1] = t;
-    r.k[2] = -v.blocks_per_core;
-    r.k[3] = -v.blocks_per_core * (v.cfg.threads / d.lane_count);
-    r.k[4] = -v.cfg.bk;
+    r.k[2] = -v.cfg.bk;
+    r.k[3] = -v.blocks_per_core;
+    r.k[4] = -v.blocks_per_core * (v.cfg.threads / d.lane_count);
     r.k[5] = -v.cfg.stages;
     r.k[6] = v.smem_total;
   }
