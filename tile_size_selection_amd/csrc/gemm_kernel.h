@@ -11,15 +11,10 @@
 //
 // Memory-hierarchy techniques of the same page, in their gfx950 form:
 //   * staging with a multi-stage pipeline: `stages` LDS buffers in a ring;
-//     K tile t+stages-1 is in flight while tile t is computed.  With three or
-//     four stages the copy is a direct HBM->LDS buffer load
-//     (buffer_load_dwordx4 ... lds) that bypasses registers, the analogue of
-//     the page's asynchronous copy, so several tiles are in flight without
-//     holding registers.  With two stages (double buffering) the tile goes
-//     through registers (buffer_load_dwordx4, then ds_write_b128 once the
-//     current tile's MFMAs are issued), the page's older HBM -> register ->
-//     shared-memory path: on gfx950 it measured faster than the direct copy
-//     for this depth;
+//     K tile t+stages-1 is in flight while tile t is computed.  The copy is a
+//     direct HBM->LDS buffer load (buffer_load_dwordx4 ... lds) that bypasses
+//     registers, the analogue of the page's asynchronous copy, so several
+//     tiles are in flight without holding registers;
 //   * coalescing: each load instruction moves 64 lanes x 16 B = 1 KiB of whole
 //     rows;
 //   * bank-conflict-free LDS: 16-byte chunks are XOR-swizzled per row (the
@@ -94,6 +89,32 @@ __device__ __forceinline__ void wait_vmcnt_lgkm0() {
 // memory clobber keeps the compiler from moving LDS accesses across it; the
 // needed waits are issued explicitly.
 __device__ __forceinline__ void block_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// Buffer resource for the HBM -> LDS copy below: base, no stride, `range`
+// bytes (accesses at or past it read as zero), the gfx950 default format word.
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ i32x4 buffer_rsrc(const void *base, uint32_t range) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  i32x4 r;
+  r[0] = int(uint32_t(a));
+  r[1] = int(uint32_t(a >> 32) & 0xffffu);
+  r[2] = int(range);
+  r[3] = 0x00020000;
+  return r;
+}
+
+// Direct HBM -> LDS copy of 16 bytes per lane (buffer_load_dwordx4 ... lds):
+// lane i's 16 bytes land at dst + 16*i.  Issued as inline assembly because the
+// compiler, unable to tell which stage a later LDS read touches, would
+// otherwise make every LDS read wait for every copy in flight (vmcnt(0)),
+// which serializes the multi-stage ring.  The kernel orders the copies itself
+// with explicit s_waitcnt vmcnt + s_barrier pairs.  M0 holds the LDS address;
+// one wait state separates its write from the load that reads it.
+__device__ __forceinline__ void copy_to_lds16(i32x4 rs, uint32_t voff, const lds_void *dst) {
+  const uint32_t m0 = uint32_t(reinterpret_cast<uintptr_t>(dst));
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rs), "s"(m0)
+               : "memory", "m0");
+}
 
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   uint32_t u = __builtin_bit_cast(uint32_t, f);
@@ -341,15 +362,16 @@ __global__ __launch_bounds__(G::THREADS) void tiled_gemm_kernel(KernelArgs p) {
 
   const T *Ab = reinterpret_cast<const T *>(p.A) + (CONV ? 0 : int64_t(bz) * p.batch_stride_a) + int64_t(m0) * K;
   const uint32_t a_range = uint32_t(min(G::BM, M - m0)) * uint32_t(K) * 2u;  // rows [m0, M)
-  __amdgpu_buffer_rsrc_t rsA = __builtin_amdgcn_make_buffer_rsrc((void *)Ab, (short)0, (int)a_range, 0x00020000);
-  __amdgpu_buffer_rsrc_t rsB;
+  const i32x4 rsA4 = buffer_rsrc(Ab, a_range);
+  i32x4 rsB4{};                 // GEMM: the B operand for the direct copy
+  __amdgpu_buffer_rsrc_t rsB;    // conv: the input, for the element gather
   if constexpr (CONV) {
     const uint32_t x_range = uint32_t(p.Nb) * uint32_t(p.Cin) * uint32_t(p.H) * uint32_t(p.W) * 2u;
     rsB = __builtin_amdgcn_make_buffer_rsrc((void *)p.B, (short)0, (int)x_range, 0x00020000);
   } else {
     const T *Bb = reinterpret_cast<const T *>(p.B) + int64_t(bz) * p.batch_stride_b + n0;
     const uint32_t b_range = (uint32_t(K) * uint32_t(N) - uint32_t(n0)) * 2u;  // elements [n0, K*N)
-    rsB = __builtin_amdgcn_make_buffer_rsrc((void *)Bb, (short)0, (int)b_range, 0x00020000);
+    rsB4 = buffer_rsrc(Bb, b_range);
   }
 
   // -- A copy plan: wave load j of a stage covers LDS chunks (j*NW+wave)*64 + lane
@@ -404,9 +426,6 @@ __global__ __launch_bounds__(G::THREADS) void tiled_gemm_kernel(KernelArgs p) {
   // keep those gathers in flight.
   constexpr int NSET = CONV ? (S > 2 ? S - 1 : 1) : 1;
   i16x8 g_reg[NSET][CONV ? G::B_LOADS : 1];
-  // two-stage ring: the next tile's copy is staged in registers
-  constexpr bool REG_COPY = S == 2;
-  i16x8 ra[REG_COPY ? G::A_LOADS : 1], rb[(REG_COPY && !CONV) ? G::B_LOADS : 1];
   // vector-memory instructions one iteration issues per thread
   constexpr int VPI = G::A_LOADS + (CONV ? 8 * G::B_LOADS : G::B_LOADS);
 
@@ -419,21 +438,14 @@ __global__ __launch_bounds__(G::THREADS) void tiled_gemm_kernel(KernelArgs p) {
 #pragma unroll
     for (int j = 0; j < G::A_LOADS; ++j) {
       uint32_t off = (k0 + a_kc[j] < K) ? a_off[j] + uint32_t(k0) * 2u : kOOB;
-      if constexpr (REG_COPY)
-        ra[j] = __builtin_bit_cast(i16x8, __builtin_amdgcn_raw_buffer_load_b128(rsA, off, 0, 0));
-      else
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsA, (lds_void *)(sa + (j * G::NW + wave) * 1024), 16, off, 0, 0, 0);
+      copy_to_lds16(rsA4, off, (lds_void *)(sa + (j * G::NW + wave) * 1024));
     }
     if constexpr (!CONV) {
       char *sb = sa + G::A_BYTES;
 #pragma unroll
       for (int j = 0; j < G::B_LOADS; ++j) {
         uint32_t off = (k0 + b_k[j] < K) ? b_off[j] + uint32_t(k0) * uint32_t(N) * 2u : kOOB;
-        if constexpr (REG_COPY)
-          rb[j] = __builtin_bit_cast(i16x8, __builtin_amdgcn_raw_buffer_load_b128(rsB, off, 0, 0));
-        else
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(rsB, (lds_void *)(sb + (j * G::NW + wave) * 1024), 16, off, 0, 0,
-                                                   0);
+        copy_to_lds16(rsB4, off, (lds_void *)(sb + (j * G::NW + wave) * 1024));
       }
     } else {
       const int khw = p.kh * p.kw;
@@ -457,21 +469,10 @@ __global__ __launch_bounds__(G::THREADS) void tiled_gemm_kernel(KernelArgs p) {
       }
     }
   };
-  // write the register-staged part of a stage (after its loads returned):
-  // the two-stage ring's A and B chunks at the positions the direct copy
-  // would use, and the convolution's gathered B rows
+  // write the convolution's gathered B rows of a stage (after their loads
+  // returned) into the B layout of the GEMM
   auto store_staged = [&](int stage, auto set_c) __attribute__((always_inline)) {
     constexpr int SET = decltype(set_c)::value;
-    if constexpr (REG_COPY) {
-      char *sa = smem + stage * G::STAGE_BYTES;
-#pragma unroll
-      for (int j = 0; j < G::A_LOADS; ++j) *(lds_i16x8 *)(sa + (j * G::NW + wave) * 1024 + lane * 16) = ra[j];
-      if constexpr (!CONV) {
-        char *sb = sa + G::A_BYTES;
-#pragma unroll
-        for (int j = 0; j < G::B_LOADS; ++j) *(lds_i16x8 *)(sb + (j * G::NW + wave) * 1024 + lane * 16) = rb[j];
-      }
-    }
     if constexpr (CONV) {
       char *sb = smem + stage * G::STAGE_BYTES + G::A_BYTES;
 #pragma unroll
@@ -580,6 +581,10 @@ __global__ __launch_bounds__(G::THREADS) void tiled_gemm_kernel(KernelArgs p) {
   using I2 = std::integral_constant<int, (NSET > 2 ? 2 : 0)>;
   int kt = 0, cs = 0, ls = S - 1;
 
+  // The copies read buffer descriptors that may have just been written by a
+  // vector instruction (v_readfirstlane); five wait states cover that hazard
+  // once, before the first copy.
+  asm volatile("s_nop 4" ::: "memory");
   if constexpr (NSET == 1) {
     // -- prologue: stages 0 .. S-2 in flight
 #pragma unroll
