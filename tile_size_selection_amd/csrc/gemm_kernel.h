@@ -11,10 +11,12 @@
 //
 // Memory-hierarchy techniques of the same page, in their gfx950 form:
 //   * staging with a multi-stage pipeline: `stages` LDS buffers in a ring;
-//     K tile t+stages-1 is in flight while tile t is computed.  The copy is a
-//     direct HBM->LDS buffer load (buffer_load_dwordx4 ... lds) that bypasses
-//     registers, the analogue of the page's asynchronous copy, so several
-//     tiles are in flight without holding registers;
+//     the next stages-1 K tiles are in flight while one tile is computed.
+//     The copy is a direct HBM->LDS buffer load (buffer_load_dwordx4 ... lds)
+//     that bypasses registers, the analogue of the page's asynchronous copy,
+//     so several tiles are in flight without holding registers.  In the GEMM
+//     loop the copies are spread between the MFMAs and the next tile's
+//     fragments are read before the barrier that frees a stage (see the loop);
 //   * coalescing: each load instruction moves 64 lanes x 16 B = 1 KiB of whole
 //     rows;
 //   * bank-conflict-free LDS: 16-byte chunks are XOR-swizzled per row (the
@@ -36,6 +38,8 @@
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <utility>
 
 #include "../../include/tss.h"
 
@@ -68,6 +72,10 @@ struct KernelArgs {
 // ---- small device helpers --------------------------------------------------
 
 constexpr uint32_t kOOB = 0x80000000u;  // voffset beyond any accepted buffer range
+
+// GEMM main loop: MFMA rows of a tile's last step issued before the barrier
+// that frees a stage (measured at 4096^3 and 8192^3: 2 rows ahead of 0 and 1).
+constexpr int kBarrierRows = 2;
 
 // s_waitcnt with vmcnt = n and the other counters left alone (gfx9 encoding:
 // vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] in bits [15:14]).
@@ -104,15 +112,21 @@ __device__ __forceinline__ i32x4 buffer_rsrc(const void *base, uint32_t range) {
 }
 
 // Direct HBM -> LDS copy of 16 bytes per lane (buffer_load_dwordx4 ... lds):
-// lane i's 16 bytes land at dst + 16*i.  Issued as inline assembly because the
-// compiler, unable to tell which stage a later LDS read touches, would
-// otherwise make every LDS read wait for every copy in flight (vmcnt(0)),
-// which serializes the multi-stage ring.  The kernel orders the copies itself
-// with explicit s_waitcnt vmcnt + s_barrier pairs.  M0 holds the LDS address;
-// one wait state separates its write from the load that reads it.
-__device__ __forceinline__ void copy_to_lds16(i32x4 rs, uint32_t voff, const lds_void *dst) {
+// lane i's 16 bytes at byte offset voff + soff land at dst + 16*i.  Issued as
+// inline assembly because the compiler, unable to tell which stage a later
+// LDS read touches, would otherwise make every LDS read wait for every copy
+// in flight (vmcnt(0)), which serializes the multi-stage ring.  The kernel
+// orders the copies itself with explicit s_waitcnt vmcnt + s_barrier pairs.
+// M0 holds the LDS address; one wait state separates its write from the load
+// that reads it.  soff is wave-uniform (an SGPR): the K advance of a tile, so
+// the per-lane voff stays fixed over the K loop and costs no vector ALU work.
+// Callers keep voff + soff below 2^32 and give out-of-range lanes a voff at
+// or past the range on its own, so the result does not depend on whether the
+// hardware's range check includes soff.
+__device__ __forceinline__ void copy_to_lds16(i32x4 rs, uint32_t voff, uint32_t soff, const lds_void *dst) {
   const uint32_t m0 = uint32_t(reinterpret_cast<uintptr_t>(dst));
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rs), "s"(m0)
+  asm volatile("s_mov_b32 m0, %3\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds" ::"v"(voff), "s"(rs),
+               "s"(soff), "s"(m0)
                : "memory", "m0");
 }
 
@@ -430,24 +444,29 @@ __global__ __launch_bounds__(G::THREADS) void tiled_gemm_kernel(KernelArgs p) {
   constexpr int VPI = G::A_LOADS + (CONV ? 8 * G::B_LOADS : G::B_LOADS);
 
   const int nk = (K + G::BK - 1) / G::BK;
+  const int nfull = K / G::BK;  // K tiles that lie inside K
 
+  // One K tile of the convolution: the weights (A) go HBM -> LDS directly,
+  // the im2col rows of the input (B) are gathered into register set SET.
   auto issue = [&](int kt, int stage, auto set_c) __attribute__((always_inline)) {
     constexpr int SET = decltype(set_c)::value;
     const int k0 = kt * G::BK;
     char *sa = smem + stage * G::STAGE_BYTES;
+    // Every K tile but a ragged last one lies inside K: its copies take the
+    // fixed per-lane offsets and advance by k0 through the scalar offset.
+    // The ragged tile masks the chunks at or past K per lane.
+    if (k0 + G::BK <= K) {
 #pragma unroll
-    for (int j = 0; j < G::A_LOADS; ++j) {
-      uint32_t off = (k0 + a_kc[j] < K) ? a_off[j] + uint32_t(k0) * 2u : kOOB;
-      copy_to_lds16(rsA4, off, (lds_void *)(sa + (j * G::NW + wave) * 1024));
-    }
-    if constexpr (!CONV) {
-      char *sb = sa + G::A_BYTES;
-#pragma unroll
-      for (int j = 0; j < G::B_LOADS; ++j) {
-        uint32_t off = (k0 + b_k[j] < K) ? b_off[j] + uint32_t(k0) * uint32_t(N) * 2u : kOOB;
-        copy_to_lds16(rsB4, off, (lds_void *)(sb + (j * G::NW + wave) * 1024));
-      }
+      for (int j = 0; j < G::A_LOADS; ++j)
+        copy_to_lds16(rsA4, a_off[j], uint32_t(k0) * 2u, (lds_void *)(sa + (j * G::NW + wave) * 1024));
     } else {
+#pragma unroll
+      for (int j = 0; j < G::A_LOADS; ++j) {
+        uint32_t off = (k0 + a_kc[j] < K) ? a_off[j] + uint32_t(k0) * 2u : kOOB;
+        copy_to_lds16(rsA4, off, 0u, (lds_void *)(sa + (j * G::NW + wave) * 1024));
+      }
+    }
+    if constexpr (CONV) {
       const int khw = p.kh * p.kw;
       const int HW = p.H * p.W;
 #pragma unroll
@@ -467,6 +486,19 @@ __global__ __launch_bounds__(G::THREADS) void tiled_gemm_kernel(KernelArgs p) {
           g_reg[SET][j][e] = (short)__builtin_amdgcn_raw_buffer_load_b16(rsB, off, 0, 0);
         }
       }
+    }
+  };
+  // Copy j (0 .. LPW-1) of full K tile kt into `stage`: the A copies first,
+  // then the B copies (GEMM only).
+  auto issue_one = [&](int kt, int stage, int j) __attribute__((always_inline)) {
+    const int k0 = kt * G::BK;
+    char *sa = smem + stage * G::STAGE_BYTES;
+    if (j < G::A_LOADS) {
+      copy_to_lds16(rsA4, a_off[j], uint32_t(k0) * 2u, (lds_void *)(sa + (j * G::NW + wave) * 1024));
+    } else if constexpr (!CONV) {
+      const int jb = j - G::A_LOADS;
+      copy_to_lds16(rsB4, b_off[jb], uint32_t(k0) * uint32_t(N) * 2u,
+                    (lds_void *)(sa + G::A_BYTES + (jb * G::NW + wave) * 1024));
     }
   };
   // write the convolution's gathered B rows of a stage (after their loads
@@ -585,7 +617,164 @@ __global__ __launch_bounds__(G::THREADS) void tiled_gemm_kernel(KernelArgs p) {
   // vector instruction (v_readfirstlane); five wait states cover that hazard
   // once, before the first copy.
   asm volatile("s_nop 4" ::: "memory");
-  if constexpr (NSET == 1) {
+  if constexpr (!CONV) {
+    // GEMM.  Three changes to the plain ring further below, all against
+    // stalls of the matrix pipe:
+    //  * fragment reads cross the barrier: the last MFMA step of tile kt runs
+    //    on fragments already in registers while the first step's fragments
+    //    of tile kt+1 are read, and the barrier sits inside that last step,
+    //    after its first MFMA rows, so the pipe has work while the waves meet;
+    //  * the copies of the tile refilling the freed stage are spread over the
+    //    MFMA rows of that last step (a copy occupies the CU's load path for
+    //    about as long as four MFMAs; issued as a burst, they block the
+    //    in-order issue of every wave in front of its MFMAs);
+    //  * every tile refills a stage: refills past the last K tile copy zeros
+    //    into a stage nobody reads again, so the waits are the same for every
+    //    tile and one loop body serves the whole K loop.
+    // A fragments are single-buffered (slot i is refilled right after the
+    // last MFMA that reads it); B fragments are double-buffered, every MFMA
+    // row of a step reads all of them.  The steps alternate B buffers and
+    // every tile starts on buffer 0.
+    i16x8 fa_[G::TM], fb_[2][G::TN];
+    auto read_a = [&](const char *st, int q, int i) __attribute__((always_inline)) {
+      fa_[i] = *(const lds_i16x8 *)(st + fa[q] + i * MF * G::BK * 2);
+    };
+    auto read_b = [&](const char *st, int q, int pb, int j) __attribute__((always_inline)) {
+      const char *bp = st + fb[j] + q * G::FK * G::BN * 2;
+      i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(bp));
+      i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(bp + 4 * G::BN * 2));
+      fb_[pb][j] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    };
+    // Copy j of K tile ckt into stage cst: a full tile advances through the
+    // scalar offset; the ragged last tile masks the chunks at or past K per
+    // lane; a tile past the end reads zeros only.
+    auto copy = [&](int ckt, int cst, int j) __attribute__((always_inline)) {
+      if (ckt < nfull) {
+        issue_one(ckt, cst, j);
+      } else {
+        const int k0 = ckt * G::BK;
+        char *sa = smem + cst * G::STAGE_BYTES;
+        if (j < G::A_LOADS) {
+          const uint32_t off = (k0 + a_kc[j] < K) ? a_off[j] + uint32_t(k0) * 2u : kOOB;
+          copy_to_lds16(rsA4, off, 0u, (lds_void *)(sa + (j * G::NW + wave) * 1024));
+        } else {
+          const int jb = j - G::A_LOADS;
+          const uint32_t off = (k0 + b_k[jb] < K) ? b_off[jb] + uint32_t(k0) * uint32_t(N) * 2u : kOOB;
+          copy_to_lds16(rsB4, off, 0u, (lds_void *)(sa + G::A_BYTES + (jb * G::NW + wave) * 1024));
+        }
+      }
+    };
+    // One MFMA step on (fa_, fb_[PB]).  NEXT: the fragments of step nq of the
+    // stage at nst are read into (fa_, fb_[1-PB]) meanwhile, each A fragment
+    // right after its last MFMA row, the B fragments spread over the rows.
+    // COPY: the copies of K tile ckt into stage cst are spread over the
+    // rows (mode 2: ckt is a full K tile, copied without a per-copy test).  BAR >= 0: the step starts with BAR MFMA rows, then the wait and
+    // barrier that make stage nst readable and free stage cst; the reads and
+    // copies fill the rows from there on, while the MFMAs already issued keep
+    // the matrix pipe busy through the barrier.
+    auto step = [&](auto pb_c, auto next_c, auto copy_c, auto bar_c, const char *nst, int nq, int ckt, int cst)
+                    __attribute__((always_inline)) {
+      constexpr int PB = decltype(pb_c)::value;
+      constexpr bool NEXT = decltype(next_c)::value;
+      constexpr int COPY_MODE = decltype(copy_c)::value;  // 0 none, 1 any tile, 2 a full K tile
+      constexpr bool COPY = COPY_MODE != 0, COPY_FULL = COPY_MODE == 2;
+      constexpr int BAR = decltype(bar_c)::value;
+      constexpr int R0 = BAR > 0 ? BAR : 0;     // first row that may read or copy
+      constexpr int NR = G::TM - R0;            // rows that read and copy
+      auto row = [&](auto i_c) __attribute__((always_inline)) {
+        constexpr int i = decltype(i_c)::value;
+        if constexpr (i == BAR) {
+          __builtin_amdgcn_sched_barrier(0);
+          wait_vmcnt_lgkm0<(S - 2) * G::LPW>();  // the next tile has landed (this wave's copies)
+          block_barrier();                       // ... every wave's; the computed stage is free
+          __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int j = 0; j < G::TN; ++j) {
+          if constexpr (MF == 32) acc[i][j] = Mfma<T>::m32(fb_[PB][j], fa_[i], acc[i][j]);
+          else acc[i][j] = Mfma<T>::m16(fb_[PB][j], fa_[i], acc[i][j]);
+        }
+        if constexpr (i >= R0) {
+          constexpr int r = i - R0;
+          constexpr int a0 = r == 0 ? 0 : i, a1 = i + 1;                     // A fragments refilled here
+          constexpr int b0 = r * G::TN / NR, b1 = (r + 1) * G::TN / NR;     // B fragments read here
+          if constexpr (NEXT) {
+#pragma unroll
+            for (int j = b0; j < b1; ++j) read_b(nst, nq, 1 - PB, j);
+#pragma unroll
+            for (int a = a0; a < a1; ++a) read_a(nst, nq, a);
+            __builtin_amdgcn_sched_group_barrier(0x008, G::TN, 0);                        // the row's MFMAs
+            __builtin_amdgcn_sched_group_barrier(0x100, 2 * (b1 - b0) + (a1 - a0), 0);   // then its LDS reads
+          }
+          if constexpr (COPY) {
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int c = r * G::LPW / NR; c < (r + 1) * G::LPW / NR; ++c) {
+              if constexpr (COPY_FULL) issue_one(ckt, cst, c);
+              else copy(ckt, cst, c);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        } else {
+          __builtin_amdgcn_sched_group_barrier(0x008, G::TN, 0);
+        }
+      };
+      [&]<int... I>(std::integer_sequence<int, I...>) __attribute__((always_inline)) {
+        (row(std::integral_constant<int, I>{}), ...);
+      }(std::make_integer_sequence<int, G::TM>{});
+    };
+    using F = std::false_type;
+    using Tr = std::true_type;
+    using NoBar = std::integral_constant<int, -1>;
+    using BarRow = std::integral_constant<int, (kBarrierRows < G::TM ? kBarrierRows : G::TM - 1)>;
+    using C0 = std::integral_constant<int, 0>;
+    // One tile.  MODE 2: refill with a full K tile; 1: refill with any tile;
+    // 0: the last tile, no refill and no read-ahead.
+    auto tile = [&](auto mode_c) __attribute__((always_inline)) {
+      constexpr int MODE = decltype(mode_c)::value;
+      const char *st = smem + cs * G::STAGE_BYTES;
+      // steps 0 .. KSUB-2, each reading the next step's fragments from this stage
+      [&]<int... Q>(std::integer_sequence<int, Q...>) __attribute__((always_inline)) {
+        (step(std::integral_constant<int, Q & 1>{}, Tr{}, C0{}, NoBar{}, st, Q + 1, 0, 0), ...);
+      }(std::make_integer_sequence<int, G::KSUB - 1>{});
+      using PLast = std::integral_constant<int, (G::KSUB - 1) & 1>;
+      if constexpr (MODE != 0) {
+        const int ns = cs + 1 == S ? 0 : cs + 1;
+        step(PLast{}, Tr{}, mode_c, BarRow{}, smem + ns * G::STAGE_BYTES, 0, kt + S, cs);
+        if constexpr (PLast::value == 0) {
+          // odd number of steps: the next tile's first B fragments were read
+          // into buffer 1; move them so that every tile starts on buffer 0
+#pragma unroll
+          for (int j = 0; j < G::TN; ++j) fb_[0][j] = fb_[1][j];
+        }
+        cs = ns;
+        ++kt;
+      } else {
+        step(PLast{}, F{}, C0{}, NoBar{}, st, 0, 0, 0);
+      }
+    };
+
+    // prologue: tiles 0 .. S-1 in flight, tile 0's first fragments read
+#pragma unroll
+    for (int s = 0; s < S; ++s)
+#pragma unroll
+      for (int j = 0; j < G::LPW; ++j) copy(s, s, j);
+    wait_vmcnt_lgkm0<(S - 1) * G::LPW>();
+    block_barrier();
+    if (nk > 0) {
+#pragma unroll
+      for (int i = 0; i < G::TM; ++i) read_a(smem, 0, i);
+#pragma unroll
+      for (int j = 0; j < G::TN; ++j) read_b(smem, 0, 0, j);
+    }
+    // steady state: the refill is a full K tile; then the tiles whose refill
+    // is the ragged tile or past the end; then the last tile
+    while (kt + S < nfull) tile(std::integral_constant<int, 2>{});
+    while (kt + 1 < nk) tile(std::integral_constant<int, 1>{});
+    if (kt < nk) tile(C0{});
+    // the refills past the end are still landing in LDS, which the epilogue reuses
+    wait_vmcnt_lgkm0<0>();
+  } else if constexpr (NSET == 1) {
     // -- prologue: stages 0 .. S-2 in flight
 #pragma unroll
     for (int s = 0; s < S - 1; ++s)
