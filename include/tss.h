@@ -167,8 +167,10 @@ int32_t tss_evaluate(const tss_tile_config *cfg, const tss_device *dev, int64_t 
  *                 {16, 32, 64}, stages 2..4, threads {128, 256, 512}, both
  *                 MFMA shapes, 16x16x32 first (or the one in instr_filter);
  *                 key (ceil(grid / CUs) * (BM + BN), round(traffic), -BK,
- *                 -blocks/CU, -resident waves/CU, -stages, LDS bytes): the
- *                 first term is the C0 panel traffic of the busiest CU.
+ *                 -u, -u * waves/block, -stages, LDS bytes) with
+ *                 u = min(blocks/CU, ceil(grid / CUs)), the blocks a CU can
+ *                 actually hold: the first term is the C0 panel traffic of
+ *                 the busiest CU.
  * instr_filter: 0 = every shape of the device, else one TSS_INSTR_*.
  * best (nullable) receives the top verdict; list (nullable) the first
  * min(cap, n) verdicts in rank order; *n_feasible (nullable) the count.
@@ -211,19 +213,35 @@ int32_t tss_gemm(int64_t M, int64_t N, int64_t K, int32_t dtype, const void *A, 
 /*
  * 2-D convolution, NCHW input x[N][C][H][W], OIHW weights w[Cout][C][kh][kw],
  * output y[N][Cout][OH][OW] with OH = (H + 2ph - (kh-1)dh - 1)/sh + 1 and OW
- * likewise, computed as an implicit GEMM (M = Cout, N = pixels, K = C*kh*kw)
- * over output-row tiles of tile_oh rows.  Each H-tile reads exactly its
- * input slice [in_start, min(in_end, H)) with the sub-operator pads of the
- * Tiling page's formulas (tss_hw_tile); the batch never crosses a tile.
+ * likewise, computed as an implicit GEMM (M = Cout, N = pixels, K over the
+ * kh*kw taps and the channels) over output-row tiles of tile_oh rows.  Each
+ * H-tile reads exactly its input slice [in_start, min(in_end, H)) with the
+ * sub-operator pads of the Tiling page's H/W tiling formulas (tss_hw_tile);
+ * the batch never crosses a tile.
+ * Two launches on `stream`: the operands are first rewritten into
+ * `workspace` (input channel-last x[n][h][w][c], weights w[o][r][s][c], the
+ * channels zero-padded to Cp = C rounded up to a multiple of the tile's K
+ * step, 16, 32 or 64), then the implicit GEMM reads them.  workspace: device memory of at least
+ * tss_conv2d_workspace_size(...) bytes, 16-byte aligned, owned by the caller;
+ * its contents are scratch and are overwritten on every call (calls that
+ * share a workspace must be ordered on one stream).
  * dtype TSS_F16 / TSS_BF16, fp32 accumulation, out_dtype TSS_F32 or dtype.
  * tile_oh in [1, OH]; cfg NULL = planner's choice for the GEMM
- * (Cout x N*OH*OW x C*kh*kw).  Requirements: C*kh*kw a multiple of 8;
- * x, w, y 16-byte aligned.  Errors as tss_gemm.
+ * (Cout x N*OH*OW x kh*kw*Cp).  x, w, y 16-byte aligned.
+ * Errors: TSS_E_ARG (also for a missing or too small workspace), TSS_E_DTYPE,
+ * TSS_E_ALIGN, TSS_E_INFEASIBLE, TSS_E_UNSUPPORTED, TSS_E_HIP.
  */
 int32_t tss_conv2d(int64_t N, int64_t C, int64_t H, int64_t W, int64_t Cout, int64_t kh,
                    int64_t kw, int64_t sh, int64_t sw, int64_t ph, int64_t pw, int64_t dh,
                    int64_t dw, int64_t tile_oh, int32_t dtype, int32_t out_dtype, const void *x,
-                   const void *w, void *y, const tss_tile_config *cfg, void *stream);
+                   const void *w, void *y, void *workspace, int64_t workspace_bytes,
+                   const tss_tile_config *cfg, void *stream);
+
+/* Bytes of workspace tss_conv2d needs for these sizes with any tile
+   configuration (channels padded to 64), or TSS_E_ARG (< 0) for sizes
+   tss_conv2d would reject as non-positive or above 2^30. */
+int64_t tss_conv2d_workspace_size(int64_t N, int64_t C, int64_t H, int64_t W, int64_t Cout,
+                                  int64_t kh, int64_t kw);
 
 /* 1 if a kernel is compiled for cfg and dtype (op 0 = GEMM, 1 = conv), else 0. */
 int32_t tss_kernel_available(const tss_tile_config *cfg, int32_t dtype, int32_t op);

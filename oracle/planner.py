@@ -329,15 +329,17 @@ def rank_key(v: Verdict, dev: DeviceModel):
     quantization), then least total traffic (C0); then, as the Tiling page's
     rules of thumb advise when on-chip memory has room, the larger block_K;
     then most resident blocks and most resident waves per CU (occupancy, that
-    page's third constraint); then the deeper pipeline; then less LDS.
+    page's third constraint), counting only the blocks the grid can supply
+    (a CU never holds more than ceil(grid / cores) blocks at once); then the
+    deeper pipeline; then less LDS.
     """
     t = round_half_even(v.traffic)
     if dev.ranking == "pages":
         return (t, -v.blocks_per_core, v.smem_total)
     c = v.config
-    resident_waves = v.blocks_per_core * (c.threads // dev.lane_count)
-    return (busiest_core_traffic(v, dev), t, -c.block_k, -v.blocks_per_core, -resident_waves, -c.stages,
-            v.smem_total)
+    usable = min(v.blocks_per_core, _ceil_div(v.grid, dev.cores))
+    resident_waves = usable * (c.threads // dev.lane_count)
+    return (busiest_core_traffic(v, dev), t, -c.block_k, -usable, -resident_waves, -c.stages, v.smem_total)
 
 
 def candidates(dev: DeviceModel, k: int, instrs: Sequence[str]):

@@ -22,7 +22,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 def test_library_exports_every_declared_symbol():
     with open(os.path.join(ROOT, "include", "tss.h")) as f:
         hdr = f.read()
-    declared = set(re.findall(r"^(?:int32_t|const char \*)\s*(tss_\w+)\(", hdr, flags=re.M))
+    declared = set(re.findall(r"^(?:int32_t|int64_t|const char \*)\s*(tss_\w+)\(", hdr, flags=re.M))
     assert declared == set(C.EXPORTS)
     L = C.lib()
     for name in declared:
@@ -155,14 +155,26 @@ def test_argument_errors_before_device_work():
     nv = C.TileConfig(128, 128, 32, 2, 256, C.INSTR["wgmma"])
     assert g(64, 64, 64, C.TSS_F16, 16, 16, 16, 1, C.TSS_F32, ctypes.byref(nv), None) == C.TSS_E_ARG
     cv = lambda *a: L.tss_conv2d(*a)
+    wsz = L.tss_conv2d_workspace_size
+    # channel-last input at offset 0, reordered weights at the next 256-byte boundary; channels rounded up
+    # to 64 (the largest K step a tile can take)
+    assert wsz(8, 256, 56, 56, 256, 3, 3) == 8 * 56 * 56 * 256 * 2 + 256 * 9 * 256 * 2
+    assert wsz(2, 3, 5, 5, 4, 3, 3) == 2 * 5 * 5 * 64 * 2 + 4 * 9 * 64 * 2     # 6400 B: already aligned
+    assert wsz(1, 8, 1, 1, 4, 1, 1) == 256 + 4 * 64 * 2                         # xc 64*2 = 128 B -> 256
+    assert wsz(1, 72, 1, 3, 8, 1, 1) == 3 * 128 * 2 + 8 * 128 * 2              # C 72 -> 128 channels
+    assert wsz(0, 3, 5, 5, 4, 3, 3) == C.TSS_E_ARG
+    assert wsz(1, 1 << 31, 5, 5, 4, 3, 3) == C.TSS_E_ARG
     base = [8, 256, 56, 56, 256, 3, 3, 2, 2, 1, 1, 1, 1]
-    assert cv(*base, 0, C.TSS_F16, C.TSS_F32, 16, 16, 16, None, None) == C.TSS_E_ARG        # tile_oh 0
-    assert cv(*base, 29, C.TSS_F16, C.TSS_F32, 16, 16, 16, None, None) == C.TSS_E_ARG       # tile_oh > OH
-    assert cv(*[8, 3, 56, 56, 256, 3, 3, 2, 2, 1, 1, 1, 1], 8, C.TSS_F16, C.TSS_F32, 16, 16, 16, None,
-              None) == C.TSS_E_ALIGN                                                         # C*kh*kw = 27
-    assert cv(*base, 8, C.TSS_F32, C.TSS_F32, 16, 16, 16, None, None) == C.TSS_E_DTYPE
-    assert cv(*base, 8, C.TSS_F16, C.TSS_F32, 16, 24, 16, None, None) == C.TSS_E_ALIGN
-    assert cv(*[8, 256, 1, 56, 256, 3, 3, 2, 2, 0, 1, 1, 1], 1, C.TSS_F16, C.TSS_F32, 16, 16, 16, None,
+    ws = wsz(*base[:7])
+    ok_ptrs = [16, 16, 16, 256, ws]
+    assert cv(*base, 0, C.TSS_F16, C.TSS_F32, *ok_ptrs, None, None) == C.TSS_E_ARG          # tile_oh 0
+    assert cv(*base, 29, C.TSS_F16, C.TSS_F32, *ok_ptrs, None, None) == C.TSS_E_ARG         # tile_oh > OH
+    assert cv(*base, 8, C.TSS_F32, C.TSS_F32, *ok_ptrs, None, None) == C.TSS_E_DTYPE
+    assert cv(*base, 8, C.TSS_F16, C.TSS_F32, 16, 24, 16, 256, ws, None, None) == C.TSS_E_ALIGN
+    assert cv(*base, 8, C.TSS_F16, C.TSS_F32, 16, 16, 16, None, ws, None, None) == C.TSS_E_ARG   # no workspace
+    assert cv(*base, 8, C.TSS_F16, C.TSS_F32, 16, 16, 16, 256, ws - 1, None, None) == C.TSS_E_ARG  # too small
+    assert cv(*base, 8, C.TSS_F16, C.TSS_F32, 16, 16, 16, 264, ws, None, None) == C.TSS_E_ALIGN  # misaligned
+    assert cv(*[8, 256, 1, 56, 256, 3, 3, 2, 2, 0, 1, 1, 1], 1, C.TSS_F16, C.TSS_F32, *ok_ptrs, None,
               None) == C.TSS_E_ARG                                                           # window > input
     assert L.tss_evaluate(ctypes.byref(cfg), None, 0, 1, 1, 1, 2, ctypes.byref(C.Verdict())) == C.TSS_E_ARG
     assert L.tss_hw_tile(9, 3, 2, 1, 1, 2, 2, ctypes.byref(C.HwSlice())) == C.TSS_E_ARG

@@ -48,6 +48,8 @@ CASES = [  # N, C, H, W, Co, kh, kw, stride, pad, dil, tile_oh
     (1, 64, 8, 8, 72, 1, 1, (1, 1), (0, 0), (1, 1), 3),      # 1x1: a plain GEMM
     (2, 8, 11, 4, 16, 2, 2, (3, 2), (0, 1), (1, 2), 1),
     (1, 24, 30, 30, 136, 3, 3, (2, 2), (1, 1), (1, 1), 7),   # ragged channel tiles
+    (2, 3, 17, 17, 16, 3, 3, (2, 2), (1, 1), (1, 1), 4),     # 3 channels, padded to 8 in the channel-last copy
+    (1, 12, 10, 12, 8, 3, 2, (1, 1), (1, 0), (1, 1), 10),    # C*kh*kw = 72, Cp = 16
 ]
 
 
@@ -77,3 +79,26 @@ def test_conv_low_precision_output():
     y = tss.conv2d(x.to(CUDA), wt.to(CUDA), w.stride, w.pad, w.dil, tile_oh=8)
     assert y.dtype == torch.float16
     check_bound(to_f64(y), ref, S, "conv f16 out")
+
+
+def test_conv_workspace_reuse_and_errors():
+    """A caller-owned workspace serves calls of different sizes in a row on
+    one stream; a workspace below tss_conv2d_workspace_size is rejected
+    before anything is launched."""
+    big = (2, 16, 13, 11, 24, 3, 3)
+    small = (1, 8, 9, 9, 16, 3, 3)
+    nbytes = tss.conv2d_workspace_size(*big)
+    assert nbytes == 2 * 13 * 11 * 64 * 2 + 24 * 9 * 64 * 2     # channels padded to 64; 36608 B is 256-aligned
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=CUDA)
+    for shape, seed in ((big, 61), (small, 63), (big, 65)):
+        N, Ci, H, W, Co, kh, kw = shape
+        x = draw((N, Ci, H, W), "int", -2, 2, "f16", seed)
+        w = draw((Co, Ci, kh, kw), "int", -2, 2, "f16", seed + 1)
+        ref, _ = G.conv2d(x.double().numpy(), w.double().numpy(), (2, 1), (1, 1), (1, 1))
+        y = tss.conv2d(x.to(CUDA), w.to(CUDA), (2, 1), (1, 1), 1, tile_oh=2, out_dtype="f32", workspace=ws)
+        torch.cuda.synchronize()
+        assert np.array_equal(to_f64(y), ref), shape
+    x = torch.zeros((2, 16, 13, 11), dtype=torch.float16, device=CUDA)
+    w = torch.zeros((24, 16, 3, 3), dtype=torch.float16, device=CUDA)
+    with pytest.raises(ValueError):
+        tss.conv2d(x, w, 1, 1, 1, workspace=ws[: nbytes - 1])

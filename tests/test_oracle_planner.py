@@ -231,8 +231,13 @@ def test_gfx950_conv_and_small_shape_choices():
     g = P.device_gfx950()
     ins = [s for s, _ in g.instr_shapes]
     c = P.sweep(256, 6272, 2304, g, ins)[0].config
-    # 128x64 and 64x128 tie on every key but order: the taller tile comes first
-    assert (c.block_m, c.block_n, c.block_k, c.stages, c.threads, c.instr) == (128, 64, 64, 2, 512, "mfma16")
+    # 128x64 and 64x128 tie on every key but order: the taller tile comes first.  Its 196 tiles leave every CU
+    # one block at most, so the LDS room for 3 blocks of a 2-stage ring buys nothing and the 4-stage ring wins
+    assert (c.block_m, c.block_n, c.block_k, c.stages, c.threads, c.instr) == (128, 64, 64, 4, 512, "mfma16")
+    v = P.sweep(256, 6272, 2304, g, ins)[0]
+    assert v.blocks_per_core == 1 and P.rank_key(v, g)[3:6] == (-1, -8, -4)
+    two = P.finish_parallelism(P.evaluate(P.TileConfig(128, 64, 64, 2, 512, "mfma16"), g), 256, 6272, g)
+    assert two.blocks_per_core == 3 and P.rank_key(two, g)[3:6] == (-1, -8, -2)   # 3 resident, 1 usable
     c = P.sweep(256, 256, 256, g, ins)[0].config
     assert (c.block_m, c.block_n) == (64, 64)     # 16 tiles over 16 CUs beat one 256x256 tile
     c = P.sweep(3000, 5000, 2048, g, ins, batch=4)[0].config

@@ -153,11 +153,22 @@ def gemm(A, B, out_dtype: Optional[str] = None, cfg: Optional[TileConfig] = None
     return out
 
 
+def conv2d_workspace_size(N: int, Ci: int, H: int, W: int, Cout: int, kh: int, kw: int) -> int:
+    """Bytes of device workspace tss_conv2d needs for these sizes (Ci input
+    channels)."""
+    n = C.lib().tss_conv2d_workspace_size(N, Ci, H, W, Cout, kh, kw)
+    if n < 0:
+        C.check(int(n), "tss_conv2d_workspace_size")
+    return int(n)
+
+
 def conv2d(x, w, stride: Union[int, Sequence[int]] = 1, padding: Union[int, Sequence[int]] = 0,
            dilation: Union[int, Sequence[int]] = 1, tile_oh: Optional[int] = None, out_dtype: Optional[str] = None,
-           cfg: Optional[TileConfig] = None, out=None, stream=None):
+           cfg: Optional[TileConfig] = None, out=None, stream=None, workspace=None):
     """NCHW convolution as an implicit GEMM over output-row tiles of tile_oh
-    rows (default: the whole output height)."""
+    rows (default: the whole output height).  workspace: optional device
+    tensor of at least conv2d_workspace_size(...) bytes for the operands'
+    channel-last copies (allocated here when not given)."""
     pair = lambda v: (v, v) if isinstance(v, int) else tuple(v)
     (sh, sw), (ph, pw), (dh, dw) = pair(stride), pair(padding), pair(dilation)
     if x.dim() != 4 or w.dim() != 4 or x.dtype != w.dtype:
@@ -178,8 +189,17 @@ def conv2d(x, w, stride: Union[int, Sequence[int]] = 1, padding: Union[int, Sequ
         out = torch.empty(shape, dtype=tdt, device=x.device)
     elif tuple(out.shape) != shape or out.dtype != tdt or not out.is_contiguous():
         raise ValueError("out has the wrong shape, dtype or layout")
+    ws_bytes = conv2d_workspace_size(N, Ci, H, W, Co, kh, kw)
+    if workspace is None:
+        # torch's caching allocator: device memory only, no host copy; the
+        # convolution's two launches fill and read it on the same stream
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=x.device)
+    elif not (workspace.is_cuda and workspace.is_contiguous() and workspace.numel() * workspace.element_size()
+              >= ws_bytes):
+        raise ValueError(f"workspace must be a contiguous device tensor of at least {ws_bytes} bytes")
     st = C.lib().tss_conv2d(N, Ci, H, W, Co, kh, kw, sh, sw, ph, pw, dh, dw, tile_oh or OH, _DT[dt], _DT[od],
-                            x.data_ptr(), w.data_ptr(), out.data_ptr(), ctypes.byref(cfg.c()) if cfg else None,
+                            x.data_ptr(), w.data_ptr(), out.data_ptr(), workspace.data_ptr(),
+                            workspace.numel() * workspace.element_size(), ctypes.byref(cfg.c()) if cfg else None,
                             _stream_ptr(stream))
     C.check(st, "tss_conv2d")
     return out

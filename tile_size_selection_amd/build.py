@@ -25,8 +25,14 @@ LIB = os.path.join(PKG, "libtss.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # -packed-fp32-ops off: compiler-made v_pk_{add,mul,fma}_f32 are avoided.
+# amdgpu-mfma-vgpr-form: MFMA accumulators stay in the architectural VGPRs.
+# Left to its heuristic, the compiler put part of the accumulators of 4-wave
+# tiles in AGPRs and copied them into the MFMA's source registers before
+# most MFMAs (e.g. 300 accvgpr moves in the 128x128x64/256-thread
+# convolution loop); with the flag the accumulators are updated in place.
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++20", "-fPIC", "-Wall", "-Wno-unused-variable",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         "-mllvm", "-amdgpu-mfma-vgpr-form=true",
          "-I", os.path.join(ROOT, "include")]
 
 
@@ -35,20 +41,49 @@ def sources():
             + sorted(glob.glob(os.path.join(CSRC, "inst", "*.hip"))))
 
 
-def _headers_mtime():
-    hs = glob.glob(os.path.join(CSRC, "*.h")) + glob.glob(os.path.join(CSRC, "*.inc")) + \
-        glob.glob(os.path.join(ROOT, "include", "*.h"))
-    return max(os.path.getmtime(h) for h in hs)
-
-
 def _obj(src):
     rel = os.path.relpath(src, CSRC).replace(os.sep, "_")
     return os.path.join(OUT_DIR, rel + ".o")
 
 
+def _flags_stamp():
+    """A file whose content is the compile flags; rewritten (and so newer
+    than every object) when they change."""
+    path = os.path.join(OUT_DIR, "flags.txt")
+    text = " ".join([HIPCC] + FLAGS)
+    if not os.path.exists(path) or open(path).read() != text:
+        with open(path, "w") as f:
+            f.write(text)
+    return path
+
+
+def _up_to_date(src, obj):
+    """True if obj is newer than src, the compile flags and every file its
+    dependency list (written by the compiler next to it) names."""
+    dep = obj[:-2] + ".d"
+    if not (os.path.exists(obj) and os.path.exists(dep)):
+        return False
+    if os.path.getmtime(_flags_stamp()) >= os.path.getmtime(obj):
+        return False
+    with open(dep) as f:
+        text = f.read().replace("\\\n", " ")
+    files = text.split(":", 1)[1].split() if ":" in text else []
+    t = os.path.getmtime(obj)
+    return all(os.path.exists(d) and os.path.getmtime(d) < t for d in [src] + files)
+
+
+def _flags_for(src):
+    """The wide-accumulator units (256 accumulators per lane) keep the
+    compiler's own accumulator placement: the in-VGPR form does not fit them
+    (and this compiler fails on them with it)."""
+    if src.endswith("_wide.hip"):
+        return [f for f in FLAGS if f not in ("-mllvm", "-amdgpu-mfma-vgpr-form=true")]
+    return FLAGS
+
+
 def _compile(src, obj):
     t0 = time.time()
-    cmd = [HIPCC, *FLAGS, "-x", "hip", "-c", src, "-o", obj]
+    cmd = [HIPCC, *_flags_for(src), "-x", "hip", "-c", src, "-o", obj, "-MD", "-MF", obj[:-2] + ".d"]
     r = subprocess.run(cmd, capture_output=True, text=True)
     errs = "\n".join(l for l in (r.stderr or "").splitlines() if "packed-fp32-ops" not in l)
     if r.returncode != 0:
@@ -58,11 +93,10 @@ def _compile(src, obj):
 
 def build(incremental: bool = False, jobs: int = 0, verbose: bool = True) -> str:
     os.makedirs(OUT_DIR, exist_ok=True)
-    hm = _headers_mtime()
     todo = []
     for s in sources():
         o = _obj(s)
-        if incremental and os.path.exists(o) and os.path.getmtime(o) > max(os.path.getmtime(s), hm):
+        if incremental and _up_to_date(s, o):
             continue
         todo.append((s, o))
     jobs = jobs or min(16, os.cpu_count() or 4)

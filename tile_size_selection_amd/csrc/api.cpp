@@ -9,6 +9,7 @@
 #include <tuple>
 #include <vector>
 
+#include "conv_layout.h"
 #include "planner.h"
 #include "registry.h"
 
@@ -30,7 +31,11 @@ const std::map<Key, KernelEntry> &registry() {
     KernelTable (*tables[])() = {table_gemm_f16_bm64,  table_gemm_f16_bm128,  table_gemm_f16_bm256,
                                  table_gemm_bf16_bm64, table_gemm_bf16_bm128, table_gemm_bf16_bm256,
                                  table_conv_f16_bm64,  table_conv_f16_bm128,  table_conv_f16_bm256,
-                                 table_conv_bf16_bm64, table_conv_bf16_bm128, table_conv_bf16_bm256};
+                                 table_conv_bf16_bm64, table_conv_bf16_bm128, table_conv_bf16_bm256,
+                                 table_gemm_f16_bm128_wide,  table_gemm_f16_bm256_wide,
+                                 table_gemm_bf16_bm128_wide, table_gemm_bf16_bm256_wide,
+                                 table_conv_f16_bm128_wide,  table_conv_f16_bm256_wide,
+                                 table_conv_bf16_bm128_wide, table_conv_bf16_bm256_wide};
     for (auto fn : tables) {
       KernelTable t = fn();
       for (int i = 0; i < t.n; ++i) {
@@ -91,6 +96,26 @@ int group_m_for(int tiles_m) {
 }
 
 constexpr int64_t kTwoGiB = int64_t(1) << 31;
+constexpr int64_t kConvChannelAlignMax = 64;  // the largest BK of the gfx950 candidate space
+
+// Workspace of tss_conv2d: the channel-last input copy xc, then (at a
+// 256-byte aligned offset) the reordered weights wr.
+struct ConvWorkspace {
+  int64_t Cp, xc_bytes, wr_offset, wr_bytes, total;
+};
+// Cp = C rounded up to a multiple of `align` (the tile's BK when launching,
+// so that a K tile never straddles two taps; 64, the largest BK, for the
+// size a caller allocates).
+ConvWorkspace conv_workspace(int64_t N, int64_t C, int64_t H, int64_t W, int64_t Cout, int64_t kh, int64_t kw,
+                             int64_t align) {
+  ConvWorkspace ws;
+  ws.Cp = (C + align - 1) / align * align;
+  ws.xc_bytes = N * H * W * ws.Cp * 2;
+  ws.wr_offset = (ws.xc_bytes + 255) / 256 * 256;
+  ws.wr_bytes = Cout * kh * kw * ws.Cp * 2;
+  ws.total = ws.wr_offset + ws.wr_bytes;
+  return ws;
+}
 
 }  // namespace
 
@@ -166,10 +191,18 @@ int32_t tss_gemm(int64_t M, int64_t N, int64_t K, int32_t dtype, const void *A, 
   return err == hipSuccess ? TSS_OK : TSS_E_HIP;
 }
 
+int64_t tss_conv2d_workspace_size(int64_t N, int64_t C, int64_t H, int64_t W, int64_t Cout, int64_t kh,
+                                  int64_t kw) {
+  const int64_t lim = int64_t(1) << 30;
+  if (N < 1 || C < 1 || H < 1 || W < 1 || Cout < 1 || kh < 1 || kw < 1) return TSS_E_ARG;
+  if (N > lim || C > lim || H > lim || W > lim || Cout > lim || kh > lim || kw > lim) return TSS_E_ARG;
+  return conv_workspace(N, C, H, W, Cout, kh, kw, kConvChannelAlignMax).total;
+}
+
 int32_t tss_conv2d(int64_t N, int64_t C, int64_t H, int64_t W, int64_t Cout, int64_t kh, int64_t kw, int64_t sh,
                    int64_t sw, int64_t ph, int64_t pw, int64_t dh, int64_t dw, int64_t tile_oh, int32_t dtype,
-                   int32_t out_dtype, const void *x, const void *w, void *y, const tss_tile_config *cfg,
-                   void *stream) {
+                   int32_t out_dtype, const void *x, const void *w, void *y, void *workspace,
+                   int64_t workspace_bytes, const tss_tile_config *cfg, void *stream) {
   const int64_t lim = int64_t(1) << 30;
   if (N < 1 || C < 1 || H < 1 || W < 1 || Cout < 1 || kh < 1 || kw < 1 || sh < 1 || sw < 1 || ph < 0 || pw < 0 ||
       dh < 1 || dw < 1)
@@ -183,30 +216,63 @@ int32_t tss_conv2d(int64_t N, int64_t C, int64_t H, int64_t W, int64_t Cout, int
   const int64_t OW = (W + 2 * pw - (kw - 1) * dw - 1) / sw + 1;
   if (H + 2 * ph < (kh - 1) * dh + 1 || W + 2 * pw < (kw - 1) * dw + 1) return TSS_E_ARG;
   if (tile_oh < 1 || tile_oh > OH) return TSS_E_ARG;
-  const int64_t Kc = C * kh * kw;
-  if (Kc % 8) return TSS_E_ALIGN;
-  if (N * C * H * W * 2 >= kTwoGiB || Cout * Kc * 2 >= kTwoGiB || Kc > INT32_MAX) return TSS_E_ARG;
+  // sizes with the largest channel padding any tile can ask for
+  const ConvWorkspace wmax = conv_workspace(N, C, H, W, Cout, kh, kw, kConvChannelAlignMax);
+  // every operand, and both layout copies, addressable with 32-bit byte offsets
+  if (N * C * H * W * 2 >= kTwoGiB || Cout * C * kh * kw * 2 >= kTwoGiB || wmax.xc_bytes >= kTwoGiB ||
+      wmax.wr_bytes >= kTwoGiB || kh * kw * wmax.Cp > INT32_MAX)
+    return TSS_E_ARG;
   const int64_t out_bytes = out_dtype == TSS_F32 ? 4 : 2;
   if (N * Cout * OH * OW * out_bytes >= (int64_t(1) << 40)) return TSS_E_ARG;
   const int64_t tile_pixels = N * tile_oh * OW;
   if (tile_pixels > INT32_MAX) return TSS_E_ARG;
-  if (!x || !w || !y) return TSS_E_ARG;
-  if (!aligned16(x) || !aligned16(w) || !aligned16(y)) return TSS_E_ALIGN;
+  if (!x || !w || !y || !workspace) return TSS_E_ARG;
+  if (workspace_bytes < wmax.total) return TSS_E_ARG;
+  if (!aligned16(x) || !aligned16(w) || !aligned16(y) || !aligned16(workspace)) return TSS_E_ALIGN;
   tss_tile_config c{};
   if (cfg) {
     c = *cfg;
     int32_t st = check_config(c);
     if (st != TSS_OK) return st;
   } else {
-    // The implicit GEMM: M = Cout, N = every output pixel, K = C*kh*kw.
-    int32_t st = planned_config(1, Cout, N * OH * OW, Kc, &c);
+    // The implicit GEMM: M = Cout, N = every output pixel, K = kh*kw*C
+    // (channels rounded up to 8 for the plan; the tile's BK pads them next).
+    int32_t st = planned_config(1, Cout, N * OH * OW, kh * kw * ((C + 7) / 8 * 8), &c);
     if (st != TSS_OK) return st;
   }
   const KernelEntry *e = find_kernel(c, dtype, 1);
   if (!e) return TSS_E_UNSUPPORTED;
+  const ConvWorkspace ws = conv_workspace(N, C, H, W, Cout, kh, kw, c.bk);
+  const int64_t Kc = kh * kw * ws.Cp;  // K of the implicit GEMM, over (r, s, ci)
+
+  // 1. operands in (r, s, ci) order: channel-last input, reordered weights
+  uint16_t *xc = static_cast<uint16_t *>(workspace);
+  uint16_t *wr = reinterpret_cast<uint16_t *>(static_cast<char *>(workspace) + ws.wr_offset);
+  LayoutArgs la{};
+  la.x = static_cast<const uint16_t *>(x);
+  la.xc = xc;
+  la.w = static_cast<const uint16_t *>(w);
+  la.wr = wr;
+  la.N = int32_t(N);
+  la.C = int32_t(C);
+  la.HW = int32_t(H * W);
+  la.Cp = int32_t(ws.Cp);
+  la.Cout = int32_t(Cout);
+  la.KHW = int32_t(kh * kw);
+  la.c_tiles = int32_t((ws.Cp + 63) / 64);
+  la.p_tiles = int32_t((H * W + 63) / 64);
+  const int64_t x_blocks = N * la.c_tiles * la.p_tiles;
+  const int64_t w_blocks = Cout;  // one block per output channel
+  if (x_blocks + w_blocks > int64_t(INT32_MAX)) return TSS_E_ARG;
+  hipLaunchKernelGGL(conv_layout_kernel, dim3(uint32_t(w_blocks + x_blocks)), dim3(kLayoutThreads), 0,
+                     (hipStream_t)stream, la);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return TSS_E_HIP;
+
+  // 2. the implicit GEMM over H-tiles
   KernelArgs a{};
-  a.A = w;
-  a.B = x;
+  a.A = wr;
+  a.B = xc;
   a.C = y;
   a.M = int32_t(Cout);
   a.N = int32_t(tile_pixels);
@@ -230,10 +296,11 @@ int32_t tss_conv2d(int64_t N, int64_t C, int64_t H, int64_t W, int64_t Cout, int
   a.OH = int32_t(OH);
   a.OW = int32_t(OW);
   a.tile_oh = int32_t(tile_oh);
+  a.Cp = int32_t(ws.Cp);
   const int64_t n_htiles = (OH + tile_oh - 1) / tile_oh;
   const int64_t blocks = n_htiles * a.tiles_m * a.tiles_n;
   if (blocks * c.threads > int64_t(UINT32_MAX)) return TSS_E_ARG;
-  hipError_t err = e->launch(a, dim3(uint32_t(blocks)), e->stage_bytes * c.stages, (hipStream_t)stream);
+  err = e->launch(a, dim3(uint32_t(blocks)), e->stage_bytes * c.stages, (hipStream_t)stream);
   return err == hipSuccess ? TSS_OK : TSS_E_HIP;
 }
 

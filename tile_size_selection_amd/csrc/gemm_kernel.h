@@ -29,12 +29,14 @@
 // epilogue masks rows >= M and columns >= N.
 //
 // The same kernel computes a convolution as an implicit GEMM (CONV = true):
-// A is the OIHW weight matrix (Cout x C*kh*kw, K-contiguous, loaded exactly as
-// the GEMM's A); B is the im2col matrix of one H-tile, gathered element by
-// element from the NCHW input into the B layout of the GEMM; the batch index
+// A is the weight matrix Cout x (kh*kw*Cp) with K ordered (r, s, ci), loaded
+// exactly as the GEMM's A; B is the im2col matrix of one H-tile, stored in
+// LDS transposed (pixels x K, laid out like A) and copied HBM -> LDS from a
+// channel-last copy of the input, 16 bytes (8 channels of one input pixel)
+// per lane.  Both operand copies come from conv_layout.h.  The batch index
 // of the GEMM is the H-tile.  Each block derives its input slice and the
-// sub-operator pads from the Tiling page's H/W tiling formulas; rows of the
-// slice's pads read as zero.
+// sub-operator pads from the Tiling page's H/W tiling formulas; chunks that
+// fall in a pad or outside the slice read as zero.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -57,16 +59,17 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 typedef __attribute__((address_space(3))) i16x8 lds_i16x8;
 
 struct KernelArgs {
-  const void *A;  // GEMM: A[batch][M][K].       conv: weights [Cout][C*kh*kw]
-  const void *B;  // GEMM: B[batch][K][N].       conv: input x[Nb][C][H][W]
+  const void *A;  // GEMM: A[batch][M][K].       conv: weights wr[Cout][kh][kw][Cp]
+  const void *B;  // GEMM: B[batch][K][N].       conv: input xc[Nb][H][W][Cp]
   void *C;        // GEMM: C[batch][M][N].       conv: output y[Nb][Cout][OH][OW]
-  int32_t M, N, K;  // conv: M = Cout, K = C*kh*kw, N = pixels of a full H-tile
+  int32_t M, N, K;  // conv: M = Cout, K = kh*kw*Cp, N = pixels of a full H-tile
   int32_t tiles_m, tiles_n;
   int32_t group_m;    // tile rows per group of the L2-friendly tile order
   int32_t out_dtype;  // TSS_F32 / TSS_F16 / TSS_BF16
   int64_t batch_stride_a, batch_stride_b, batch_stride_c;  // GEMM only, elements
   // convolution geometry (CONV only); the GEMM batch index is the H-tile
   int32_t Nb, Cin, H, W, kh, kw, sh, sw, ph, pw, dh, dw, OH, OW, tile_oh;
+  int32_t Cp;  // channels of the channel-last input copy: Cin rounded up to a multiple of BK
 };
 
 // ---- small device helpers --------------------------------------------------
@@ -303,7 +306,10 @@ __device__ __forceinline__ void store_tile(const Acc (&acc)[G::TM][G::TN], O *C,
 }
 
 // Convolution epilogue: row = output channel, column = pixel of the H-tile
-// (image n, output row o0 + oh_l, output column ow); y is NCHW.
+// (image n, output row o0 + oh_l, output column ow); y is NCHW.  The pixels
+// a lane holds do not depend on the MFMA row, so each is decoded once: the
+// first of every group of 4 consecutive columns by division, the next three
+// by stepping (ow, oh_l, n) forward.
 template <typename G, typename O, typename Acc>
 __device__ __forceinline__ void store_conv(const Acc (&acc)[G::TM][G::TN], O *y, const KernelArgs &p, int m0, int n0,
                                            int wr, int wc, int lane, int o0, int rows_t, int npix) {
@@ -311,6 +317,29 @@ __device__ __forceinline__ void store_conv(const Acc (&acc)[G::TM][G::TN], O *y,
   constexpr int NACC = AccType<MF>::n;
   const int plane = rows_t * p.OW;
   const int64_t chan = int64_t(p.OH) * p.OW;
+  int64_t off[G::TN][NACC];  // y offset of the pixel at channel 0, or -1 past the last pixel
+#pragma unroll
+  for (int j = 0; j < G::TN; ++j)
+#pragma unroll
+    for (int e4 = 0; e4 < NACC / 4; ++e4) {
+      int pix = n0 + wc * G::WTN + j * MF + acc_col4<MF>(e4, lane);
+      int n = pix / plane;
+      const int rem = pix - n * plane;
+      int oh = rem / p.OW;
+      int ow = rem - oh * p.OW;
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        off[j][e4 * 4 + d] = pix < npix ? (int64_t(n) * p.M * chan + int64_t(o0 + oh) * p.OW + ow) : int64_t(-1);
+        ++pix;
+        if (++ow == p.OW) {
+          ow = 0;
+          if (++oh == rows_t) {
+            oh = 0;
+            ++n;
+          }
+        }
+      }
+    }
 #pragma unroll
   for (int i = 0; i < G::TM; ++i) {
     const int co = m0 + wr * G::WTM + i * MF + lane % MF;
@@ -318,13 +347,8 @@ __device__ __forceinline__ void store_conv(const Acc (&acc)[G::TM][G::TN], O *y,
 #pragma unroll
     for (int j = 0; j < G::TN; ++j)
 #pragma unroll
-      for (int e = 0; e < NACC; ++e) {
-        const int pix = n0 + wc * G::WTN + j * MF + acc_col4<MF>(e / 4, lane) + e % 4;
-        if (pix >= npix) continue;
-        const int n = pix / plane, rem = pix - n * plane;
-        const int oh = o0 + rem / p.OW, ow = rem - (rem / p.OW) * p.OW;
-        y[(int64_t(n) * p.M + co) * chan + int64_t(oh) * p.OW + ow] = convert_out<O>(acc[i][j][e]);
-      }
+      for (int e = 0; e < NACC; ++e)
+        if (off[j][e] >= 0) y[off[j][e] + int64_t(co) * chan] = convert_out<O>(acc[i][j][e]);
   }
 }
 
@@ -377,15 +401,13 @@ __global__ __launch_bounds__(G::THREADS) void tiled_gemm_kernel(KernelArgs p) {
   const T *Ab = reinterpret_cast<const T *>(p.A) + (CONV ? 0 : int64_t(bz) * p.batch_stride_a) + int64_t(m0) * K;
   const uint32_t a_range = uint32_t(min(G::BM, M - m0)) * uint32_t(K) * 2u;  // rows [m0, M)
   const i32x4 rsA4 = buffer_rsrc(Ab, a_range);
-  i32x4 rsB4{};                 // GEMM: the B operand for the direct copy
-  __amdgpu_buffer_rsrc_t rsB;    // conv: the input, for the element gather
+  i32x4 rsB4;
   if constexpr (CONV) {
-    const uint32_t x_range = uint32_t(p.Nb) * uint32_t(p.Cin) * uint32_t(p.H) * uint32_t(p.W) * 2u;
-    rsB = __builtin_amdgcn_make_buffer_rsrc((void *)p.B, (short)0, (int)x_range, 0x00020000);
+    // the channel-last input xc[Nb][H][W][Cp]
+    rsB4 = buffer_rsrc(p.B, uint32_t(p.Nb) * uint32_t(p.H) * uint32_t(p.W) * uint32_t(p.Cp) * 2u);
   } else {
     const T *Bb = reinterpret_cast<const T *>(p.B) + int64_t(bz) * p.batch_stride_b + n0;
-    const uint32_t b_range = (uint32_t(K) * uint32_t(N) - uint32_t(n0)) * 2u;  // elements [n0, K*N)
-    rsB4 = buffer_rsrc(Bb, b_range);
+    rsB4 = buffer_rsrc(Bb, (uint32_t(K) * uint32_t(N) - uint32_t(n0)) * 2u);  // elements [n0, K*N)
   }
 
   // -- A copy plan: wave load j of a stage covers LDS chunks (j*NW+wave)*64 + lane
@@ -399,125 +421,117 @@ __global__ __launch_bounds__(G::THREADS) void tiled_gemm_kernel(KernelArgs p) {
     a_off[j] = uint32_t(r) * uint32_t(K) * 2u + uint32_t(lc) * 16u;
     a_kc[j] = lc * 8;
   }
-  // -- B copy plan (GEMM): the same for the K x N operand
-  uint32_t b_off[CONV ? 1 : G::B_LOADS];
-  int b_k[CONV ? 1 : G::B_LOADS];
-  if constexpr (!CONV) {
+  // -- B copy plan.
+  // GEMM: B is K x N, N-contiguous; chunk (k, lc) of the stage holds columns
+  // 8lc .. 8lc+7 of row k.
+  // conv: B is the im2col matrix, stored transposed (pixels x K, K-contiguous,
+  // laid out and swizzled like A); K runs over (r, s, ci) of the channel-last
+  // input, so a 16-byte chunk is 8 consecutive channels of one input pixel.
+  // Per lane: the byte offset of its pixel's window corner (channel 0), the
+  // corner's slice row and input column, and the chunk's first K element.
+  uint32_t b_off[G::B_LOADS];
+  int b_k[G::B_LOADS];
+  int b_row[CONV ? G::B_LOADS : 1], b_col[CONV ? G::B_LOADS : 1];
 #pragma unroll
-    for (int j = 0; j < G::B_LOADS; ++j) {
-      int pchunk = (j * G::NW + wave) * 64 + lane;
+  for (int j = 0; j < G::B_LOADS; ++j) {
+    const int pchunk = (j * G::NW + wave) * 64 + lane;
+    if constexpr (!CONV) {
       int k = pchunk / G::CB, pc = pchunk % G::CB;
       int lc = pc ^ G::swz_b(k);
       bool col_ok = n0 + lc * 8 < N;
       b_off[j] = col_ok ? uint32_t(k) * uint32_t(N) * 2u + uint32_t(lc) * 16u : kOOB;
       b_k[j] = col_ok ? k : (1 << 30);
-    }
-  }
-  // -- B gather plan (conv): the thread fills logical pixel chunk g_lc (8
-  // consecutive pixels) of B rows g_k0 + j*(THREADS/CB).  Per pixel it keeps
-  // the byte offset of the window's first tap and the tap's slice row and
-  // input column, so each gathered element costs two range checks and an add.
-  const int g_lc = threadIdx.x % G::CB;
-  const int g_k0 = threadIdx.x / G::CB;
-  int px_off[CONV ? 8 : 1], px_row[CONV ? 8 : 1], px_col[CONV ? 8 : 1];
-  if constexpr (CONV) {
-    const int plane = rows_t * p.OW;
-    const int row0 = in_start - pt_sub;  // input row of slice row 0 (= o0*sh - ph)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int pix = n0 + g_lc * 8 + e;
+    } else {
+      const int r = pchunk / G::CA, pc = pchunk % G::CA;
+      const int lc = pc ^ G::swz_a(r);
+      const int pix = n0 + r;
+      const int plane = rows_t * p.OW;
       const int n = pix / plane, rem = pix - n * plane;
       const int oh_l = rem / p.OW, ow = rem - oh_l * p.OW;
-      const int sr = oh_l * p.sh;        // slice row of the window's first tap
-      const int iw = ow * p.sw - p.pw;   // input column of the window's first tap
-      px_off[e] = ((n * p.Cin * p.H + row0 + sr) * p.W + iw) * 2;
-      px_row[e] = pix < N ? sr - pt_sub : (1 << 30);  // rows [pt', pt' + rows_in) hold data
-      px_col[e] = iw;
+      const int sr = oh_l * p.sh;                 // slice row of the window's top tap
+      const int iw = ow * p.sw - p.pw;            // input column of the window's left tap
+      const int ih = in_start - pt_sub + sr;      // its input row (= (o0 + oh_l)*sh - ph)
+      // may wrap below zero for a pad corner; used only where the chunk is valid
+      b_off[j] = uint32_t(((n * p.H + ih) * p.W + iw) * p.Cp + lc * 8) * 2u;
+      b_k[j] = lc * 8;
+      b_row[j] = pix < N ? sr - pt_sub : (1 << 30);  // slice rows [pt', pt' + rows_in) hold data
+      b_col[j] = iw;
     }
   }
-  // The gather of tile t is issued S-1 iterations before tile t is computed
-  // and written to LDS at the end of the iteration before; S-1 register sets
-  // keep those gathers in flight.
-  constexpr int NSET = CONV ? (S > 2 ? S - 1 : 1) : 1;
-  i16x8 g_reg[NSET][CONV ? G::B_LOADS : 1];
-  // vector-memory instructions one iteration issues per thread
-  constexpr int VPI = G::A_LOADS + (CONV ? 8 * G::B_LOADS : G::B_LOADS);
 
   const int nk = (K + G::BK - 1) / G::BK;
   const int nfull = K / G::BK;  // K tiles that lie inside K
 
-  // One K tile of the convolution: the weights (A) go HBM -> LDS directly,
-  // the im2col rows of the input (B) are gathered into register set SET.
-  auto issue = [&](int kt, int stage, auto set_c) __attribute__((always_inline)) {
-    constexpr int SET = decltype(set_c)::value;
-    const int k0 = kt * G::BK;
-    char *sa = smem + stage * G::STAGE_BYTES;
-    // Every K tile but a ragged last one lies inside K: its copies take the
-    // fixed per-lane offsets and advance by k0 through the scalar offset.
-    // The ragged tile masks the chunks at or past K per lane.
-    if (k0 + G::BK <= K) {
-#pragma unroll
-      for (int j = 0; j < G::A_LOADS; ++j)
-        copy_to_lds16(rsA4, a_off[j], uint32_t(k0) * 2u, (lds_void *)(sa + (j * G::NW + wave) * 1024));
-    } else {
-#pragma unroll
-      for (int j = 0; j < G::A_LOADS; ++j) {
-        uint32_t off = (k0 + a_kc[j] < K) ? a_off[j] + uint32_t(k0) * 2u : kOOB;
-        copy_to_lds16(rsA4, off, 0u, (lds_void *)(sa + (j * G::NW + wave) * 1024));
-      }
-    }
+  // conv: the refill cursor.  K tiles are copied in order 0, 1, 2, ...; Cp is
+  // a multiple of BK, so each tile is one tap (r, s) and channels ci0 ..
+  // ci0+BK-1 of it, and the cursor steps to the next tile with scalar adds
+  // once a tile's copies are issued.
+  int cur_ci = 0, cur_s = 0, cur_r = 0;
+  auto cursor_next = [&]() __attribute__((always_inline)) {
     if constexpr (CONV) {
-      const int khw = p.kh * p.kw;
-      const int HW = p.H * p.W;
-#pragma unroll
-      for (int j = 0; j < G::B_LOADS; ++j) {
-        const int k = k0 + g_k0 + j * (G::THREADS / G::CB);
-        const bool kok = k < K;
-        const int ci = kok ? k / khw : 0;
-        const int rs = k - ci * khw;
-        const int r = rs / p.kw, s = rs - r * p.kw;
-        const int dr = r * p.dh, ds = s * p.dw;
-        const int delta = (ci * HW + dr * p.W + ds) * 2;
-        const uint32_t rows_ok = kok ? uint32_t(rows_in) : 0u;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const bool ok = uint32_t(px_row[e] + dr) < rows_ok && uint32_t(px_col[e] + ds) < uint32_t(p.W);
-          const uint32_t off = ok ? uint32_t(px_off[e] + delta) : kOOB;
-          g_reg[SET][j][e] = (short)__builtin_amdgcn_raw_buffer_load_b16(rsB, off, 0, 0);
+      cur_ci += G::BK;
+      if (cur_ci == p.Cp) {
+        cur_ci = 0;
+        if (++cur_s == p.kw) {
+          cur_s = 0;
+          ++cur_r;
         }
       }
     }
   };
+  // conv, the K tile at the cursor (starting at k0): byte offset of the copy
+  // of B chunk j, or kOOB where the chunk lies in a pad, outside the H-tile's
+  // slice, past the last pixel or past K
+  auto conv_b_off = [&](int k0, int j) __attribute__((always_inline)) -> uint32_t {
+    const int dr = cur_r * p.dh, ds = cur_s * p.dw;
+    const bool ok = k0 + b_k[j] < K && uint32_t(b_row[j] + dr) < uint32_t(rows_in) &&
+                    uint32_t(b_col[j] + ds) < uint32_t(p.W);
+    return ok ? b_off[j] + uint32_t(((dr * p.W + ds) * p.Cp + cur_ci) * 2) : kOOB;
+  };
   // Copy j (0 .. LPW-1) of full K tile kt into `stage`: the A copies first,
-  // then the B copies (GEMM only).
+  // then the B copies.  A (and the GEMM's B) advance through the scalar
+  // offset: the per-lane offsets stay fixed over the K loop.
   auto issue_one = [&](int kt, int stage, int j) __attribute__((always_inline)) {
     const int k0 = kt * G::BK;
     char *sa = smem + stage * G::STAGE_BYTES;
     if (j < G::A_LOADS) {
       copy_to_lds16(rsA4, a_off[j], uint32_t(k0) * 2u, (lds_void *)(sa + (j * G::NW + wave) * 1024));
-    } else if constexpr (!CONV) {
+    } else {
       const int jb = j - G::A_LOADS;
-      copy_to_lds16(rsB4, b_off[jb], uint32_t(k0) * uint32_t(N) * 2u,
-                    (lds_void *)(sa + G::A_BYTES + (jb * G::NW + wave) * 1024));
+      lds_void *dst = (lds_void *)(sa + G::A_BYTES + (jb * G::NW + wave) * 1024);
+      if constexpr (CONV) copy_to_lds16(rsB4, conv_b_off(k0, jb), 0u, dst);
+      else copy_to_lds16(rsB4, b_off[jb], uint32_t(k0) * uint32_t(N) * 2u, dst);
     }
   };
-  // write the convolution's gathered B rows of a stage (after their loads
-  // returned) into the B layout of the GEMM
-  auto store_staged = [&](int stage, auto set_c) __attribute__((always_inline)) {
-    constexpr int SET = decltype(set_c)::value;
-    if constexpr (CONV) {
-      char *sb = smem + stage * G::STAGE_BYTES + G::A_BYTES;
-#pragma unroll
-      for (int j = 0; j < G::B_LOADS; ++j) {
-        const int kk = g_k0 + j * (G::THREADS / G::CB);
-        *(lds_i16x8 *)(sb + kk * G::BN * 2 + ((g_lc ^ G::swz_b(kk)) * 16)) = g_reg[SET][j];
+  // Copy j of any K tile ckt into stage cst: a full tile as above; the
+  // ragged last tile masks the chunks at or past K per lane; a tile past the
+  // end reads zeros only.
+  auto copy = [&](int ckt, int cst, int j) __attribute__((always_inline)) {
+    if (ckt < nfull) {
+      issue_one(ckt, cst, j);
+    } else {
+      const int k0 = ckt * G::BK;
+      char *sa = smem + cst * G::STAGE_BYTES;
+      if (j < G::A_LOADS) {
+        const uint32_t off = (k0 + a_kc[j] < K) ? a_off[j] + uint32_t(k0) * 2u : kOOB;
+        copy_to_lds16(rsA4, off, 0u, (lds_void *)(sa + (j * G::NW + wave) * 1024));
+      } else {
+        const int jb = j - G::A_LOADS;
+        lds_void *dst = (lds_void *)(sa + G::A_BYTES + (jb * G::NW + wave) * 1024);
+        if constexpr (CONV) {
+          copy_to_lds16(rsB4, conv_b_off(k0, jb), 0u, dst);
+        } else {
+          const uint32_t off = (k0 + b_k[jb] < K) ? b_off[jb] + uint32_t(k0) * uint32_t(N) * 2u : kOOB;
+          copy_to_lds16(rsB4, off, 0u, dst);
+        }
       }
     }
   };
 
   // -- per-lane fragment addresses (bytes within a stage)
   // A: lane reads row (lane % MF) of each MFMA tile, logical chunk
-  //    q*(FK/8) + lane/MF; the swizzle depends only on lane % MF.
+  //    q*(FK/8) + lane/MF; the swizzle depends only on lane % MF (rows 16
+  //    apart share it), so MFMA tile i adds i*MF rows as an immediate.
   uint32_t fa[G::KSUB];
   {
     const int r = lane % MF;
@@ -528,10 +542,21 @@ __global__ __launch_bounds__(G::THREADS) void tiled_gemm_kernel(KernelArgs p) {
       fa[q] = uint32_t((wr * G::WTM + r) * G::BK * 2 + ((lc ^ x) * 16));
     }
   }
-  // B (transpose read, 4 k-rows x 16 columns per 16-lane group): source lane
-  // s = lane % 16 points at row kbase + s/4, columns cbase + 4*(s%4) .. +3.
-  uint32_t fb[G::TN];
-  {
+  // B, GEMM (transpose read, 4 k-rows x 16 columns per 16-lane group): source
+  // lane s = lane % 16 points at row kbase + s/4, columns cbase + 4*(s%4) ..
+  // +3; one address per MFMA tile, K step q adds q*FK rows.
+  // B, conv (pixel rows, K-contiguous): read like A, one address per K step.
+  constexpr int NFB = CONV ? G::KSUB : G::TN;
+  uint32_t fb[NFB];
+  if constexpr (CONV) {
+    const int r = lane % MF;
+    const int x = G::swz_a(r);
+#pragma unroll
+    for (int q = 0; q < G::KSUB; ++q) {
+      int lc = q * (G::FK / 8) + lane / MF;
+      fb[q] = uint32_t(G::A_BYTES + (wc * G::WTN + r) * G::BK * 2 + ((lc ^ x) * 16));
+    }
+  } else {
     const int g = lane / 16, s = lane % 16;
     int krow, ncol;
     if (MF == 32) {
@@ -556,70 +581,15 @@ __global__ __launch_bounds__(G::THREADS) void tiled_gemm_kernel(KernelArgs p) {
 #pragma unroll
     for (int j = 0; j < G::TN; ++j) acc[i][j] = Acc{};
 
-  auto load_frags = [&](const char *st, int q, i16x8(&af)[G::TM], i16x8(&bf)[G::TN]) {
-#pragma unroll
-    for (int i = 0; i < G::TM; ++i) af[i] = *(const lds_i16x8 *)(st + fa[q] + i * MF * G::BK * 2);
-#pragma unroll
-    for (int j = 0; j < G::TN; ++j) {
-      const char *bp = st + fb[j] + q * G::FK * G::BN * 2;
-      i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(bp));
-      i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(bp + 4 * G::BN * 2));
-      bf[j] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-    }
-  };
-  auto mfmas = [&](const i16x8(&af)[G::TM], const i16x8(&bf)[G::TN]) {
-#pragma unroll
-    for (int i = 0; i < G::TM; ++i)
-#pragma unroll
-      for (int j = 0; j < G::TN; ++j) {
-        // B fragment as the MFMA's row operand: the accumulator then holds
-        // C^T, i.e. each lane owns 4 consecutive columns of one C row
-        if constexpr (MF == 32) acc[i][j] = Mfma<T>::m32(bf[j], af[i], acc[i][j]);
-        else acc[i][j] = Mfma<T>::m16(bf[j], af[i], acc[i][j]);
-      }
-  };
-  // Fragments of K step q+1 are read while the MFMAs of step q run.  The
-  // schedule is pinned: each LDS fragment read is issued right after an
-  // MFMA, spread evenly over the step, so the reads overlap the matrix
-  // pipeline instead of stalling it just before each MFMA.
-  auto compute = [&](int stage) __attribute__((always_inline)) {
-    const char *st = smem + stage * G::STAGE_BYTES;
-    i16x8 af0[G::TM], bf0[G::TN], af1[G::TM], bf1[G::TN];
-    load_frags(st, 0, af0, bf0);
-#pragma unroll
-    for (int q = 0; q < G::KSUB; q += 2) {
-      if (q + 1 < G::KSUB) load_frags(st, q + 1, af1, bf1);
-      mfmas(af0, bf0);
-      if (q + 2 < G::KSUB) load_frags(st, q + 2, af0, bf0);
-      if (q + 1 < G::KSUB) mfmas(af1, bf1);
-    }
-    constexpr int NMF = G::TM * G::TN, NDS = G::TM + 2 * G::TN;
-    __builtin_amdgcn_sched_group_barrier(0x100, NDS, 0);  // first step's fragments
-#pragma unroll
-    for (int q = 0; q + 1 < G::KSUB; ++q) {
-#pragma unroll
-      for (int i = 0; i < NMF; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-        const int nds = (i + 1) * NDS / NMF - i * NDS / NMF;
-#pragma unroll
-        for (int d = 0; d < nds; ++d) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
-      }
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, NMF, 0);  // last step
-  };
-
-  using I0 = std::integral_constant<int, 0>;
-  using I1 = std::integral_constant<int, (NSET > 1 ? 1 : 0)>;
-  using I2 = std::integral_constant<int, (NSET > 2 ? 2 : 0)>;
-  int kt = 0, cs = 0, ls = S - 1;
+  int kt = 0, cs = 0;
 
   // The copies read buffer descriptors that may have just been written by a
   // vector instruction (v_readfirstlane); five wait states cover that hazard
   // once, before the first copy.
   asm volatile("s_nop 4" ::: "memory");
-  if constexpr (!CONV) {
-    // GEMM.  Three changes to the plain ring further below, all against
-    // stalls of the matrix pipe:
+  {
+    // The K loop.  Three changes to a plain ring (barrier, burst of copies,
+    // fragment reads, MFMAs), all against stalls of the matrix pipe:
     //  * fragment reads cross the barrier: the last MFMA step of tile kt runs
     //    on fragments already in registers while the first step's fragments
     //    of tile kt+1 are read, and the barrier sits inside that last step,
@@ -640,30 +610,16 @@ __global__ __launch_bounds__(G::THREADS) void tiled_gemm_kernel(KernelArgs p) {
       fa_[i] = *(const lds_i16x8 *)(st + fa[q] + i * MF * G::BK * 2);
     };
     auto read_b = [&](const char *st, int q, int pb, int j) __attribute__((always_inline)) {
-      const char *bp = st + fb[j] + q * G::FK * G::BN * 2;
-      i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(bp));
-      i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(bp + 4 * G::BN * 2));
-      fb_[pb][j] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-    };
-    // Copy j of K tile ckt into stage cst: a full tile advances through the
-    // scalar offset; the ragged last tile masks the chunks at or past K per
-    // lane; a tile past the end reads zeros only.
-    auto copy = [&](int ckt, int cst, int j) __attribute__((always_inline)) {
-      if (ckt < nfull) {
-        issue_one(ckt, cst, j);
+      if constexpr (CONV) {
+        fb_[pb][j] = *(const lds_i16x8 *)(st + fb[q] + j * MF * G::BK * 2);
       } else {
-        const int k0 = ckt * G::BK;
-        char *sa = smem + cst * G::STAGE_BYTES;
-        if (j < G::A_LOADS) {
-          const uint32_t off = (k0 + a_kc[j] < K) ? a_off[j] + uint32_t(k0) * 2u : kOOB;
-          copy_to_lds16(rsA4, off, 0u, (lds_void *)(sa + (j * G::NW + wave) * 1024));
-        } else {
-          const int jb = j - G::A_LOADS;
-          const uint32_t off = (k0 + b_k[jb] < K) ? b_off[jb] + uint32_t(k0) * uint32_t(N) * 2u : kOOB;
-          copy_to_lds16(rsB4, off, 0u, (lds_void *)(sa + G::A_BYTES + (jb * G::NW + wave) * 1024));
-        }
+        const char *bp = st + fb[j] + q * G::FK * G::BN * 2;
+        i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(bp));
+        i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(bp + 4 * G::BN * 2));
+        fb_[pb][j] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
       }
     };
+    constexpr int BREADS = CONV ? 1 : 2;  // LDS reads per B fragment
     // One MFMA step on (fa_, fb_[PB]).  NEXT: the fragments of step nq of the
     // stage at nst are read into (fa_, fb_[1-PB]) meanwhile, each A fragment
     // right after its last MFMA row, the B fragments spread over the rows.
@@ -704,7 +660,7 @@ __global__ __launch_bounds__(G::THREADS) void tiled_gemm_kernel(KernelArgs p) {
 #pragma unroll
             for (int a = a0; a < a1; ++a) read_a(nst, nq, a);
             __builtin_amdgcn_sched_group_barrier(0x008, G::TN, 0);                        // the row's MFMAs
-            __builtin_amdgcn_sched_group_barrier(0x100, 2 * (b1 - b0) + (a1 - a0), 0);   // then its LDS reads
+            __builtin_amdgcn_sched_group_barrier(0x100, BREADS * (b1 - b0) + (a1 - a0), 0);  // then its LDS reads
           }
           if constexpr (COPY) {
             __builtin_amdgcn_sched_barrier(0);
@@ -741,6 +697,7 @@ __global__ __launch_bounds__(G::THREADS) void tiled_gemm_kernel(KernelArgs p) {
       if constexpr (MODE != 0) {
         const int ns = cs + 1 == S ? 0 : cs + 1;
         step(PLast{}, Tr{}, mode_c, BarRow{}, smem + ns * G::STAGE_BYTES, 0, kt + S, cs);
+        cursor_next();
         if constexpr (PLast::value == 0) {
           // odd number of steps: the next tile's first B fragments were read
           // into buffer 1; move them so that every tile starts on buffer 0
@@ -756,9 +713,11 @@ __global__ __launch_bounds__(G::THREADS) void tiled_gemm_kernel(KernelArgs p) {
 
     // prologue: tiles 0 .. S-1 in flight, tile 0's first fragments read
 #pragma unroll
-    for (int s = 0; s < S; ++s)
+    for (int s = 0; s < S; ++s) {
 #pragma unroll
       for (int j = 0; j < G::LPW; ++j) copy(s, s, j);
+      cursor_next();
+    }
     wait_vmcnt_lgkm0<(S - 1) * G::LPW>();
     block_barrier();
     if (nk > 0) {
@@ -774,70 +733,6 @@ __global__ __launch_bounds__(G::THREADS) void tiled_gemm_kernel(KernelArgs p) {
     if (kt < nk) tile(C0{});
     // the refills past the end are still landing in LDS, which the epilogue reuses
     wait_vmcnt_lgkm0<0>();
-  } else if constexpr (NSET == 1) {
-    // -- prologue: stages 0 .. S-2 in flight
-#pragma unroll
-    for (int s = 0; s < S - 1; ++s)
-      if (s < nk) {
-        issue(s, s, I0{});
-        store_staged(s, I0{});
-      }
-    // steady state: tile kt has landed once only the S-2 younger tiles'
-    // loads are outstanding; the barrier publishes every wave's copy and
-    // frees stage ls (computed in the previous iteration) for tile kt+S-1.
-    for (; kt + S - 1 < nk; ++kt) {
-      wait_vmcnt_lgkm0<(S - 2) * G::LPW>();
-      block_barrier();
-      issue(kt + S - 1, ls, I0{});
-      compute(cs);
-      store_staged(ls, I0{});
-      cs = cs + 1 == S ? 0 : cs + 1;
-      ls = ls + 1 == S ? 0 : ls + 1;
-    }
-    // drain: nothing more to load; nk-1-kt younger tiles remain outstanding
-    for (; kt < nk; ++kt) {
-      const int pend = nk - 1 - kt;
-      if (S >= 4 && pend >= 2) wait_vmcnt_lgkm0<(S >= 4 ? 2 : 0) * G::LPW>();
-      else if (S >= 3 && pend >= 1) wait_vmcnt_lgkm0<(S >= 3 ? 1 : 0) * G::LPW>();
-      else wait_vmcnt_lgkm0<0>();
-      block_barrier();
-      compute(cs);
-      cs = cs + 1 == S ? 0 : cs + 1;
-    }
-  } else {
-    // Convolution with 3 or 4 stages: A goes HBM -> LDS directly, the
-    // gathered B of tile t is issued S-1 iterations ahead into register set
-    // t % NSET and written to its stage at the end of iteration t-1.
-    constexpr int W1 = VPI < 63 ? VPI : 63;
-    constexpr int W2 = 2 * VPI < 63 ? 2 * VPI : 63;
-    if (0 < nk) issue(0, 0, I0{});
-    if (1 < nk) issue(1, 1, I1{});
-    if (S > 3 && 2 < nk) issue(2, 2 % S, I2{});
-    if (0 < nk) store_staged(0, I0{});
-    // one iteration; unrolled NSET times so every register set index is
-    // static (iteration kt issues into set kt % NSET, stores set (kt+1) % NSET)
-    auto step = [&](auto set_c) __attribute__((always_inline)) {
-      constexpr int J = decltype(set_c)::value;
-      if (kt >= nk) return;
-      // tile kt's direct copy is complete once only the younger tiles'
-      // instructions (at most S-2 iterations' worth) are outstanding
-      const int pend = nk - 1 - kt < S - 2 ? nk - 1 - kt : S - 2;
-      if (pend >= 2) wait_vmcnt_lgkm0<W2>();
-      else if (pend == 1) wait_vmcnt_lgkm0<W1>();
-      else wait_vmcnt_lgkm0<0>();
-      block_barrier();
-      if (kt + S - 1 < nk) issue(kt + S - 1, ls, std::integral_constant<int, J>{});
-      compute(cs);
-      if (kt + 1 < nk) store_staged(cs + 1 == S ? 0 : cs + 1, std::integral_constant<int, (J + 1) % NSET>{});
-      cs = cs + 1 == S ? 0 : cs + 1;
-      ls = ls + 1 == S ? 0 : ls + 1;
-      ++kt;
-    };
-    while (kt < nk) {
-      step(I0{});
-      step(I1{});
-      if constexpr (NSET > 2) step(I2{});
-    }
   }
 
   // -- epilogue

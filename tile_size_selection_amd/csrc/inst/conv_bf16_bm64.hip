@@ -4,4 +4,5 @@
 #define TSS_OP 1
 #define TSS_BM 64
 #define TSS_TABLE table_conv_bf16_bm64
+#define TSS_WIDE 0
 #include "../instances.inc"

@@ -4,4 +4,5 @@
 #define TSS_OP 1
 #define TSS_BM 128
 #define TSS_TABLE table_conv_f16_bm128
+#define TSS_WIDE 0
 #include "../instances.inc"

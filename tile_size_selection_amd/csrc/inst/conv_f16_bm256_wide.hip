@@ -1,0 +1,8 @@
+// Kernels with 256 accumulators per lane for conv with f16 inputs and block rows BM = 256.
+#define TSS_T _Float16
+#define TSS_DT TSS_F16
+#define TSS_OP 1
+#define TSS_BM 256
+#define TSS_TABLE table_conv_f16_bm256_wide
+#define TSS_WIDE 1
+#include "../instances.inc"

@@ -4,4 +4,5 @@
 #define TSS_OP 0
 #define TSS_BM 256
 #define TSS_TABLE table_gemm_f16_bm256
+#define TSS_WIDE 0
 #include "../instances.inc"

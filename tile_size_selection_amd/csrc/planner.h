@@ -271,12 +271,15 @@ constexpr Key rank_key(const tss_verdict &v, const tss_device &d) {
     // times the tiles a CU streams once the grid is dealt out in waves (every
     // candidate's intensity is below the device ridge, ~315 FLOP/B); then
     // total C0, larger BK, most resident blocks, most resident waves, deeper
-    // pipeline, less LDS
+    // pipeline, less LDS.  Residency counts only the blocks the grid can
+    // supply: with ceil(grid / CUs) waves of tiles no CU ever holds more
+    // than that many blocks at once, whatever its capacity.
+    const int64_t usable = v.blocks_per_core < cdiv(v.grid, d.cores) ? v.blocks_per_core : cdiv(v.grid, d.cores);
     r.k[0] = cdiv(v.grid, d.cores) * (v.cfg.bm + v.cfg.bn);
     r.k[1] = t;
     r.k[2] = -v.cfg.bk;
-    r.k[3] = -v.blocks_per_core;
-    r.k[4] = -v.blocks_per_core * (v.cfg.threads / d.lane_count);
+    r.k[3] = -usable;
+    r.k[4] = -usable * (v.cfg.threads / d.lane_count);
     r.k[5] = -v.cfg.stages;
     r.k[6] = v.smem_total;
   }

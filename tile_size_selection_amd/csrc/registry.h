@@ -37,6 +37,14 @@ KernelTable table_conv_f16_bm256();
 KernelTable table_conv_bf16_bm64();
 KernelTable table_conv_bf16_bm128();
 KernelTable table_conv_bf16_bm256();
+KernelTable table_gemm_f16_bm128_wide();
+KernelTable table_gemm_f16_bm256_wide();
+KernelTable table_gemm_bf16_bm128_wide();
+KernelTable table_gemm_bf16_bm256_wide();
+KernelTable table_conv_f16_bm128_wide();
+KernelTable table_conv_f16_bm256_wide();
+KernelTable table_conv_bf16_bm128_wide();
+KernelTable table_conv_bf16_bm256_wide();
 
 template <typename G, typename T, bool CONV>
 hipError_t launch_kernel(const KernelArgs &a, dim3 grid, int lds_bytes, hipStream_t s) {
