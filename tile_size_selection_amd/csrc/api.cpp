@@ -187,7 +187,7 @@ int32_t tss_gemm(int64_t M, int64_t N, int64_t K, int32_t dtype, const void *A, 
   a.batch_stride_c = M * N;
   const int64_t blocks = batch * a.tiles_m * a.tiles_n;
   if (blocks * c.threads > int64_t(UINT32_MAX)) return TSS_E_ARG;
-  hipError_t err = e->launch(a, dim3(uint32_t(blocks)), e->stage_bytes * c.stages, (hipStream_t)stream);
+  hipError_t err = e->launch(a, dim3(uint32_t(blocks)), e->lds_bytes, (hipStream_t)stream);
   return err == hipSuccess ? TSS_OK : TSS_E_HIP;
 }
 
@@ -300,7 +300,7 @@ int32_t tss_conv2d(int64_t N, int64_t C, int64_t H, int64_t W, int64_t Cout, int
   const int64_t n_htiles = (OH + tile_oh - 1) / tile_oh;
   const int64_t blocks = n_htiles * a.tiles_m * a.tiles_n;
   if (blocks * c.threads > int64_t(UINT32_MAX)) return TSS_E_ARG;
-  err = e->launch(a, dim3(uint32_t(blocks)), e->stage_bytes * c.stages, (hipStream_t)stream);
+  err = e->launch(a, dim3(uint32_t(blocks)), e->lds_bytes, (hipStream_t)stream);
   return err == hipSuccess ? TSS_OK : TSS_E_HIP;
 }
 

@@ -195,6 +195,13 @@ struct Geometry {
   static_assert(CA >= 2 && CA <= 16 && CB >= 8, "swizzle assumes 2..16 chunks per A row, >= 8 per B row");
   static_assert(ST >= 2 && ST <= 4, "2..4 pipeline stages");
   static_assert((ST - 2) * LPW < 64, "outstanding loads must fit the 6-bit vmcnt");
+  // GEMM with a 2-stage ring: a third A buffer, when the LDS holds it without
+  // costing a resident block, lets the A refill start a K step earlier (A3).
+  static constexpr int LDS_PER_CU = 163840;
+  static constexpr int occ(int bytes) { return LDS_PER_CU / bytes < 2048 / THREADS ? LDS_PER_CU / bytes : 2048 / THREADS; }
+  static constexpr bool A3 = ST == 2 && KSUB >= 2 && 3 * A_BYTES + 2 * B_BYTES <= LDS_PER_CU &&
+                             occ(3 * A_BYTES + 2 * B_BYTES) == occ(2 * STAGE_BYTES);
+  static constexpr int lds_bytes(bool conv) { return (!conv && A3) ? 3 * A_BYTES + 2 * B_BYTES : ST * STAGE_BYTES; }
 
   // A rows (K-contiguous, BK*2 bytes): chunk c of row r lives at chunk
   // c ^ swz_a(r).  16 consecutive rows read at one logical chunk land in 16
@@ -488,36 +495,42 @@ __global__ __launch_bounds__(G::THREADS) void tiled_gemm_kernel(KernelArgs p) {
                     uint32_t(b_col[j] + ds) < uint32_t(p.W);
     return ok ? b_off[j] + uint32_t(((dr * p.W + ds) * p.Cp + cur_ci) * 2) : kOOB;
   };
-  // Copy j (0 .. LPW-1) of full K tile kt into `stage`: the A copies first,
-  // then the B copies.  A (and the GEMM's B) advance through the scalar
-  // offset: the per-lane offsets stay fixed over the K loop.
-  auto issue_one = [&](int kt, int stage, int j) __attribute__((always_inline)) {
+  // LDS slots.  The plain ring: stage s holds A at s*STAGE_BYTES and B right
+  // after it.  The A3 ring (GEMM, 2 stages): three A slots, then two B slots.
+  constexpr bool A3 = !CONV && G::A3;
+  auto a_slot = [&](int s) __attribute__((always_inline)) -> char * {
+    return smem + (A3 ? s * G::A_BYTES : s * G::STAGE_BYTES);
+  };
+  auto b_slot = [&](int s) __attribute__((always_inline)) -> char * {
+    return smem + (A3 ? 3 * G::A_BYTES + s * G::B_BYTES : s * G::STAGE_BYTES + G::A_BYTES);
+  };
+  // Copy j (0 .. LPW-1) of full K tile kt, A copies (j < A_LOADS) into A slot
+  // sa, B copies into B slot sb.  A (and the GEMM's B) advance through the
+  // scalar offset: the per-lane offsets stay fixed over the K loop.
+  auto issue_one = [&](int kt, int sa, int sb, int j) __attribute__((always_inline)) {
     const int k0 = kt * G::BK;
-    char *sa = smem + stage * G::STAGE_BYTES;
     if (j < G::A_LOADS) {
-      copy_to_lds16(rsA4, a_off[j], uint32_t(k0) * 2u, (lds_void *)(sa + (j * G::NW + wave) * 1024));
+      copy_to_lds16(rsA4, a_off[j], uint32_t(k0) * 2u, (lds_void *)(a_slot(sa) + (j * G::NW + wave) * 1024));
     } else {
       const int jb = j - G::A_LOADS;
-      lds_void *dst = (lds_void *)(sa + G::A_BYTES + (jb * G::NW + wave) * 1024);
+      lds_void *dst = (lds_void *)(b_slot(sb) + (jb * G::NW + wave) * 1024);
       if constexpr (CONV) copy_to_lds16(rsB4, conv_b_off(k0, jb), 0u, dst);
       else copy_to_lds16(rsB4, b_off[jb], uint32_t(k0) * uint32_t(N) * 2u, dst);
     }
   };
-  // Copy j of any K tile ckt into stage cst: a full tile as above; the
-  // ragged last tile masks the chunks at or past K per lane; a tile past the
-  // end reads zeros only.
-  auto copy = [&](int ckt, int cst, int j) __attribute__((always_inline)) {
+  // Copy j of any K tile ckt: a full tile as above; the ragged last tile
+  // masks the chunks at or past K per lane; a tile past the end reads zeros.
+  auto copy = [&](int ckt, int sa, int sb, int j) __attribute__((always_inline)) {
     if (ckt < nfull) {
-      issue_one(ckt, cst, j);
+      issue_one(ckt, sa, sb, j);
     } else {
       const int k0 = ckt * G::BK;
-      char *sa = smem + cst * G::STAGE_BYTES;
       if (j < G::A_LOADS) {
         const uint32_t off = (k0 + a_kc[j] < K) ? a_off[j] + uint32_t(k0) * 2u : kOOB;
-        copy_to_lds16(rsA4, off, 0u, (lds_void *)(sa + (j * G::NW + wave) * 1024));
+        copy_to_lds16(rsA4, off, 0u, (lds_void *)(a_slot(sa) + (j * G::NW + wave) * 1024));
       } else {
         const int jb = j - G::A_LOADS;
-        lds_void *dst = (lds_void *)(sa + G::A_BYTES + (jb * G::NW + wave) * 1024);
+        lds_void *dst = (lds_void *)(b_slot(sb) + (jb * G::NW + wave) * 1024);
         if constexpr (CONV) {
           copy_to_lds16(rsB4, conv_b_off(k0, jb), 0u, dst);
         } else {
@@ -528,7 +541,7 @@ __global__ __launch_bounds__(G::THREADS) void tiled_gemm_kernel(KernelArgs p) {
     }
   };
 
-  // -- per-lane fragment addresses (bytes within a stage)
+  // -- per-lane fragment addresses (bytes within an A or B slot)
   // A: lane reads row (lane % MF) of each MFMA tile, logical chunk
   //    q*(FK/8) + lane/MF; the swizzle depends only on lane % MF (rows 16
   //    apart share it), so MFMA tile i adds i*MF rows as an immediate.
@@ -554,7 +567,7 @@ __global__ __launch_bounds__(G::THREADS) void tiled_gemm_kernel(KernelArgs p) {
 #pragma unroll
     for (int q = 0; q < G::KSUB; ++q) {
       int lc = q * (G::FK / 8) + lane / MF;
-      fb[q] = uint32_t(G::A_BYTES + (wc * G::WTN + r) * G::BK * 2 + ((lc ^ x) * 16));
+      fb[q] = uint32_t((wc * G::WTN + r) * G::BK * 2 + ((lc ^ x) * 16));
     }
   } else {
     const int g = lane / 16, s = lane % 16;
@@ -571,7 +584,7 @@ __global__ __launch_bounds__(G::THREADS) void tiled_gemm_kernel(KernelArgs p) {
     for (int nt = 0; nt < G::TN; ++nt) {
       int n = wc * G::WTN + nt * MF + ncol;
       int lc = n / 8;
-      fb[nt] = uint32_t(G::A_BYTES + krow * G::BN * 2 + ((lc ^ x) * 16) + (n % 8) * 2);
+      fb[nt] = uint32_t(krow * G::BN * 2 + ((lc ^ x) * 16) + (n % 8) * 2);
     }
   }
 
@@ -581,59 +594,73 @@ __global__ __launch_bounds__(G::THREADS) void tiled_gemm_kernel(KernelArgs p) {
 #pragma unroll
     for (int j = 0; j < G::TN; ++j) acc[i][j] = Acc{};
 
-  int kt = 0, cs = 0;
+  int kt = 0;
+  int ca = 0, cb = 0;  // A and B slots of the tile being computed
 
   // The copies read buffer descriptors that may have just been written by a
   // vector instruction (v_readfirstlane); five wait states cover that hazard
   // once, before the first copy.
   asm volatile("s_nop 4" ::: "memory");
   {
-    // The K loop.  Three changes to a plain ring (barrier, burst of copies,
-    // fragment reads, MFMAs), all against stalls of the matrix pipe:
+    // The K loop.  Changes to a plain ring (barrier, burst of copies, fragment
+    // reads, MFMAs), all against stalls of the matrix pipe:
     //  * fragment reads cross the barrier: the last MFMA step of tile kt runs
     //    on fragments already in registers while the first step's fragments
     //    of tile kt+1 are read, and the barrier sits inside that last step,
     //    after its first MFMA rows, so the pipe has work while the waves meet;
-    //  * the copies of the tile refilling the freed stage are spread over the
-    //    MFMA rows of that last step (a copy occupies the CU's load path for
-    //    about as long as four MFMAs; issued as a burst, they block the
-    //    in-order issue of every wave in front of its MFMAs);
-    //  * every tile refills a stage: refills past the last K tile copy zeros
-    //    into a stage nobody reads again, so the waits are the same for every
-    //    tile and one loop body serves the whole K loop.
+    //  * the refill copies are spread over MFMA rows (a copy occupies the
+    //    CU's load path for about as long as four MFMAs; issued as a burst,
+    //    they block the in-order issue of every wave in front of its MFMAs).
+    //    The plain ring refills the stage freed at the barrier during the
+    //    last step.  The A3 ring (a 2-stage GEMM ring with a third A buffer)
+    //    refills A during the first step, into the A slot freed a tile
+    //    earlier, and B during the last step, so the copies of a tile are
+    //    spread over all of it;
+    //  * every tile refills: refills past the last K tile copy zeros into
+    //    slots nobody reads again, so the waits are the same for every tile
+    //    and one loop body serves the whole K loop.
     // A fragments are single-buffered (slot i is refilled right after the
     // last MFMA that reads it); B fragments are double-buffered, every MFMA
     // row of a step reads all of them.  The steps alternate B buffers and
     // every tile starts on buffer 0.
     i16x8 fa_[G::TM], fb_[2][G::TN];
-    auto read_a = [&](const char *st, int q, int i) __attribute__((always_inline)) {
-      fa_[i] = *(const lds_i16x8 *)(st + fa[q] + i * MF * G::BK * 2);
+    auto read_a = [&](const char *sta, int q, int i) __attribute__((always_inline)) {
+      fa_[i] = *(const lds_i16x8 *)(sta + fa[q] + i * MF * G::BK * 2);
     };
-    auto read_b = [&](const char *st, int q, int pb, int j) __attribute__((always_inline)) {
+    auto read_b = [&](const char *stb, int q, int pb, int j) __attribute__((always_inline)) {
       if constexpr (CONV) {
-        fb_[pb][j] = *(const lds_i16x8 *)(st + fb[q] + j * MF * G::BK * 2);
+        fb_[pb][j] = *(const lds_i16x8 *)(stb + fb[q] + j * MF * G::BK * 2);
       } else {
-        const char *bp = st + fb[j] + q * G::FK * G::BN * 2;
+        const char *bp = stb + fb[j] + q * G::FK * G::BN * 2;
         i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(bp));
         i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(bp + 4 * G::BN * 2));
         fb_[pb][j] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
       }
     };
     constexpr int BREADS = CONV ? 1 : 2;  // LDS reads per B fragment
+    // outstanding copies at the barrier once the next tile has landed: the
+    // plain ring's S-2 younger tiles; the A3 ring's A refill of this tile
+    constexpr int WAIT_VM = A3 ? G::A_LOADS : (S - 2) * G::LPW;
+    // copy selections: which copies of a tile a step issues, and whether the
+    // tile is a full K tile (copied without a per-copy test)
+    enum { kNone = 0, kAll = 1, kA = 2, kB = 3 };
     // One MFMA step on (fa_, fb_[PB]).  NEXT: the fragments of step nq of the
-    // stage at nst are read into (fa_, fb_[1-PB]) meanwhile, each A fragment
-    // right after its last MFMA row, the B fragments spread over the rows.
-    // COPY: the copies of K tile ckt into stage cst are spread over the
-    // rows (mode 2: ckt is a full K tile, copied without a per-copy test).  BAR >= 0: the step starts with BAR MFMA rows, then the wait and
-    // barrier that make stage nst readable and free stage cst; the reads and
-    // copies fill the rows from there on, while the MFMAs already issued keep
-    // the matrix pipe busy through the barrier.
-    auto step = [&](auto pb_c, auto next_c, auto copy_c, auto bar_c, const char *nst, int nq, int ckt, int cst)
-                    __attribute__((always_inline)) {
+    // slots at (nsa, nsb) are read into (fa_, fb_[1-PB]) meanwhile, each A
+    // fragment right after its last MFMA row, the B fragments spread over the
+    // rows.  CP = 2*part + full: the selected copies of K tile ckt into A slot
+    // csa / B slot csb are spread over the rows.  BAR >= 0: the step starts
+    // with BAR MFMA rows, then the wait and barrier that make the next tile
+    // readable and free the slots computed; the reads and copies fill the
+    // rows from there on, while the MFMAs already issued keep the matrix
+    // pipe busy through the barrier.
+    auto step = [&](auto pb_c, auto next_c, auto cp_c, auto bar_c, const char *nsa, const char *nsb, int nq, int ckt,
+                    int csa, int csb) __attribute__((always_inline)) {
       constexpr int PB = decltype(pb_c)::value;
       constexpr bool NEXT = decltype(next_c)::value;
-      constexpr int COPY_MODE = decltype(copy_c)::value;  // 0 none, 1 any tile, 2 a full K tile
-      constexpr bool COPY = COPY_MODE != 0, COPY_FULL = COPY_MODE == 2;
+      constexpr int PART = decltype(cp_c)::value / 2;
+      constexpr bool FULL = decltype(cp_c)::value % 2 == 1;
+      constexpr int NC = PART == kAll ? G::LPW : PART == kA ? G::A_LOADS : PART == kB ? G::B_LOADS : 0;
+      constexpr int J0 = PART == kB ? G::A_LOADS : 0;
       constexpr int BAR = decltype(bar_c)::value;
       constexpr int R0 = BAR > 0 ? BAR : 0;     // first row that may read or copy
       constexpr int NR = G::TM - R0;            // rows that read and copy
@@ -641,8 +668,8 @@ __global__ __launch_bounds__(G::THREADS) void tiled_gemm_kernel(KernelArgs p) {
         constexpr int i = decltype(i_c)::value;
         if constexpr (i == BAR) {
           __builtin_amdgcn_sched_barrier(0);
-          wait_vmcnt_lgkm0<(S - 2) * G::LPW>();  // the next tile has landed (this wave's copies)
-          block_barrier();                       // ... every wave's; the computed stage is free
+          wait_vmcnt_lgkm0<WAIT_VM>();  // the next tile has landed (this wave's copies)
+          block_barrier();              // ... every wave's; the slots computed are free
           __builtin_amdgcn_sched_barrier(0);
         }
 #pragma unroll
@@ -656,18 +683,18 @@ __global__ __launch_bounds__(G::THREADS) void tiled_gemm_kernel(KernelArgs p) {
           constexpr int b0 = r * G::TN / NR, b1 = (r + 1) * G::TN / NR;     // B fragments read here
           if constexpr (NEXT) {
 #pragma unroll
-            for (int j = b0; j < b1; ++j) read_b(nst, nq, 1 - PB, j);
+            for (int j = b0; j < b1; ++j) read_b(nsb, nq, 1 - PB, j);
 #pragma unroll
-            for (int a = a0; a < a1; ++a) read_a(nst, nq, a);
+            for (int a = a0; a < a1; ++a) read_a(nsa, nq, a);
             __builtin_amdgcn_sched_group_barrier(0x008, G::TN, 0);                        // the row's MFMAs
             __builtin_amdgcn_sched_group_barrier(0x100, BREADS * (b1 - b0) + (a1 - a0), 0);  // then its LDS reads
           }
-          if constexpr (COPY) {
+          if constexpr (NC > 0) {
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int c = r * G::LPW / NR; c < (r + 1) * G::LPW / NR; ++c) {
-              if constexpr (COPY_FULL) issue_one(ckt, cst, c);
-              else copy(ckt, cst, c);
+            for (int c = r * NC / NR; c < (r + 1) * NC / NR; ++c) {
+              if constexpr (FULL) issue_one(ckt, csa, csb, J0 + c);
+              else copy(ckt, csa, csb, J0 + c);
             }
             __builtin_amdgcn_sched_barrier(0);
           }
@@ -683,20 +710,30 @@ __global__ __launch_bounds__(G::THREADS) void tiled_gemm_kernel(KernelArgs p) {
     using Tr = std::true_type;
     using NoBar = std::integral_constant<int, -1>;
     using BarRow = std::integral_constant<int, (kBarrierRows < G::TM ? kBarrierRows : G::TM - 1)>;
-    using C0 = std::integral_constant<int, 0>;
-    // One tile.  MODE 2: refill with a full K tile; 1: refill with any tile;
-    // 0: the last tile, no refill and no read-ahead.
+    using NoCopy = std::integral_constant<int, 0>;
+    // One tile.  MODE 2: its refill is a full K tile; 1: any tile (ragged or
+    // past the end); 0: the last tile, no refill and no read-ahead.
     auto tile = [&](auto mode_c) __attribute__((always_inline)) {
       constexpr int MODE = decltype(mode_c)::value;
-      const char *st = smem + cs * G::STAGE_BYTES;
-      // steps 0 .. KSUB-2, each reading the next step's fragments from this stage
+      constexpr int FULL = MODE == 2 ? 1 : 0;
+      const char *sta = a_slot(ca), *stb = b_slot(cb);
+      // the A3 ring's A refill (tile kt+2, into the A slot computed a tile ago)
+      // rides the first step; the plain ring refills everything in the last
+      const int ra = ca == 0 ? 2 : ca - 1;
+      using FirstCopy = std::integral_constant<int, (A3 && MODE != 0) ? 2 * kA + FULL : 0>;
+      // steps 0 .. KSUB-2, each reading the next step's fragments from this tile's slots
       [&]<int... Q>(std::integer_sequence<int, Q...>) __attribute__((always_inline)) {
-        (step(std::integral_constant<int, Q & 1>{}, Tr{}, C0{}, NoBar{}, st, Q + 1, 0, 0), ...);
+        (step(std::integral_constant<int, Q & 1>{}, Tr{},
+              std::integral_constant<int, Q == 0 ? FirstCopy::value : 0>{}, NoBar{}, sta, stb, Q + 1, kt + 2, ra,
+              0),
+         ...);
       }(std::make_integer_sequence<int, G::KSUB - 1>{});
       using PLast = std::integral_constant<int, (G::KSUB - 1) & 1>;
       if constexpr (MODE != 0) {
-        const int ns = cs + 1 == S ? 0 : cs + 1;
-        step(PLast{}, Tr{}, mode_c, BarRow{}, smem + ns * G::STAGE_BYTES, 0, kt + S, cs);
+        const int na = A3 ? (ca == 2 ? 0 : ca + 1) : (ca + 1 == S ? 0 : ca + 1);
+        const int nb = A3 ? 1 - cb : na;
+        using LastCopy = std::integral_constant<int, 2 * (A3 ? kB : kAll) + FULL>;
+        step(PLast{}, Tr{}, LastCopy{}, BarRow{}, a_slot(na), b_slot(nb), 0, A3 ? kt + 2 : kt + S, ca, cb);
         cursor_next();
         if constexpr (PLast::value == 0) {
           // odd number of steps: the next tile's first B fragments were read
@@ -704,33 +741,36 @@ __global__ __launch_bounds__(G::THREADS) void tiled_gemm_kernel(KernelArgs p) {
 #pragma unroll
           for (int j = 0; j < G::TN; ++j) fb_[0][j] = fb_[1][j];
         }
-        cs = ns;
+        ca = na;
+        cb = nb;
         ++kt;
       } else {
-        step(PLast{}, F{}, C0{}, NoBar{}, st, 0, 0, 0);
+        step(PLast{}, F{}, NoCopy{}, NoBar{}, sta, stb, 0, 0, 0, 0);
       }
     };
 
-    // prologue: tiles 0 .. S-1 in flight, tile 0's first fragments read
+    // prologue: tiles 0 .. S-1 in flight (the A3 ring: tiles 0 and 1), tile
+    // 0's first fragments read
 #pragma unroll
     for (int s = 0; s < S; ++s) {
 #pragma unroll
-      for (int j = 0; j < G::LPW; ++j) copy(s, s, j);
+      for (int j = 0; j < G::LPW; ++j) copy(s, s, s, j);
       cursor_next();
     }
     wait_vmcnt_lgkm0<(S - 1) * G::LPW>();
     block_barrier();
     if (nk > 0) {
 #pragma unroll
-      for (int i = 0; i < G::TM; ++i) read_a(smem, 0, i);
+      for (int i = 0; i < G::TM; ++i) read_a(a_slot(0), 0, i);
 #pragma unroll
-      for (int j = 0; j < G::TN; ++j) read_b(smem, 0, 0, j);
+      for (int j = 0; j < G::TN; ++j) read_b(b_slot(0), 0, 0, j);
     }
     // steady state: the refill is a full K tile; then the tiles whose refill
     // is the ragged tile or past the end; then the last tile
-    while (kt + S < nfull) tile(std::integral_constant<int, 2>{});
+    constexpr int AHEAD = A3 ? 2 : S;  // the refill of tile kt is tile kt + AHEAD
+    while (kt + AHEAD < nfull) tile(std::integral_constant<int, 2>{});
     while (kt + 1 < nk) tile(std::integral_constant<int, 1>{});
-    if (kt < nk) tile(C0{});
+    if (kt < nk) tile(std::integral_constant<int, 0>{});
     // the refills past the end are still landing in LDS, which the epilogue reuses
     wait_vmcnt_lgkm0<0>();
   }

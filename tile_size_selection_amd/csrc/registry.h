@@ -16,7 +16,7 @@ using Launch = hipError_t (*)(const KernelArgs &, dim3 grid, int lds_bytes, hipS
 struct KernelEntry {
   int32_t bm, bn, bk, stages, threads, instr, dtype, op;  // op 0 = GEMM, 1 = conv
   Launch launch;
-  int32_t stage_bytes;
+  int32_t lds_bytes;  // dynamic LDS of one block
 };
 
 struct KernelTable {
