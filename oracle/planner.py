@@ -303,8 +303,8 @@ def round_half_even(x: Fraction) -> int:
 PAGES_SPACE = dict(bm=(16, 32, 64, 128, 256), bn=(16, 32, 64, 128, 256), bk=(16, 32, 64, 128),
                    stages=(2, 3, 4), threads=(128, 256, 512))
 # gfx950: tile sides largest first, so that of two otherwise equal tiles the
-# taller one comes first (its B panel -- the operand the convolution gathers
-# element by element -- is reused over more rows).
+# taller one comes first (it copies fewer B chunks per FLOP; in the
+# convolution those are the copies that carry per-lane pad and slice tests).
 GFX950_SPACE = dict(bm=(256, 128, 64), bn=(256, 128, 64), bk=(16, 32, 64),
                     stages=(2, 3, 4), threads=(128, 256, 512))
 

@@ -231,8 +231,8 @@ constexpr Space space_for(const tss_device &d, int32_t instr_filter) {
     s.ninstr = 3;
   } else {
     // largest first: of two otherwise equal tiles the taller one comes first
-    // (its B panel, the operand the convolution gathers element by element,
-    // is reused over more rows)
+    // (it copies fewer B chunks per FLOP; in the convolution those are the
+    // copies that carry per-lane pad and slice tests)
     int32_t sizes[3] = {256, 128, 64};
     for (int i = 0; i < 3; ++i) s.bm[i] = s.bn[i] = sizes[i];
     s.nbm = s.nbn = 3;
