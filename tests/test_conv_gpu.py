@@ -50,6 +50,9 @@ CASES = [  # N, C, H, W, Co, kh, kw, stride, pad, dil, tile_oh
     (1, 24, 30, 30, 136, 3, 3, (2, 2), (1, 1), (1, 1), 7),   # ragged channel tiles
     (2, 3, 17, 17, 16, 3, 3, (2, 2), (1, 1), (1, 1), 4),     # 3 channels, padded to 8 in the channel-last copy
     (1, 12, 10, 12, 8, 3, 2, (1, 1), (1, 0), (1, 1), 10),    # C*kh*kw = 72, Cp = 16
+    # 6x6 outputs, one row per H-tile: groups of 4 pixels that are one aligned
+    # run of y, that straddle two images, or that start misaligned
+    (3, 16, 12, 12, 24, 3, 3, (2, 2), (1, 1), (1, 1), 1),
 ]
 
 

@@ -316,15 +316,19 @@ __device__ __forceinline__ void store_tile(const Acc (&acc)[G::TM][G::TN], O *C,
 // (image n, output row o0 + oh_l, output column ow); y is NCHW.  The pixels
 // a lane holds do not depend on the MFMA row, so each is decoded once: the
 // first of every group of 4 consecutive columns by division, the next three
-// by stepping (ow, oh_l, n) forward.
+// by stepping (ow, oh_l, n) forward.  A lane's 4 consecutive columns are 4
+// consecutive y elements unless they straddle two images; where they are
+// (and the channel plane keeps them aligned) they go out as one vector store.
 template <typename G, typename O, typename Acc>
 __device__ __forceinline__ void store_conv(const Acc (&acc)[G::TM][G::TN], O *y, const KernelArgs &p, int m0, int n0,
                                            int wr, int wc, int lane, int o0, int rows_t, int npix) {
   constexpr int MF = G::MF;
   constexpr int NACC = AccType<MF>::n;
+  using V4 = typename Vec4<O>::type;
   const int plane = rows_t * p.OW;
   const int64_t chan = int64_t(p.OH) * p.OW;
   int64_t off[G::TN][NACC];  // y offset of the pixel at channel 0, or -1 past the last pixel
+  bool run[G::TN][NACC / 4];  // the group of 4 is one aligned vector in every channel
 #pragma unroll
   for (int j = 0; j < G::TN; ++j)
 #pragma unroll
@@ -346,6 +350,8 @@ __device__ __forceinline__ void store_conv(const Acc (&acc)[G::TM][G::TN], O *y,
           }
         }
       }
+      const int64_t o = off[j][e4 * 4];
+      run[j][e4] = chan % 4 == 0 && o >= 0 && o % 4 == 0 && off[j][e4 * 4 + 3] == o + 3;
     }
 #pragma unroll
   for (int i = 0; i < G::TM; ++i) {
@@ -354,8 +360,20 @@ __device__ __forceinline__ void store_conv(const Acc (&acc)[G::TM][G::TN], O *y,
 #pragma unroll
     for (int j = 0; j < G::TN; ++j)
 #pragma unroll
-      for (int e = 0; e < NACC; ++e)
-        if (off[j][e] >= 0) y[off[j][e] + int64_t(co) * chan] = convert_out<O>(acc[i][j][e]);
+      for (int e4 = 0; e4 < NACC / 4; ++e4) {
+        if (run[j][e4]) {
+          V4 v;
+#pragma unroll
+          for (int d = 0; d < 4; ++d) v[d] = convert_out<O>(acc[i][j][e4 * 4 + d]);
+          *(V4 *)(y + off[j][e4 * 4] + int64_t(co) * chan) = v;
+        } else {
+#pragma unroll
+          for (int d = 0; d < 4; ++d) {
+            const int e = e4 * 4 + d;
+            if (off[j][e] >= 0) y[off[j][e] + int64_t(co) * chan] = convert_out<O>(acc[i][j][e]);
+          }
+        }
+      }
   }
 }
 
