@@ -237,6 +237,29 @@ int32_t tss_conv2d(int64_t N, int64_t C, int64_t H, int64_t W, int64_t Cout, int
                    const void *w, void *y, void *workspace, int64_t workspace_bytes,
                    const tss_tile_config *cfg, void *stream);
 
+/*
+ * The same convolution over tiles of tile_n images x tile_oh output rows x
+ * tile_ow output columns (tss_conv2d is tile_n = N, tile_ow = OW).  The H/W
+ * tiling formulas of the Tiling page hold for either dimension: a tile reads
+ * input rows [in_start, min(in_end, H)) and columns [w_start, min(w_end, W))
+ * of its images, with the sub-operator pads pt'/pb' and pl'/pr' that
+ * tss_hw_tile gives for (H, kh, sh, ph, dh) and for (W, kw, sw, pw, dw);
+ * neighbouring tiles re-read the halo rows and columns.  Splitting the batch
+ * (the page's batch split) needs no halo.  The tiling changes which input a
+ * block reads, not the order of the sums: any tiling gives the same bits for
+ * the same cfg.
+ * tile_n in [1, N], tile_oh in [1, OH], tile_ow in [1, OW], and
+ * tile_n * tile_oh * tile_ow < 2^31.  Everything else as tss_conv2d (one
+ * GEMM batch entry per tile; cfg NULL = the planner's choice for the whole
+ * Cout x N*OH*OW x kh*kw*Cp GEMM).
+ * Errors: as tss_conv2d.
+ */
+int32_t tss_conv2d_tiled(int64_t N, int64_t C, int64_t H, int64_t W, int64_t Cout, int64_t kh,
+                         int64_t kw, int64_t sh, int64_t sw, int64_t ph, int64_t pw, int64_t dh,
+                         int64_t dw, int64_t tile_n, int64_t tile_oh, int64_t tile_ow, int32_t dtype,
+                         int32_t out_dtype, const void *x, const void *w, void *y, void *workspace,
+                         int64_t workspace_bytes, const tss_tile_config *cfg, void *stream);
+
 /* Bytes of workspace tss_conv2d needs for these sizes with any tile
    configuration (channels padded to 64), or TSS_E_ARG (< 0) for sizes
    tss_conv2d would reject as non-positive or above 2^30. */

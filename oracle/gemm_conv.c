@@ -24,6 +24,9 @@
  *        summation order equals the direct conv's, so the two agree bit for
  *        bit.
  *
+ *  Tiled conv: tiles over images, output rows and output columns; rows and
+ *        columns each take their slice and pads from the same formulas.
+ *
  * Inputs are the exact fp16 / bf16 values the device receives, widened to
  * double by the caller.  All arrays are dense row-major.
  */
@@ -146,6 +149,58 @@ int oracle_conv2d_htiled(int64_t N, int64_t Ci, int64_t H, int64_t W, int64_t Co
                   acc += xs[((n * Ci + ci) * HP + oh * sh + r * dh) * WP + ow * sw + s * dw] *
                          w[((co * Ci + ci) * kh + r) * kw + s];
             y[((n * Co + co) * OH + o0 + oh) * OW + ow] = acc;
+          }
+    free(xs);
+  }
+  return 0;
+}
+
+/*
+ * Tiles over images, output rows and output columns.  tiles: ntiles rows of
+ * (n0, n1, o0, o1, h_start, h_end, pt', pb', q0, q1, w_start, w_end, pl', pr'):
+ * images [n0, n1), output rows [o0, o1) and columns [q0, q1).  The H/W tiling
+ * formulas of the Tiling page hold for either dimension, so the columns get
+ * their own slice [w_start, min(w_end, W)) and pads pl' (left), pr' (right),
+ * as the rows do; images split without any halo.  Each tile materialises its
+ * zero-padded slice and runs an unpadded strided conv over it, in the direct
+ * conv's (ci, r, s) order, writing y[n0:n1, :, o0:o1, q0:q1].
+ */
+int oracle_conv2d_tiled(int64_t N, int64_t Ci, int64_t H, int64_t W, int64_t Co, int64_t kh,
+                        int64_t kw, int64_t sh, int64_t sw, int64_t ph, int64_t pw, int64_t dh,
+                        int64_t dw, int64_t ntiles, const int64_t *tiles, const double *x,
+                        const double *w, double *y) {
+  int64_t OH = out_extent(H, kh, sh, ph, ph, dh), OW = out_extent(W, kw, sw, pw, pw, dw);
+  for (int64_t t = 0; t < ntiles; ++t) {
+    const int64_t *tt = tiles + 14 * t;
+    int64_t n0 = tt[0], n1 = tt[1];
+    int64_t o0 = tt[2], o1 = tt[3], h_start = tt[4], h_end = tt[5], ptp = tt[6], pbp = tt[7];
+    int64_t q0 = tt[8], q1 = tt[9], w_start = tt[10], w_end = tt[11], plp = tt[12], prp = tt[13];
+    if (n0 < 0 || n1 > N || n0 >= n1) return -3;
+    int64_t rows_in = (h_end < H ? h_end : H) - h_start;
+    int64_t cols_in = (w_end < W ? w_end : W) - w_start;
+    int64_t HP = ptp + rows_in + pbp, WP = plp + cols_in + prp;
+    int64_t sub_oh = out_extent(HP, kh, sh, 0, 0, dh), sub_ow = out_extent(WP, kw, sw, 0, 0, dw);
+    if (sub_oh != o1 - o0 || sub_ow != q1 - q0) return -1; /* the slice does not produce the tile */
+    int64_t nb = n1 - n0;
+    double *xs = (double *)calloc((size_t)(nb * Ci * HP * WP), sizeof(double));
+    if (!xs) return -2;
+    for (int64_t n = 0; n < nb; ++n)
+      for (int64_t ci = 0; ci < Ci; ++ci)
+        for (int64_t r = 0; r < rows_in; ++r)
+          memcpy(xs + ((n * Ci + ci) * HP + ptp + r) * WP + plp,
+                 x + (((n0 + n) * Ci + ci) * H + h_start + r) * W + w_start, (size_t)cols_in * sizeof(double));
+#pragma omp parallel for collapse(2) schedule(dynamic, 1)
+    for (int64_t n = 0; n < nb; ++n)
+      for (int64_t co = 0; co < Co; ++co)
+        for (int64_t oh = 0; oh < sub_oh; ++oh)
+          for (int64_t ow = 0; ow < sub_ow; ++ow) {
+            double acc = 0.0;
+            for (int64_t ci = 0; ci < Ci; ++ci)
+              for (int64_t r = 0; r < kh; ++r)
+                for (int64_t s = 0; s < kw; ++s)
+                  acc += xs[((n * Ci + ci) * HP + oh * sh + r * dh) * WP + ow * sw + s * dw] *
+                         w[((co * Ci + ci) * kh + r) * kw + s];
+            y[(((n0 + n) * Co + co) * OH + o0 + oh) * OW + q0 + ow] = acc;
           }
     free(xs);
   }

@@ -47,6 +47,8 @@ def lib():
         L.oracle_conv2d.restype = None
         L.oracle_conv2d_htiled.argtypes = [i64] * 14 + [ip, dp, dp, dp]
         L.oracle_conv2d_htiled.restype = ctypes.c_int
+        L.oracle_conv2d_tiled.argtypes = [i64] * 14 + [ip, dp, dp, dp]
+        L.oracle_conv2d_tiled.restype = ctypes.c_int
         L.oracle_threads.argtypes = []
         L.oracle_threads.restype = ctypes.c_int
         _lib = L
@@ -125,6 +127,34 @@ def conv2d_htiled(x, w, stride=(1, 1), pad=(0, 0), dil=(1, 1), tile_oh: int = 8)
                                     _p(tiles, ctypes.c_int64), _p(x), _p(w), _p(y))
     if rc != 0:
         raise RuntimeError(f"H-tile slice table is inconsistent (rc={rc})")
+    return y
+
+
+def conv2d_tiled(x, w, stride=(1, 1), pad=(0, 0), dil=(1, 1), tile_oh: int = 8, tile_ow: Optional[int] = None,
+                 tile_n: Optional[int] = None):
+    """The same convolution assembled from tiles of tile_n images x tile_oh
+    output rows x tile_ow output columns.  Rows and columns each take their
+    slice and pads from oracle.htile (the Tiling page's H/W formulas, applied
+    to (H, kh, sh, ph, dh) and to (W, kw, sw, pw, dw)); images split with no
+    halo.  tile_ow / tile_n default to the whole width / batch."""
+    x, w = _f64(x), _f64(w)
+    N, Ci, H, W = x.shape
+    Co, _, kh, kw = w.shape
+    (sh, sw), (ph, pw), (dh, dw) = stride, pad, dil
+    shape = conv_out_shape(N, Co, H, W, kh, kw, sh, sw, ph, pw, dh, dw)
+    tile_ow = shape[3] if tile_ow is None else tile_ow
+    tile_n = N if tile_n is None else tile_n
+    rows = htile.tile_table(H, kh, sh, ph, dh, shape[2], tile_oh)
+    cols = htile.tile_table(W, kw, sw, pw, dw, shape[3], tile_ow)
+    table = [[n0, min(n0 + tile_n, N), r.o0, r.o1, r.in_start, r.in_end, r.pt, r.pb,
+              c.o0, c.o1, c.in_start, c.in_end, c.pt, c.pb]
+             for n0 in range(0, N, tile_n) for r in rows for c in cols]
+    tiles = np.ascontiguousarray(np.array(table, dtype=np.int64).reshape(-1, 14))
+    y = np.full(shape, np.nan)
+    rc = lib().oracle_conv2d_tiled(N, Ci, H, W, Co, kh, kw, sh, sw, ph, pw, dh, dw, len(table),
+                                   _p(tiles, ctypes.c_int64), _p(x), _p(w), _p(y))
+    if rc != 0:
+        raise RuntimeError(f"tile slice table is inconsistent (rc={rc})")
     return y
 
 

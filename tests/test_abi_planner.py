@@ -176,6 +176,10 @@ def test_argument_errors_before_device_work():
     assert cv(*base, 8, C.TSS_F16, C.TSS_F32, 16, 16, 16, 264, ws, None, None) == C.TSS_E_ALIGN  # misaligned
     assert cv(*[8, 256, 1, 56, 256, 3, 3, 2, 2, 0, 1, 1, 1], 1, C.TSS_F16, C.TSS_F32, *ok_ptrs, None,
               None) == C.TSS_E_ARG                                                           # window > input
+    cvt = lambda *a: L.tss_conv2d_tiled(*a)
+    for tn, toh, tow in [(0, 8, 8), (9, 8, 8), (8, 0, 8), (8, 29, 8), (8, 8, 0), (8, 8, 29)]:
+        assert cvt(*base, tn, toh, tow, C.TSS_F16, C.TSS_F32, *ok_ptrs, None, None) == C.TSS_E_ARG, (tn, toh, tow)
+    assert cvt(*base, 8, 8, 8, C.TSS_F16, C.TSS_F32, 16, 16, 16, 256, ws - 1, None, None) == C.TSS_E_ARG
     assert L.tss_evaluate(ctypes.byref(cfg), None, 0, 1, 1, 1, 2, ctypes.byref(C.Verdict())) == C.TSS_E_ARG
     assert L.tss_hw_tile(9, 3, 2, 1, 1, 2, 2, ctypes.byref(C.HwSlice())) == C.TSS_E_ARG
     assert L.tss_tile_plan(1, 64, 64, 64, 2, None, 99, None, None, 0, None) == C.TSS_E_ARG

@@ -74,6 +74,50 @@ def test_conv_small_exact(case, dtype):
         assert np.array_equal(to_f64(y), ref), (case, cfg)
 
 
+TILINGS = {  # case index in CASES -> (tile_n, tile_oh, tile_ow) triples, ragged tiles included
+    0: [(1, 2, 2), (2, 5, 3), (1, 1, 5), (2, 3, 1)],
+    1: [(1, 4, 3), (1, 13, 4), (1, 5, 11)],
+    2: [(2, 3, 4), (1, 9, 1), (3, 2, 5)],
+    3: [(1, 5, 3), (2, 7, 2), (1, 15, 1)],
+    5: [(1, 1, 1), (2, 2, 2), (1, 3, 1)],
+    9: [(2, 1, 4), (1, 6, 5), (3, 4, 6)],
+}
+
+
+@pytest.mark.parametrize("idx", sorted(TILINGS))
+def test_conv_2d_and_batch_tiles_exact(idx):
+    """Tiles of images x output rows x output columns, each reading its row
+    and column slices with the H/W formulas' pads: integer inputs give the
+    exact result, and every tiling gives the bits of the untiled run with the
+    same tile configuration."""
+    N, Ci, H, W, Co, kh, kw, st, pd, dl, _ = CASES[idx]
+    x = draw((N, Ci, H, W), "int", -2, 2, "f16", 71)
+    w = draw((Co, Ci, kh, kw), "int", -2, 2, "f16", 72)
+    ref, _ = G.conv2d(x.double().numpy(), w.double().numpy(), st, pd, dl)
+    dx, dw = x.to(CUDA), w.to(CUDA)
+    for cfg in (None, tss.TileConfig(64, 64, 16, 2, 128, "mfma32"), tss.TileConfig(128, 64, 64, 3, 256, "mfma16")):
+        whole = tss.conv2d(dx, dw, st, pd, dl, out_dtype="f32", cfg=cfg)
+        for tn, toh, tow in TILINGS[idx]:
+            y = tss.conv2d(dx, dw, st, pd, dl, tile_oh=toh, tile_ow=tow, tile_n=tn, out_dtype="f32", cfg=cfg)
+            torch.cuda.synchronize()
+            assert np.array_equal(to_f64(y), ref), (idx, cfg, tn, toh, tow)
+            assert torch.equal(y, whole), (idx, cfg, tn, toh, tow)
+
+
+def test_conv_workload_2d_tiles():
+    """The conv workload cut into 8x8-pixel tiles of 2 images: within the
+    bound of the fp64 oracle, and the same bits as its H-tiles alone."""
+    w = WORKLOADS[5]
+    x, wt = w.make()
+    dx, dw = x.to(CUDA), wt.to(CUDA)
+    y = tss.conv2d(dx, dw, w.stride, w.pad, w.dil, tile_oh=8, tile_ow=8, tile_n=2, out_dtype=w.out_dtype)
+    h_only = tss.conv2d(dx, dw, w.stride, w.pad, w.dil, tile_oh=8, out_dtype=w.out_dtype)
+    torch.cuda.synchronize()
+    assert torch.equal(y, h_only)
+    ref, S = G.conv2d(x.double().numpy(), wt.double().numpy(), w.stride, w.pad, w.dil)
+    check_bound(to_f64(y), ref, S, w.name + " 2-D tiles")
+
+
 def test_conv_low_precision_output():
     w = WORKLOADS[5]
     x, wt = w.make()

@@ -136,3 +136,35 @@ def test_conv_htiled_equals_direct_bitwise(H, W, k, stride, pad, dil, toh):
     y, _ = G.conv2d(x, w, (stride, stride), (pad, pad), (dil, dil))
     yt = G.conv2d_htiled(x, w, (stride, stride), (pad, pad), (dil, dil), toh)
     assert np.array_equal(y, yt)
+
+
+@pytest.mark.parametrize("H,W,kh,kw,stride,pad,dil,tilings", [
+    (9, 9, 3, 3, (2, 2), (1, 1), (1, 1), [(1, 2, 2), (2, 4, 1), (3, 1, 3)]),          # the worked example, both axes
+    (56, 56, 3, 3, (2, 2), (1, 1), (1, 1), [(1, 8, 8), (2, 28, 5), (3, 3, 28)]),      # the conv workload's geometry
+    (13, 11, 3, 5, (1, 2), (1, 2), (1, 1), [(1, 3, 2), (2, 13, 1), (3, 1, 6)]),
+    (15, 17, 3, 3, (2, 1), (2, 1), (2, 2), [(2, 4, 5), (1, 8, 17), (3, 2, 3)]),
+    (11, 12, 2, 3, (3, 2), (0, 1), (1, 2), [(1, 1, 1), (2, 2, 3), (3, 4, 2)]),
+])
+def test_conv_tiled_equals_direct_bitwise(H, W, kh, kw, stride, pad, dil, tilings):
+    """Tiles over images, output rows and output columns, the columns taking
+    their slice and pads from the same formulas as the rows: the direct
+    convolution's bits for every tiling (ragged tiles, pads on both sides,
+    dilation, unequal strides)."""
+    x = draw((3, 5, H, W), "uniform", -1, 1, "f16", 93).double().numpy()
+    w = draw((4, 5, kh, kw), "normal", 0, 0.05, "f16", 94).double().numpy()
+    y, _ = G.conv2d(x, w, stride, pad, dil)
+    for tn, toh, tow in tilings:
+        yt = G.conv2d_tiled(x, w, stride, pad, dil, toh, min(tow, y.shape[3]), tn)
+        assert np.array_equal(y, yt), (tn, toh, tow)
+
+
+def test_conv_tiled_columns_are_rows_transposed():
+    """Column tiles are row tiles of the transposed problem: tiling W of x
+    gives the transpose of tiling H of x with H and W swapped."""
+    x = draw((2, 3, 10, 13), "uniform", -1, 1, "f16", 95).double().numpy()
+    w = draw((4, 3, 3, 2), "normal", 0, 0.05, "f16", 96).double().numpy()
+    st, pd, dl = (2, 1), (1, 0), (1, 2)
+    y = G.conv2d_tiled(x, w, st, pd, dl, tile_oh=5, tile_ow=3)
+    xt, wt = np.ascontiguousarray(x.transpose(0, 1, 3, 2)), np.ascontiguousarray(w.transpose(0, 1, 3, 2))
+    yt = G.conv2d_tiled(xt, wt, st[::-1], pd[::-1], dl[::-1], tile_oh=3, tile_ow=5)
+    assert np.array_equal(y, yt.transpose(0, 1, 3, 2))

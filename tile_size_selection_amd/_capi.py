@@ -48,8 +48,8 @@ class HwSlice(ctypes.Structure):
 
 
 EXPORTS = ["tss_device_gfx950", "tss_device_pages", "tss_device_query", "tss_evaluate", "tss_tile_plan",
-           "tss_hw_tile", "tss_gemm", "tss_conv2d", "tss_conv2d_workspace_size", "tss_kernel_available",
-           "tss_gemm_default_config", "tss_status_string"]
+           "tss_hw_tile", "tss_gemm", "tss_conv2d", "tss_conv2d_tiled", "tss_conv2d_workspace_size",
+           "tss_kernel_available", "tss_gemm_default_config", "tss_status_string"]
 
 _lib = None
 
@@ -72,6 +72,7 @@ def lib():
     L.tss_hw_tile.argtypes = [i64, i64, i64, i64, i64, i64, i64, P(HwSlice)]
     L.tss_gemm.argtypes = [i64, i64, i64, i32, vp, vp, vp, i64, i32, P(TileConfig), vp]
     L.tss_conv2d.argtypes = [i64] * 14 + [i32, i32, vp, vp, vp, vp, i64, P(TileConfig), vp]
+    L.tss_conv2d_tiled.argtypes = [i64] * 16 + [i32, i32, vp, vp, vp, vp, i64, P(TileConfig), vp]
     L.tss_conv2d_workspace_size.argtypes = [i64] * 7
     L.tss_kernel_available.argtypes = [P(TileConfig), i32, i32]
     L.tss_gemm_default_config.argtypes = [i64, i64, i64, i64, i32, P(TileConfig)]

@@ -164,10 +164,12 @@ def conv2d_workspace_size(N: int, Ci: int, H: int, W: int, Cout: int, kh: int, k
 
 def conv2d(x, w, stride: Union[int, Sequence[int]] = 1, padding: Union[int, Sequence[int]] = 0,
            dilation: Union[int, Sequence[int]] = 1, tile_oh: Optional[int] = None, out_dtype: Optional[str] = None,
-           cfg: Optional[TileConfig] = None, out=None, stream=None, workspace=None):
-    """NCHW convolution as an implicit GEMM over output-row tiles of tile_oh
-    rows (default: the whole output height).  workspace: optional device
-    tensor of at least conv2d_workspace_size(...) bytes for the operands'
+           cfg: Optional[TileConfig] = None, out=None, stream=None, workspace=None, tile_ow: Optional[int] = None,
+           tile_n: Optional[int] = None):
+    """NCHW convolution as an implicit GEMM over tiles of tile_n images x
+    tile_oh output rows x tile_ow output columns (defaults: the whole batch,
+    height and width; tss_conv2d_tiled).  workspace: optional device tensor
+    of at least conv2d_workspace_size(...) bytes for the operands'
     channel-last copies (allocated here when not given)."""
     pair = lambda v: (v, v) if isinstance(v, int) else tuple(v)
     (sh, sw), (ph, pw), (dh, dw) = pair(stride), pair(padding), pair(dilation)
@@ -197,9 +199,9 @@ def conv2d(x, w, stride: Union[int, Sequence[int]] = 1, padding: Union[int, Sequ
     elif not (workspace.is_cuda and workspace.is_contiguous() and workspace.numel() * workspace.element_size()
               >= ws_bytes):
         raise ValueError(f"workspace must be a contiguous device tensor of at least {ws_bytes} bytes")
-    st = C.lib().tss_conv2d(N, Ci, H, W, Co, kh, kw, sh, sw, ph, pw, dh, dw, tile_oh or OH, _DT[dt], _DT[od],
-                            x.data_ptr(), w.data_ptr(), out.data_ptr(), workspace.data_ptr(),
-                            workspace.numel() * workspace.element_size(), ctypes.byref(cfg.c()) if cfg else None,
-                            _stream_ptr(stream))
-    C.check(st, "tss_conv2d")
+    st = C.lib().tss_conv2d_tiled(N, Ci, H, W, Co, kh, kw, sh, sw, ph, pw, dh, dw, tile_n or N, tile_oh or OH,
+                                  tile_ow or OW, _DT[dt], _DT[od], x.data_ptr(), w.data_ptr(), out.data_ptr(),
+                                  workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                  ctypes.byref(cfg.c()) if cfg else None, _stream_ptr(stream))
+    C.check(st, "tss_conv2d_tiled")
     return out

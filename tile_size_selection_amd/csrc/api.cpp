@@ -199,10 +199,11 @@ int64_t tss_conv2d_workspace_size(int64_t N, int64_t C, int64_t H, int64_t W, in
   return conv_workspace(N, C, H, W, Cout, kh, kw, kConvChannelAlignMax).total;
 }
 
-int32_t tss_conv2d(int64_t N, int64_t C, int64_t H, int64_t W, int64_t Cout, int64_t kh, int64_t kw, int64_t sh,
-                   int64_t sw, int64_t ph, int64_t pw, int64_t dh, int64_t dw, int64_t tile_oh, int32_t dtype,
-                   int32_t out_dtype, const void *x, const void *w, void *y, void *workspace,
-                   int64_t workspace_bytes, const tss_tile_config *cfg, void *stream) {
+int32_t tss_conv2d_tiled(int64_t N, int64_t C, int64_t H, int64_t W, int64_t Cout, int64_t kh, int64_t kw,
+                         int64_t sh, int64_t sw, int64_t ph, int64_t pw, int64_t dh, int64_t dw, int64_t tile_n,
+                         int64_t tile_oh, int64_t tile_ow, int32_t dtype, int32_t out_dtype, const void *x,
+                         const void *w, void *y, void *workspace, int64_t workspace_bytes,
+                         const tss_tile_config *cfg, void *stream) {
   const int64_t lim = int64_t(1) << 30;
   if (N < 1 || C < 1 || H < 1 || W < 1 || Cout < 1 || kh < 1 || kw < 1 || sh < 1 || sw < 1 || ph < 0 || pw < 0 ||
       dh < 1 || dw < 1)
@@ -215,7 +216,7 @@ int32_t tss_conv2d(int64_t N, int64_t C, int64_t H, int64_t W, int64_t Cout, int
   const int64_t OH = (H + 2 * ph - (kh - 1) * dh - 1) / sh + 1;
   const int64_t OW = (W + 2 * pw - (kw - 1) * dw - 1) / sw + 1;
   if (H + 2 * ph < (kh - 1) * dh + 1 || W + 2 * pw < (kw - 1) * dw + 1) return TSS_E_ARG;
-  if (tile_oh < 1 || tile_oh > OH) return TSS_E_ARG;
+  if (tile_oh < 1 || tile_oh > OH || tile_ow < 1 || tile_ow > OW || tile_n < 1 || tile_n > N) return TSS_E_ARG;
   // sizes with the largest channel padding any tile can ask for
   const ConvWorkspace wmax = conv_workspace(N, C, H, W, Cout, kh, kw, kConvChannelAlignMax);
   // every operand, and both layout copies, addressable with 32-bit byte offsets
@@ -224,7 +225,7 @@ int32_t tss_conv2d(int64_t N, int64_t C, int64_t H, int64_t W, int64_t Cout, int
     return TSS_E_ARG;
   const int64_t out_bytes = out_dtype == TSS_F32 ? 4 : 2;
   if (N * Cout * OH * OW * out_bytes >= (int64_t(1) << 40)) return TSS_E_ARG;
-  const int64_t tile_pixels = N * tile_oh * OW;
+  const int64_t tile_pixels = tile_n * tile_oh * tile_ow;
   if (tile_pixels > INT32_MAX) return TSS_E_ARG;
   if (!x || !w || !y || !workspace) return TSS_E_ARG;
   if (workspace_bytes < wmax.total) return TSS_E_ARG;
@@ -269,7 +270,7 @@ int32_t tss_conv2d(int64_t N, int64_t C, int64_t H, int64_t W, int64_t Cout, int
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return TSS_E_HIP;
 
-  // 2. the implicit GEMM over H-tiles
+  // 2. the implicit GEMM over the tiles
   KernelArgs a{};
   a.A = wr;
   a.B = xc;
@@ -297,11 +298,29 @@ int32_t tss_conv2d(int64_t N, int64_t C, int64_t H, int64_t W, int64_t Cout, int
   a.OW = int32_t(OW);
   a.tile_oh = int32_t(tile_oh);
   a.Cp = int32_t(ws.Cp);
-  const int64_t n_htiles = (OH + tile_oh - 1) / tile_oh;
-  const int64_t blocks = n_htiles * a.tiles_m * a.tiles_n;
+  a.tile_ow = int32_t(tile_ow);
+  a.tile_n = int32_t(tile_n);
+  a.n_ht = int32_t((OH + tile_oh - 1) / tile_oh);
+  a.n_wt = int32_t((OW + tile_ow - 1) / tile_ow);
+  const int64_t n_tiles = (N + tile_n - 1) / tile_n * a.n_ht * a.n_wt;
+  const int64_t blocks = n_tiles * a.tiles_m * a.tiles_n;
   if (blocks * c.threads > int64_t(UINT32_MAX)) return TSS_E_ARG;
   err = e->launch(a, dim3(uint32_t(blocks)), e->lds_bytes, (hipStream_t)stream);
   return err == hipSuccess ? TSS_OK : TSS_E_HIP;
+}
+
+int32_t tss_conv2d(int64_t N, int64_t C, int64_t H, int64_t W, int64_t Cout, int64_t kh, int64_t kw, int64_t sh,
+                   int64_t sw, int64_t ph, int64_t pw, int64_t dh, int64_t dw, int64_t tile_oh, int32_t dtype,
+                   int32_t out_dtype, const void *x, const void *w, void *y, void *workspace,
+                   int64_t workspace_bytes, const tss_tile_config *cfg, void *stream) {
+  // H-tiles only: every tile spans the whole batch and the whole output width
+  const int64_t lim = int64_t(1) << 30;
+  if (N < 1 || W < 1 || kw < 1 || sw < 1 || pw < 0 || dw < 1) return TSS_E_ARG;
+  if (N > lim || W > lim || kw > lim || sw > lim || pw > lim || dw > lim) return TSS_E_ARG;
+  if (W + 2 * pw < (kw - 1) * dw + 1) return TSS_E_ARG;
+  const int64_t OW = (W + 2 * pw - (kw - 1) * dw - 1) / sw + 1;
+  return tss_conv2d_tiled(N, C, H, W, Cout, kh, kw, sh, sw, ph, pw, dh, dw, N, tile_oh, OW, dtype, out_dtype, x, w,
+                          y, workspace, workspace_bytes, cfg, stream);
 }
 
 }  // extern "C"

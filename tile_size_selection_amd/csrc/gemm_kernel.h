@@ -62,14 +62,17 @@ struct KernelArgs {
   const void *A;  // GEMM: A[batch][M][K].       conv: weights wr[Cout][kh][kw][Cp]
   const void *B;  // GEMM: B[batch][K][N].       conv: input xc[Nb][H][W][Cp]
   void *C;        // GEMM: C[batch][M][N].       conv: output y[Nb][Cout][OH][OW]
-  int32_t M, N, K;  // conv: M = Cout, K = kh*kw*Cp, N = pixels of a full H-tile
+  int32_t M, N, K;  // conv: M = Cout, K = kh*kw*Cp, N = pixels of a full tile
   int32_t tiles_m, tiles_n;
   int32_t group_m;    // tile rows per group of the L2-friendly tile order
   int32_t out_dtype;  // TSS_F32 / TSS_F16 / TSS_BF16
   int64_t batch_stride_a, batch_stride_b, batch_stride_c;  // GEMM only, elements
-  // convolution geometry (CONV only); the GEMM batch index is the H-tile
+  // convolution geometry (CONV only).  The output is cut into tiles of
+  // tile_n images x tile_oh rows x tile_ow columns; the GEMM batch index is
+  // the tile, (image group * n_ht + row tile) * n_wt + column tile.
   int32_t Nb, Cin, H, W, kh, kw, sh, sw, ph, pw, dh, dw, OH, OW, tile_oh;
   int32_t Cp;  // channels of the channel-last input copy: Cin rounded up to a multiple of BK
+  int32_t tile_ow, tile_n, n_ht, n_wt;
 };
 
 // ---- small device helpers --------------------------------------------------
@@ -312,20 +315,21 @@ __device__ __forceinline__ void store_tile(const Acc (&acc)[G::TM][G::TN], O *C,
   }
 }
 
-// Convolution epilogue: row = output channel, column = pixel of the H-tile
-// (image n, output row o0 + oh_l, output column ow); y is NCHW.  The pixels
-// a lane holds do not depend on the MFMA row, so each is decoded once: the
-// first of every group of 4 consecutive columns by division, the next three
-// by stepping (ow, oh_l, n) forward.  A lane's 4 consecutive columns are 4
+// Convolution epilogue: row = output channel, column = pixel of the tile
+// (image nb0 + n_l, output row o0 + oh_l, output column q0 + ow_l); y is
+// NCHW.  The pixels a lane holds do not depend on the MFMA row, so each is
+// decoded once: the first of every group of 4 consecutive columns by
+// division, the next three by stepping (ow_l, oh_l, n) forward.  A lane's 4 consecutive columns are 4
 // consecutive y elements unless they straddle two images; where they are
 // (and the channel plane keeps them aligned) they go out as one vector store.
 template <typename G, typename O, typename Acc>
 __device__ __forceinline__ void store_conv(const Acc (&acc)[G::TM][G::TN], O *y, const KernelArgs &p, int m0, int n0,
-                                           int wr, int wc, int lane, int o0, int rows_t, int npix) {
+                                           int wr, int wc, int lane, int nb0, int o0, int rows_t, int q0, int cols_t,
+                                           int npix) {
   constexpr int MF = G::MF;
   constexpr int NACC = AccType<MF>::n;
   using V4 = typename Vec4<O>::type;
-  const int plane = rows_t * p.OW;
+  const int plane = rows_t * cols_t;
   const int64_t chan = int64_t(p.OH) * p.OW;
   int64_t off[G::TN][NACC];  // y offset of the pixel at channel 0, or -1 past the last pixel
   bool run[G::TN][NACC / 4];  // the group of 4 is one aligned vector in every channel
@@ -336,13 +340,15 @@ __device__ __forceinline__ void store_conv(const Acc (&acc)[G::TM][G::TN], O *y,
       int pix = n0 + wc * G::WTN + j * MF + acc_col4<MF>(e4, lane);
       int n = pix / plane;
       const int rem = pix - n * plane;
-      int oh = rem / p.OW;
-      int ow = rem - oh * p.OW;
+      int oh = rem / cols_t;
+      int ow = rem - oh * cols_t;
+      n += nb0;
 #pragma unroll
       for (int d = 0; d < 4; ++d) {
-        off[j][e4 * 4 + d] = pix < npix ? (int64_t(n) * p.M * chan + int64_t(o0 + oh) * p.OW + ow) : int64_t(-1);
+        off[j][e4 * 4 + d] =
+            pix < npix ? (int64_t(n) * p.M * chan + int64_t(o0 + oh) * p.OW + q0 + ow) : int64_t(-1);
         ++pix;
-        if (++ow == p.OW) {
+        if (++ow == cols_t) {
           ow = 0;
           if (++oh == rows_t) {
             oh = 0;
@@ -408,19 +414,32 @@ __global__ __launch_bounds__(G::THREADS) void tiled_gemm_kernel(KernelArgs p) {
   const int m0 = tm * G::BM, n0 = tn * G::BN;
   const int M = p.M, K = p.K;
 
-  // -- convolution: this block's H-tile, its input slice and sub-operator pads
+  // -- convolution: this block's tile (images, output rows, output
+  // columns), its input slice and the sub-operator pads.  Rows and columns
+  // each follow the H/W tiling formulas; images split with no halo.
   int N = p.N;
   int o0 = 0, rows_t = 0, in_start = 0, pt_sub = 0, rows_in = 0;
+  int q0 = 0, cols_t = 0, w_start = 0, pl_sub = 0, cols_in = 0, nb0 = 0;
   if constexpr (CONV) {
-    o0 = bz * p.tile_oh;
+    const int wt = bz % p.n_wt, hz = bz / p.n_wt;
+    const int ht = hz % p.n_ht, ng = hz / p.n_ht;
+    o0 = ht * p.tile_oh;
     const int o1 = min(o0 + p.tile_oh, p.OH);
     rows_t = o1 - o0;
-    N = p.Nb * rows_t * p.OW;        // pixels of this H-tile, over the batch
-    if (n0 >= N) return;             // ragged last H-tile: whole block idle
-    in_start = max(0, o0 * p.sh - p.ph);                          // (1)
+    q0 = wt * p.tile_ow;
+    const int q1 = min(q0 + p.tile_ow, p.OW);
+    cols_t = q1 - q0;
+    nb0 = ng * p.tile_n;
+    N = min(p.tile_n, p.Nb - nb0) * rows_t * cols_t;  // pixels of this tile
+    if (n0 >= N) return;                                  // ragged last tile: whole block idle
+    in_start = max(0, o0 * p.sh - p.ph);                                // (1)
     const int in_end = (o1 - 1) * p.sh - p.ph + (p.kh - 1) * p.dh + 1;  // (2), exclusive
-    pt_sub = max(0, p.ph - o0 * p.sh);                            // (3)
-    rows_in = min(in_end, p.H) - in_start;                        // slice rows; (4) pads the rest
+    pt_sub = max(0, p.ph - o0 * p.sh);                                  // (3)
+    rows_in = min(in_end, p.H) - in_start;                              // slice rows; (4) pads the rest
+    w_start = max(0, q0 * p.sw - p.pw);
+    const int w_end = (q1 - 1) * p.sw - p.pw + (p.kw - 1) * p.dw + 1;
+    pl_sub = max(0, p.pw - q0 * p.sw);
+    cols_in = min(w_end, p.W) - w_start;
   }
 
   const T *Ab = reinterpret_cast<const T *>(p.A) + (CONV ? 0 : int64_t(bz) * p.batch_stride_a) + int64_t(m0) * K;
@@ -453,7 +472,7 @@ __global__ __launch_bounds__(G::THREADS) void tiled_gemm_kernel(KernelArgs p) {
   // laid out and swizzled like A); K runs over (r, s, ci) of the channel-last
   // input, so a 16-byte chunk is 8 consecutive channels of one input pixel.
   // Per lane: the byte offset of its pixel's window corner (channel 0), the
-  // corner's slice row and input column, and the chunk's first K element.
+  // corner's slice row and slice column, and the chunk's first K element.
   uint32_t b_off[G::B_LOADS];
   int b_k[G::B_LOADS];
   int b_row[CONV ? G::B_LOADS : 1], b_col[CONV ? G::B_LOADS : 1];
@@ -470,17 +489,18 @@ __global__ __launch_bounds__(G::THREADS) void tiled_gemm_kernel(KernelArgs p) {
       const int r = pchunk / G::CA, pc = pchunk % G::CA;
       const int lc = pc ^ G::swz_a(r);
       const int pix = n0 + r;
-      const int plane = rows_t * p.OW;
+      const int plane = rows_t * cols_t;
       const int n = pix / plane, rem = pix - n * plane;
-      const int oh_l = rem / p.OW, ow = rem - oh_l * p.OW;
-      const int sr = oh_l * p.sh;                 // slice row of the window's top tap
-      const int iw = ow * p.sw - p.pw;            // input column of the window's left tap
+      const int oh_l = rem / cols_t, ow_l = rem - oh_l * cols_t;
+      const int sr = oh_l * p.sh;                 // padded-slice row of the window's top tap
+      const int sc = ow_l * p.sw;                 // padded-slice column of its left tap
       const int ih = in_start - pt_sub + sr;      // its input row (= (o0 + oh_l)*sh - ph)
+      const int iw = w_start - pl_sub + sc;       // its input column (= (q0 + ow_l)*sw - pw)
       // may wrap below zero for a pad corner; used only where the chunk is valid
-      b_off[j] = uint32_t(((n * p.H + ih) * p.W + iw) * p.Cp + lc * 8) * 2u;
+      b_off[j] = uint32_t((((nb0 + n) * p.H + ih) * p.W + iw) * p.Cp + lc * 8) * 2u;
       b_k[j] = lc * 8;
       b_row[j] = pix < N ? sr - pt_sub : (1 << 30);  // slice rows [pt', pt' + rows_in) hold data
-      b_col[j] = iw;
+      b_col[j] = sc - pl_sub;                        // slice columns [pl', pl' + cols_in) likewise
     }
   }
 
@@ -505,12 +525,12 @@ __global__ __launch_bounds__(G::THREADS) void tiled_gemm_kernel(KernelArgs p) {
     }
   };
   // conv, the K tile at the cursor (starting at k0): byte offset of the copy
-  // of B chunk j, or kOOB where the chunk lies in a pad, outside the H-tile's
+  // of B chunk j, or kOOB where the chunk lies in a pad, outside the tile's
   // slice, past the last pixel or past K
   auto conv_b_off = [&](int k0, int j) __attribute__((always_inline)) -> uint32_t {
     const int dr = cur_r * p.dh, ds = cur_s * p.dw;
     const bool ok = k0 + b_k[j] < K && uint32_t(b_row[j] + dr) < uint32_t(rows_in) &&
-                    uint32_t(b_col[j] + ds) < uint32_t(p.W);
+                    uint32_t(b_col[j] + ds) < uint32_t(cols_in);
     return ok ? b_off[j] + uint32_t(((dr * p.W + ds) * p.Cp + cur_ci) * 2) : kOOB;
   };
   // LDS slots.  The plain ring: stage s holds A at s*STAGE_BYTES and B right
@@ -804,11 +824,14 @@ __global__ __launch_bounds__(G::THREADS) void tiled_gemm_kernel(KernelArgs p) {
       store_tile<G, __bf16>(acc, reinterpret_cast<__bf16 *>(p.C) + cbase, smem, m0, n0, wave, wr, wc, lane, M, N);
   } else {
     if (p.out_dtype == TSS_F32)
-      store_conv<G, float>(acc, reinterpret_cast<float *>(p.C), p, m0, n0, wr, wc, lane, o0, rows_t, N);
+      store_conv<G, float>(acc, reinterpret_cast<float *>(p.C), p, m0, n0, wr, wc, lane, nb0, o0, rows_t, q0, cols_t,
+                                N);
     else if (p.out_dtype == TSS_F16)
-      store_conv<G, _Float16>(acc, reinterpret_cast<_Float16 *>(p.C), p, m0, n0, wr, wc, lane, o0, rows_t, N);
+      store_conv<G, _Float16>(acc, reinterpret_cast<_Float16 *>(p.C), p, m0, n0, wr, wc, lane, nb0, o0, rows_t, q0, cols_t,
+                                N);
     else
-      store_conv<G, __bf16>(acc, reinterpret_cast<__bf16 *>(p.C), p, m0, n0, wr, wc, lane, o0, rows_t, N);
+      store_conv<G, __bf16>(acc, reinterpret_cast<__bf16 *>(p.C), p, m0, n0, wr, wc, lane, nb0, o0, rows_t, q0, cols_t,
+                                N);
   }
 }
 
