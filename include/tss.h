@@ -180,6 +180,32 @@ int32_t tss_tile_plan(int64_t batch, int64_t M, int64_t N, int64_t K, int32_t el
                       const tss_device *dev, int32_t instr_filter, tss_verdict *best,
                       tss_verdict *list, int32_t cap, int32_t *n_feasible);
 
+/*
+ * The planner with feedback from the compiled kernels.  The tile_decision.py
+ * page's C2 counts only the accumulators, and its README lists the register
+ * model as a known limitation.  Here each candidate takes what its compiled
+ * kernel uses: the registers per lane replace the model's estimate (rounded
+ * up to the allocation granule) in the occupancy, and so in C4's resident
+ * blocks, waves and fill and in the ranking; a kernel that spills to scratch
+ * fails C2 (the page's "expect spilling to local memory").  Which
+ * configurations are candidates is still the model's decision (C3, C1, C2 on
+ * the accumulators, occupancy).
+ * table: n_table entries (configuration, registers per lane > 0, scratch
+ * bytes per lane >= 0); a candidate absent from the table is left out.
+ * gfx950 model and ranking (as tss_tile_plan with dev = NULL, instr_filter
+ * = 0).
+ * Errors: TSS_E_ARG (bad sizes, n_table < 0, table NULL with n_table > 0, a
+ * register count <= 0 or negative scratch), TSS_E_INFEASIBLE (no candidate).
+ */
+typedef struct {
+  tss_tile_config cfg;
+  int32_t regs_per_lane, scratch_bytes;
+} tss_measured_usage;
+
+int32_t tss_tile_plan_usage(int64_t batch, int64_t M, int64_t N, int64_t K, int32_t elem_bytes,
+                            const tss_measured_usage *table, int32_t n_table, tss_verdict *best,
+                            tss_verdict *list, int32_t cap, int32_t *n_feasible);
+
 /* One H-tile of a convolution ("Tiling（分块）" page, H/W tiling formulas):
    output rows [o0, o1) need input rows [in_start, in_end) (in_end exclusive,
    may exceed H), sub-operator pads pt' (top) and pb' (bottom), and share
@@ -268,6 +294,29 @@ int64_t tss_conv2d_workspace_size(int64_t N, int64_t C, int64_t H, int64_t W, in
 
 /* 1 if a kernel is compiled for cfg and dtype (op 0 = GEMM, 1 = conv), else 0. */
 int32_t tss_kernel_available(const tss_tile_config *cfg, int32_t dtype, int32_t op);
+
+/*
+ * What the compiled kernel for (cfg, dtype, op) uses, read through the HIP
+ * runtime from its code object: registers per lane (VGPRs and AGPRs of the
+ * unified file), LDS per block (static plus the launch's dynamic size),
+ * private memory per lane (register spills; 0 = none), the largest block it
+ * accepts, and the blocks per CU the runtime's occupancy calculator allows
+ * at the launch's block size and LDS.  Needs a GPU.
+ * Errors: TSS_E_ARG (NULL pointer, op not 0/1), TSS_E_UNSUPPORTED (no kernel
+ * compiled for cfg), TSS_E_HIP (no device, runtime error).
+ */
+typedef struct {
+  int32_t regs_per_lane, lds_bytes, scratch_bytes, max_threads, blocks_per_cu, pad_;
+} tss_kernel_usage;
+
+int32_t tss_kernel_usage_query(const tss_tile_config *cfg, int32_t dtype, int32_t op,
+                               tss_kernel_usage *out);
+
+/* tss_tile_plan_usage with the table read from every compiled kernel of
+   (dtype, op) by tss_kernel_usage_query (read once per process).  Needs a
+   GPU; errors as both. */
+int32_t tss_tile_plan_measured(int64_t batch, int64_t M, int64_t N, int64_t K, int32_t dtype, int32_t op,
+                               tss_verdict *best, tss_verdict *list, int32_t cap, int32_t *n_feasible);
 
 /* The configuration tss_gemm / tss_conv2d would take for a NULL cfg. */
 int32_t tss_gemm_default_config(int64_t batch, int64_t M, int64_t N, int64_t K, int32_t dtype,

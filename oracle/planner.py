@@ -173,7 +173,14 @@ def _ceil_div(a: int, b: int) -> int:
 # ---------------------------------------------------------------------------
 
 
-def evaluate(cfg: TileConfig, dev: DeviceModel, elem_bytes: int = 2, accum_bytes: int = 4) -> Verdict:
+def evaluate(cfg: TileConfig, dev: DeviceModel, elem_bytes: int = 2, accum_bytes: int = 4,
+             regs_measured: Optional[int] = None, spill_bytes: int = 0) -> Verdict:
+    """C3, C1, C2 and occupancy of one configuration.  regs_measured: the
+    registers per lane a compiled kernel of this configuration uses; given,
+    they replace the register estimate in the occupancy (rounded up to the
+    allocation granule).  spill_bytes > 0: that kernel spills to scratch,
+    which fails C2 -- the README page names the accumulator-only register
+    model a limitation, and C2's own message is the spill."""
     v = Verdict(config=cfg)
     bm, bn, bk, st, thr = cfg.block_m, cfg.block_n, cfg.block_k, cfg.stages, cfg.threads
 
@@ -222,10 +229,15 @@ def evaluate(cfg: TileConfig, dev: DeviceModel, elem_bytes: int = 2, accum_bytes
     raw = v.accum_per_thread * accum_bytes // 4
     acc_regs = _ceil_div(raw, dev.reg_granule_per_lane) * dev.reg_granule_per_lane
     v.regs_per_thread = acc_regs + dev.reg_overhead
+    if regs_measured:
+        v.regs_per_thread = _ceil_div(regs_measured, dev.reg_granule_per_lane) * dev.reg_granule_per_lane
     if acc_regs > dev.acc_regs_max:
         v.failures.append("C2")
         v.messages.append(f"C2 accumulators alone need {acc_regs} registers/thread"
                           f" (> {dev.acc_regs_max}); expect spilling to local memory")
+    elif spill_bytes > 0:
+        v.failures.append("C2")
+        v.messages.append(f"C2 the compiled kernel spills {spill_bytes} bytes/thread to local memory")
     v.regs_per_block = v.regs_per_thread * thr
 
     # Occupancy: resident blocks per SM/CU allowed by registers, by on-chip
@@ -362,15 +374,26 @@ def candidates(dev: DeviceModel, k: int, instrs: Sequence[str]):
 
 
 def sweep(m: int, n: int, k: int, dev: DeviceModel, instrs: Sequence[str], batch: int = 1,
-          elem_bytes: int = 2) -> List[Verdict]:
+          elem_bytes: int = 2, regs: Optional[dict] = None) -> List[Verdict]:
     """All feasible candidates in preference order (a stable sort over the
     enumeration order block_M, block_N, block_K, stages, threads, with the
-    instruction shape outermost)."""
+    instruction shape outermost).  regs: {TileConfig: (registers per lane,
+    scratch bytes per lane) of its compiled kernel}; given, the model still
+    decides which candidates exist, those missing from regs are left out, and
+    the others take their occupancy from the measured registers and fail C2
+    if they spill."""
     out = []
     for cfg in candidates(dev, k, instrs):
         v = evaluate(cfg, dev, elem_bytes=elem_bytes)
         if not v.feasible:
             continue
+        if regs is not None:
+            if cfg not in regs:
+                continue
+            r, spill = regs[cfg]
+            v = evaluate(cfg, dev, elem_bytes=elem_bytes, regs_measured=r, spill_bytes=spill)
+            if not v.feasible:
+                continue
         finish_parallelism(v, m, n, dev, batch)
         v.traffic = dram_traffic(m, n, k, cfg, elem_bytes, batch)
         out.append(v)
@@ -379,10 +402,11 @@ def sweep(m: int, n: int, k: int, dev: DeviceModel, instrs: Sequence[str], batch
 
 
 def plan(m: int, n: int, k: int, dev: Optional[DeviceModel] = None, batch: int = 1,
-         elem_bytes: int = 2, instrs: Optional[Sequence[str]] = None) -> Tuple[Optional[Verdict], int]:
+         elem_bytes: int = 2, instrs: Optional[Sequence[str]] = None,
+         regs: Optional[dict] = None) -> Tuple[Optional[Verdict], int]:
     dev = dev or device_gfx950()
     instrs = instrs or [s for s, _ in dev.instr_shapes]
-    res = sweep(m, n, k, dev, instrs, batch, elem_bytes)
+    res = sweep(m, n, k, dev, instrs, batch, elem_bytes, regs)
     return (res[0] if res else None), len(res)
 
 

@@ -80,6 +80,76 @@ def test_planner_sweep_bit_exact(name):
             _same(best, ores[0])
 
 
+def _tc(c: OP.TileConfig) -> tss.TileConfig:
+    return tss.TileConfig(c.block_m, c.block_n, c.block_k, c.stages, c.threads, c.instr)
+
+
+@pytest.mark.parametrize("seed", [1, 2, 3])
+def test_plan_with_measured_usage_bit_exact(seed):
+    """tss_tile_plan_usage against the oracle's sweep with the same table:
+    imagined compiled kernels with registers above and below the model's
+    estimate, some spilling, some missing."""
+    g = OP.device_gfx950()
+    instrs = [s for s, _ in g.instr_shapes]
+    rng = np.random.default_rng(seed)
+    feas = [c for c in OP.candidates(g, 1 << 20, instrs) if OP.evaluate(c, g).feasible]
+    usage_o = {}
+    for c in feas:
+        if rng.random() < 0.1:
+            continue                                              # no kernel
+        usage_o[c] = (int(rng.integers(1, 257)), int(rng.integers(1, 600)) if rng.random() < 0.1 else 0)
+    usage_c = {_tc(c): u for c, u in usage_o.items()}
+    for (b, M, N, K) in [(1, 4096, 4096, 4096), (1, 256, 6272, 2304), (4, 3000, 5000, 2048), (1, 100, 37, 24)]:
+        ores = OP.sweep(M, N, K, g, instrs, batch=b, regs=usage_o)
+        best, lst, n = tss.tile_plan_usage(M, N, K, usage_c, batch=b, cap=len(ores) + 5)
+        assert n == len(ores) and len(lst) == len(ores)
+        for vc, vo in zip(lst, ores):
+            _same(vc, vo)
+        _same(best, ores[0])
+        assert all(u[1] == 0 for c, u in usage_o.items() if c in {v.config for v in ores})
+
+
+def test_measured_usage_closed_forms():
+    """Occupancy from measured registers, worked by hand: per SIMD 512 /
+    registers (rounded up to 8) waves, at most 8; a block's waves spread over
+    the 4 SIMDs.  A spilling kernel fails C2; feeding the model's own
+    estimate back changes nothing."""
+    g = OP.device_gfx950()
+    big = OP.TileConfig(256, 256, 64, 2, 512, "mfma16")
+    v = OP.evaluate(big, g)                                # 128 accumulators + 32 = 160 -> 3 waves/SIMD, 12 per CU
+    assert (v.regs_per_thread, v.blocks_by_regs) == (160, 1)
+    v = OP.evaluate(big, g, regs_measured=250)             # 256 -> 2 waves/SIMD, 8 per CU: one 8-wave block
+    assert (v.regs_per_thread, v.blocks_by_regs, v.blocks_per_core) == (256, 1, 1)
+    small = OP.TileConfig(64, 64, 32, 2, 256, "mfma16")
+    v = OP.evaluate(small, g)                              # 16 + 32 = 48 -> 8 waves/SIMD, 32 per CU: 8 blocks
+    assert (v.regs_per_thread, v.blocks_by_regs) == (48, 8)
+    v = OP.evaluate(small, g, regs_measured=97)            # 104 -> 4 waves/SIMD, 16 per CU: 4 blocks of 4 waves
+    assert (v.regs_per_thread, v.blocks_by_regs, v.blocks_per_core) == (104, 4, 4)
+    assert v.accum_per_thread == 16 and not v.failures
+    wide = OP.TileConfig(256, 256, 64, 2, 256, "mfma16")   # 256 accumulators: the model's C2 lets it through
+    assert OP.evaluate(wide, g).feasible
+    v = OP.evaluate(wide, g, regs_measured=512, spill_bytes=144)
+    assert v.failures == ["C2"] and "spills 144 bytes" in v.messages[0]
+    instrs = [s for s, _ in g.instr_shapes]
+    for (b, M, N, K) in [(1, 4096, 4096, 4096), (1, 256, 6272, 2304)]:
+        plain = OP.sweep(M, N, K, g, instrs, batch=b)
+        fed = OP.sweep(M, N, K, g, instrs, batch=b, regs={x.config: (x.regs_per_thread, 0) for x in plain})
+        assert [x.config for x in fed] == [x.config for x in plain]
+        assert [x.blocks_per_core for x in fed] == [x.blocks_per_core for x in plain]
+        best_c, lst_c, n_c = tss.tile_plan_usage(M, N, K, {_tc(x.config): (x.regs_per_thread, 0) for x in plain},
+                                                 batch=b, cap=len(plain))
+        best_p, lst_p, n_p = tss.tile_plan(M, N, K, batch=b, cap=len(plain))
+        assert n_c == n_p and [x["config"] for x in lst_c] == [x["config"] for x in lst_p]
+    L = C.lib()
+    t = (C.MeasuredUsage * 1)()
+    t[0].cfg = _tc(big).c()
+    for r, sc in ((0, 0), (-1, 0), (160, -1)):
+        t[0].regs_per_lane, t[0].scratch_bytes = r, sc
+        assert L.tss_tile_plan_usage(1, 64, 64, 64, 2, t, 1, None, None, 0, None) == C.TSS_E_ARG
+    assert L.tss_tile_plan_usage(1, 64, 64, 64, 2, None, 1, None, None, 0, None) == C.TSS_E_ARG
+    assert L.tss_tile_plan_usage(1, 64, 64, 64, 2, None, 0, None, None, 0, None) == C.TSS_E_INFEASIBLE
+
+
 def test_planner_pages_printout_through_c():
     """The README page's printed sweep figures, reproduced by the C++ planner."""
     best, lst, n = tss.tile_plan(4096, 4096, 4096, dev=tss.device_pages(), instr="wgmma", cap=8)

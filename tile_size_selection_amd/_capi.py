@@ -43,13 +43,23 @@ class Verdict(ctypes.Structure):
                 + [("failures", u32), ("warnings", u32), ("binding", i32), ("pad_", i32)])
 
 
+class MeasuredUsage(ctypes.Structure):
+    _fields_ = [("cfg", TileConfig), ("regs_per_lane", i32), ("scratch_bytes", i32)]
+
+
+class KernelUsage(ctypes.Structure):
+    _fields_ = [(n, i32) for n in ("regs_per_lane", "lds_bytes", "scratch_bytes", "max_threads", "blocks_per_cu",
+                                   "pad_")]
+
+
 class HwSlice(ctypes.Structure):
     _fields_ = [(n, i64) for n in ("o0", "o1", "in_start", "in_end", "in_span", "pt", "pb", "halo")]
 
 
 EXPORTS = ["tss_device_gfx950", "tss_device_pages", "tss_device_query", "tss_evaluate", "tss_tile_plan",
-           "tss_hw_tile", "tss_gemm", "tss_conv2d", "tss_conv2d_tiled", "tss_conv2d_workspace_size",
-           "tss_kernel_available", "tss_gemm_default_config", "tss_status_string"]
+           "tss_tile_plan_usage", "tss_hw_tile", "tss_gemm", "tss_conv2d", "tss_conv2d_tiled",
+           "tss_conv2d_workspace_size", "tss_kernel_available", "tss_kernel_usage_query", "tss_tile_plan_measured",
+           "tss_gemm_default_config", "tss_status_string"]
 
 _lib = None
 
@@ -69,12 +79,16 @@ def lib():
     L.tss_device_query.argtypes = [i32, P(Device)]
     L.tss_evaluate.argtypes = [P(TileConfig), P(Device), i64, i64, i64, i64, i32, P(Verdict)]
     L.tss_tile_plan.argtypes = [i64, i64, i64, i64, i32, P(Device), i32, P(Verdict), P(Verdict), i32, P(i32)]
+    L.tss_tile_plan_usage.argtypes = [i64, i64, i64, i64, i32, P(MeasuredUsage), i32, P(Verdict), P(Verdict), i32,
+                                      P(i32)]
     L.tss_hw_tile.argtypes = [i64, i64, i64, i64, i64, i64, i64, P(HwSlice)]
     L.tss_gemm.argtypes = [i64, i64, i64, i32, vp, vp, vp, i64, i32, P(TileConfig), vp]
     L.tss_conv2d.argtypes = [i64] * 14 + [i32, i32, vp, vp, vp, vp, i64, P(TileConfig), vp]
     L.tss_conv2d_tiled.argtypes = [i64] * 16 + [i32, i32, vp, vp, vp, vp, i64, P(TileConfig), vp]
     L.tss_conv2d_workspace_size.argtypes = [i64] * 7
     L.tss_kernel_available.argtypes = [P(TileConfig), i32, i32]
+    L.tss_kernel_usage_query.argtypes = [P(TileConfig), i32, i32, P(KernelUsage)]
+    L.tss_tile_plan_measured.argtypes = [i64, i64, i64, i64, i32, i32, P(Verdict), P(Verdict), i32, P(i32)]
     L.tss_gemm_default_config.argtypes = [i64, i64, i64, i64, i32, P(TileConfig)]
     L.tss_status_string.argtypes = [i32]
     L.tss_status_string.restype = ctypes.c_char_p

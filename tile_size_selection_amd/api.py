@@ -94,6 +94,48 @@ def tile_plan(M: int, N: int, K: int, batch: int = 1, elem_bytes: int = 2, dev: 
     return verdict_dict(best), [verdict_dict(lst[i]) for i in range(min(cap, n.value))], n.value
 
 
+def _plan_result(st, best, lst, cap, n, where):
+    if st == C.TSS_E_INFEASIBLE:
+        return None, [], 0
+    C.check(st, where)
+    return verdict_dict(best), [verdict_dict(lst[i]) for i in range(min(cap, n.value))], n.value
+
+
+def tile_plan_usage(M: int, N: int, K: int, usage: dict, batch: int = 1, elem_bytes: int = 2,
+                    cap: int = 0) -> Tuple[Optional[dict], List[dict], int]:
+    """tss_tile_plan_usage: the gfx950 plan with each candidate's occupancy
+    taken from its compiled kernel's registers per lane, and kernels that
+    spill failing C2; usage = {TileConfig: (registers per lane, scratch bytes
+    per lane)}."""
+    table = (C.MeasuredUsage * max(len(usage), 1))()
+    for i, (cfg, (r, sc)) in enumerate(usage.items()):
+        table[i].cfg = cfg.c()
+        table[i].regs_per_lane = int(r)
+        table[i].scratch_bytes = int(sc)
+    best, lst, n = C.Verdict(), (C.Verdict * max(cap, 1))(), C.i32(0)
+    st = C.lib().tss_tile_plan_usage(batch, M, N, K, elem_bytes, table if usage else None, len(usage),
+                                     ctypes.byref(best), lst if cap else None, cap, ctypes.byref(n))
+    return _plan_result(st, best, lst, cap, n, "tss_tile_plan_usage")
+
+
+def kernel_usage(cfg: TileConfig, dtype: str = "f16", op: str = "gemm") -> dict:
+    """tss_kernel_usage_query: what the compiled kernel uses (needs a GPU)."""
+    u = C.KernelUsage()
+    C.check(C.lib().tss_kernel_usage_query(ctypes.byref(cfg.c()), _DT[dtype], 0 if op == "gemm" else 1,
+                                           ctypes.byref(u)), "tss_kernel_usage_query")
+    return {f: getattr(u, f) for f, _ in C.KernelUsage._fields_ if f != "pad_"}
+
+
+def tile_plan_measured(M: int, N: int, K: int, batch: int = 1, dtype: str = "f16", op: str = "gemm",
+                       cap: int = 0) -> Tuple[Optional[dict], List[dict], int]:
+    """tss_tile_plan_measured: tile_plan_usage with every compiled kernel's
+    usage read from its code object (needs a GPU)."""
+    best, lst, n = C.Verdict(), (C.Verdict * max(cap, 1))(), C.i32(0)
+    st = C.lib().tss_tile_plan_measured(batch, M, N, K, _DT[dtype], 0 if op == "gemm" else 1, ctypes.byref(best),
+                                        lst if cap else None, cap, ctypes.byref(n))
+    return _plan_result(st, best, lst, cap, n, "tss_tile_plan_measured")
+
+
 def hw_tile(H: int, kh: int, sh: int, pt: int, d: int, o0: int, o1: int) -> dict:
     s = C.HwSlice()
     C.check(C.lib().tss_hw_tile(H, kh, sh, pt, d, o0, o1, ctypes.byref(s)), "tss_hw_tile")

@@ -7,6 +7,7 @@
 #include <map>
 #include <mutex>
 #include <tuple>
+#include <utility>
 #include <vector>
 
 #include "conv_layout.h"
@@ -140,6 +141,52 @@ int32_t tss_device_query(int32_t hip_device, tss_device *out) {
 int32_t tss_kernel_available(const tss_tile_config *cfg, int32_t dtype, int32_t op) {
   if (!cfg || (op != 0 && op != 1)) return 0;
   return find_kernel(*cfg, dtype, op) ? 1 : 0;
+}
+
+int32_t tss_kernel_usage_query(const tss_tile_config *cfg, int32_t dtype, int32_t op, tss_kernel_usage *out) {
+  if (!cfg || !out || (op != 0 && op != 1)) return TSS_E_ARG;
+  const KernelEntry *e = find_kernel(*cfg, dtype, op);
+  if (!e) return TSS_E_UNSUPPORTED;
+  hipFuncAttributes attr{};
+  int blocks = 0;
+  if (e->usage(&attr, &blocks, e->lds_bytes) != hipSuccess) return TSS_E_HIP;
+  tss_kernel_usage u{};
+  u.regs_per_lane = attr.numRegs;
+  u.lds_bytes = int32_t(attr.sharedSizeBytes) + e->lds_bytes;
+  u.scratch_bytes = int32_t(attr.localSizeBytes);
+  u.max_threads = attr.maxThreadsPerBlock;
+  u.blocks_per_cu = blocks;
+  *out = u;
+  return TSS_OK;
+}
+
+int32_t tss_tile_plan_measured(int64_t batch, int64_t M, int64_t N, int64_t K, int32_t dtype, int32_t op,
+                               tss_verdict *best, tss_verdict *list, int32_t cap, int32_t *n_feasible) {
+  if (op != 0 && op != 1) return TSS_E_ARG;
+  if (dtype != TSS_F16 && dtype != TSS_BF16) return TSS_E_DTYPE;
+  // the registers of every compiled kernel of (dtype, op), read once
+  static std::mutex mu;
+  static std::map<std::pair<int32_t, int32_t>, std::vector<tss_measured_usage>> tables;
+  std::vector<tss_measured_usage> table;
+  {
+    std::lock_guard<std::mutex> g(mu);
+    auto it = tables.find({dtype, op});
+    if (it != tables.end()) table = it->second;
+  }
+  if (table.empty()) {
+    for (const auto &kv : registry()) {
+      const KernelEntry &e = kv.second;
+      if (e.dtype != dtype || e.op != op) continue;
+      tss_tile_config c{e.bm, e.bn, e.bk, e.stages, e.threads, e.instr};
+      tss_kernel_usage u{};
+      int32_t st = tss_kernel_usage_query(&c, dtype, op, &u);
+      if (st != TSS_OK) return st;
+      table.push_back(tss_measured_usage{c, u.regs_per_lane, u.scratch_bytes});
+    }
+    std::lock_guard<std::mutex> g(mu);
+    tables[{dtype, op}] = table;
+  }
+  return tss_tile_plan_usage(batch, M, N, K, 2, table.data(), int32_t(table.size()), best, list, cap, n_feasible);
 }
 
 int32_t tss_gemm_default_config(int64_t batch, int64_t M, int64_t N, int64_t K, int32_t dtype,

@@ -23,6 +23,67 @@ bool valid_config(const tss_tile_config &c, const tss_device &d) {
   return c.bm > 0 && c.bn > 0 && c.bk > 0 && c.stages > 0 && c.threads > 0 && instr_on_device(c.instr, d);
 }
 
+
+// The shared sweep: every candidate of the device's space that passes
+// C3/C1/C2/occupancy, finished for the problem and ranked.  usage_of (may be
+// null) gives the compiled kernel's measured usage for a configuration (null
+// to leave the candidate out).
+template <typename UsageOf>
+int32_t plan_sweep(int64_t batch, int64_t M, int64_t N, int64_t K, int32_t elem_bytes, const tss_device &d,
+                   int32_t instr_filter, const UsageOf *usage_of, tss_verdict *best, tss_verdict *list, int32_t cap,
+                   int32_t *n_feasible) {
+  if (batch < 1 || M < 0 || N < 0 || K < 0 || elem_bytes < 1 || elem_bytes > 8 || cap < 0) return TSS_E_ARG;
+  if (M > (int64_t(1) << 40) || N > (int64_t(1) << 40) || K > (int64_t(1) << 40) || batch > (int64_t(1) << 20))
+    return TSS_E_ARG;
+  if (!valid_device(d)) return TSS_E_ARG;
+  if (instr_filter && !instr_on_device(instr_filter, d)) return TSS_E_ARG;
+  const Space s = space_for(d, instr_filter);
+  // A K step longer than K is skipped, unless K is shorter than every
+  // candidate step: then the shortest one is kept (its tail is masked).
+  const int64_t bk_cap = K > s.bk[0] ? K : s.bk[0];
+  std::vector<tss_verdict> feas;
+  feas.reserve(512);
+  for (int ii = 0; ii < s.ninstr; ++ii) {
+    Shape sh{};
+    instr_shape(s.instr[ii], sh);
+    for (int a = 0; a < s.nbm; ++a)
+      for (int b = 0; b < s.nbn; ++b)
+        for (int c = 0; c < s.nbk; ++c) {
+          if (s.bk[c] > bk_cap) continue;
+          for (int e = 0; e < s.nst; ++e)
+            for (int f = 0; f < s.nthr; ++f) {
+              if (s.threads[f] % sh.threads) continue;
+              tss_tile_config cfg{s.bm[a], s.bn[b], s.bk[c], s.stages[e], s.threads[f], s.instr[ii]};
+              int64_t regs = 0, scratch = 0;
+              if (usage_of) {
+                if (evaluate_block(cfg, d, elem_bytes).failures) continue;  // the model decides what exists
+                const tss_measured_usage *u = (*usage_of)(cfg);
+                if (!u) continue;
+                regs = u->regs_per_lane;
+                scratch = u->scratch_bytes;
+              }
+              tss_verdict v = evaluate_block(cfg, d, elem_bytes, regs, scratch);
+              if (v.failures) continue;
+              finish(v, d, batch, M, N, K, elem_bytes);
+              feas.push_back(v);
+            }
+        }
+  }
+  std::stable_sort(feas.begin(), feas.end(), [&](const tss_verdict &x, const tss_verdict &y) {
+    return key_less(rank_key(x, d), rank_key(y, d));
+  });
+  if (n_feasible) *n_feasible = int32_t(feas.size());
+  if (list)
+    for (int32_t i = 0; i < cap && i < int32_t(feas.size()); ++i) list[i] = feas[i];
+  if (feas.empty()) return TSS_E_INFEASIBLE;
+  if (best) *best = feas[0];
+  return TSS_OK;
+}
+
+struct NoUsage {
+  const tss_measured_usage *operator()(const tss_tile_config &) const { return nullptr; }
+};
+
 }  // namespace
 
 extern "C" {
@@ -52,48 +113,30 @@ int32_t tss_evaluate(const tss_tile_config *cfg, const tss_device *dev, int64_t 
   return TSS_OK;
 }
 
+
 int32_t tss_tile_plan(int64_t batch, int64_t M, int64_t N, int64_t K, int32_t elem_bytes, const tss_device *dev,
                       int32_t instr_filter, tss_verdict *best, tss_verdict *list, int32_t cap,
                       int32_t *n_feasible) {
   const tss_device d = dev ? *dev : gfx950_device();
-  if (batch < 1 || M < 0 || N < 0 || K < 0 || elem_bytes < 1 || elem_bytes > 8 || cap < 0) return TSS_E_ARG;
-  if (M > (int64_t(1) << 40) || N > (int64_t(1) << 40) || K > (int64_t(1) << 40) || batch > (int64_t(1) << 20))
-    return TSS_E_ARG;
-  if (!valid_device(d)) return TSS_E_ARG;
-  if (instr_filter && !instr_on_device(instr_filter, d)) return TSS_E_ARG;
-  const Space s = space_for(d, instr_filter);
-  // A K step longer than K is skipped, unless K is shorter than every
-  // candidate step: then the shortest one is kept (its tail is masked).
-  const int64_t bk_cap = K > s.bk[0] ? K : s.bk[0];
-  std::vector<tss_verdict> feas;
-  feas.reserve(512);
-  for (int ii = 0; ii < s.ninstr; ++ii) {
-    Shape sh{};
-    instr_shape(s.instr[ii], sh);
-    for (int a = 0; a < s.nbm; ++a)
-      for (int b = 0; b < s.nbn; ++b)
-        for (int c = 0; c < s.nbk; ++c) {
-          if (s.bk[c] > bk_cap) continue;
-          for (int e = 0; e < s.nst; ++e)
-            for (int f = 0; f < s.nthr; ++f) {
-              if (s.threads[f] % sh.threads) continue;
-              tss_tile_config cfg{s.bm[a], s.bn[b], s.bk[c], s.stages[e], s.threads[f], s.instr[ii]};
-              tss_verdict v = evaluate_block(cfg, d, elem_bytes);
-              if (v.failures) continue;
-              finish(v, d, batch, M, N, K, elem_bytes);
-              feas.push_back(v);
-            }
-        }
-  }
-  std::stable_sort(feas.begin(), feas.end(), [&](const tss_verdict &x, const tss_verdict &y) {
-    return key_less(rank_key(x, d), rank_key(y, d));
-  });
-  if (n_feasible) *n_feasible = int32_t(feas.size());
-  if (list)
-    for (int32_t i = 0; i < cap && i < int32_t(feas.size()); ++i) list[i] = feas[i];
-  if (feas.empty()) return TSS_E_INFEASIBLE;
-  if (best) *best = feas[0];
-  return TSS_OK;
+  return plan_sweep<NoUsage>(batch, M, N, K, elem_bytes, d, instr_filter, nullptr, best, list, cap, n_feasible);
+}
+
+int32_t tss_tile_plan_usage(int64_t batch, int64_t M, int64_t N, int64_t K, int32_t elem_bytes,
+                            const tss_measured_usage *table, int32_t n_table, tss_verdict *best, tss_verdict *list,
+                            int32_t cap, int32_t *n_feasible) {
+  if (n_table < 0 || (n_table > 0 && !table)) return TSS_E_ARG;
+  for (int32_t i = 0; i < n_table; ++i)
+    if (table[i].regs_per_lane <= 0 || table[i].scratch_bytes < 0) return TSS_E_ARG;
+  auto usage_of = [&](const tss_tile_config &c) -> const tss_measured_usage * {
+    for (int32_t i = 0; i < n_table; ++i) {
+      const tss_tile_config &t = table[i].cfg;
+      if (t.bm == c.bm && t.bn == c.bn && t.bk == c.bk && t.stages == c.stages && t.threads == c.threads &&
+          t.instr == c.instr)
+        return &table[i];
+    }
+    return nullptr;
+  };
+  return plan_sweep(batch, M, N, K, elem_bytes, gfx950_device(), 0, &usage_of, best, list, cap, n_feasible);
 }
 
 int32_t tss_hw_tile(int64_t H, int64_t kh, int64_t sh, int64_t pt, int64_t d, int64_t o0, int64_t o1,

@@ -97,7 +97,12 @@ constexpr tss_device pages_device(int32_t sm_count, int32_t smem_kb) {
 constexpr int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // C3 + C1 + C2 + occupancy: the parts that do not depend on the problem.
-constexpr tss_verdict evaluate_block(const tss_tile_config &c, const tss_device &d, int32_t eb) {
+// regs_measured > 0: the registers per lane of the compiled kernel, which then
+// replace the model's estimate for occupancy (rounded up to the allocation
+// granule); scratch_measured > 0: the compiled kernel spills that many bytes
+// per lane, which fails C2 whatever the accumulator count says.
+constexpr tss_verdict evaluate_block(const tss_tile_config &c, const tss_device &d, int32_t eb,
+                                     int64_t regs_measured = 0, int64_t scratch_measured = 0) {
   tss_verdict v{};
   v.cfg = c;
   Shape s{};
@@ -129,7 +134,8 @@ constexpr tss_verdict evaluate_block(const tss_tile_config &c, const tss_device 
   int64_t raw = v.accum_per_thread * 4 / 4;
   int64_t acc_regs = cdiv(raw, d.reg_granule_per_lane) * d.reg_granule_per_lane;
   v.regs_per_thread = acc_regs + d.reg_overhead;
-  if (acc_regs > d.acc_regs_max) v.failures |= TSS_FAIL_C2;
+  if (regs_measured > 0) v.regs_per_thread = cdiv(regs_measured, d.reg_granule_per_lane) * d.reg_granule_per_lane;
+  if (acc_regs > d.acc_regs_max || scratch_measured > 0) v.failures |= TSS_FAIL_C2;
   v.regs_per_block = v.regs_per_thread * c.threads;
   // occupancy
   if (d.reg_model == TSS_REG_POOLED) {

@@ -12,11 +12,15 @@
 namespace tss {
 
 using Launch = hipError_t (*)(const KernelArgs &, dim3 grid, int lds_bytes, hipStream_t s);
+// code object attributes of the kernel, and the blocks per CU the runtime
+// allows at its block size with lds_bytes of dynamic LDS
+using Usage = hipError_t (*)(hipFuncAttributes *attr, int *blocks_per_cu, int lds_bytes);
 
 struct KernelEntry {
   int32_t bm, bn, bk, stages, threads, instr, dtype, op;  // op 0 = GEMM, 1 = conv
   Launch launch;
   int32_t lds_bytes;  // dynamic LDS of one block
+  Usage usage;
 };
 
 struct KernelTable {
@@ -53,6 +57,15 @@ hipError_t launch_kernel(const KernelArgs &a, dim3 grid, int lds_bytes, hipStrea
   if (attr != hipSuccess) return attr;
   hipLaunchKernelGGL((tiled_gemm_kernel<G, T, CONV>), grid, dim3(G::THREADS), lds_bytes, s, a);
   return hipGetLastError();
+}
+
+template <typename G, typename T, bool CONV>
+hipError_t kernel_usage(hipFuncAttributes *attr, int *blocks_per_cu, int lds_bytes) {
+  const void *f = (const void *)tiled_gemm_kernel<G, T, CONV>;
+  hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, 163840);
+  if (e == hipSuccess) e = hipFuncGetAttributes(attr, f);
+  if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, f, G::THREADS, lds_bytes);
+  return e;
 }
 
 }  // namespace tss
