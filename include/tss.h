@@ -318,6 +318,30 @@ int32_t tss_kernel_usage_query(const tss_tile_config *cfg, int32_t dtype, int32_
 int32_t tss_tile_plan_measured(int64_t batch, int64_t M, int64_t N, int64_t K, int32_t dtype, int32_t op,
                                tss_verdict *best, tss_verdict *list, int32_t cap, int32_t *n_feasible);
 
+/*
+ * LDS bank microbenchmark, the gfx950 counterpart of the Tiling page's table
+ * of bank conflicts by access stride and of its XOR swizzle.  Launches
+ * `blocks` blocks of 8 waves; every wave times (shader clock cycles) `iters`
+ * x 8 LDS reads of one pattern and writes the count to cycles[block * 8 +
+ * wave] (device memory, blocks * 8 int64, owned by the caller).
+ *   TSS_LDS_B32 / TSS_LDS_B128 / TSS_LDS_TR_B64: lane l reads 4 / 16 / 8
+ *     bytes (ds_read_b32, ds_read_b128, ds_read_b64_tr_b16) at byte
+ *     l * stride_words * 4; stride_words in [0, 4096], a multiple of 4 for
+ *     B128 and of 2 for TR_B64;
+ *   TSS_LDS_GEMM_A(_PLAIN): the GEMM kernel's A fragment read (256x256x64
+ *     tile, 8 waves, 16x16x32 MFMA) with (without) its XOR swizzle;
+ *   TSS_LDS_GEMM_B(_PLAIN): its B fragment transpose read likewise;
+ *   stride_words is ignored for the GEMM patterns.
+ * iters in [1, 2^20], blocks in [1, 65536].  Asynchronous on `stream`.
+ * Errors: TSS_E_ARG, TSS_E_HIP.
+ */
+enum {
+  TSS_LDS_B32 = 1, TSS_LDS_B128 = 2, TSS_LDS_TR_B64 = 3, TSS_LDS_GEMM_A = 4, TSS_LDS_GEMM_A_PLAIN = 5,
+  TSS_LDS_GEMM_B = 6, TSS_LDS_GEMM_B_PLAIN = 7
+};
+int32_t tss_lds_probe(int32_t pattern, int32_t stride_words, int32_t iters, int32_t blocks, int64_t *cycles,
+                      void *stream);
+
 /* The configuration tss_gemm / tss_conv2d would take for a NULL cfg. */
 int32_t tss_gemm_default_config(int64_t batch, int64_t M, int64_t N, int64_t K, int32_t dtype,
                                 tss_tile_config *out);

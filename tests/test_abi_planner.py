@@ -250,6 +250,12 @@ def test_argument_errors_before_device_work():
     for tn, toh, tow in [(0, 8, 8), (9, 8, 8), (8, 0, 8), (8, 29, 8), (8, 8, 0), (8, 8, 29)]:
         assert cvt(*base, tn, toh, tow, C.TSS_F16, C.TSS_F32, *ok_ptrs, None, None) == C.TSS_E_ARG, (tn, toh, tow)
     assert cvt(*base, 8, 8, 8, C.TSS_F16, C.TSS_F32, 16, 16, 16, 256, ws - 1, None, None) == C.TSS_E_ARG
+    lp = L.tss_lds_probe
+    assert lp(1, 1, 10, 1, None, None) == C.TSS_E_ARG                 # no output buffer
+    assert lp(99, 1, 10, 1, 64, None) == C.TSS_E_ARG                  # unknown pattern
+    assert lp(2, 6, 10, 1, 64, None) == C.TSS_E_ARG                   # 16-byte reads at a 24-byte stride
+    assert lp(3, 3, 10, 1, 64, None) == C.TSS_E_ARG                   # 8-byte reads at a 12-byte stride
+    assert lp(1, 1, 0, 1, 64, None) == C.TSS_E_ARG and lp(1, 1, 10, 0, 64, None) == C.TSS_E_ARG
     assert L.tss_evaluate(ctypes.byref(cfg), None, 0, 1, 1, 1, 2, ctypes.byref(C.Verdict())) == C.TSS_E_ARG
     assert L.tss_hw_tile(9, 3, 2, 1, 1, 2, 2, ctypes.byref(C.HwSlice())) == C.TSS_E_ARG
     assert L.tss_tile_plan(1, 64, 64, 64, 2, None, 99, None, None, 0, None) == C.TSS_E_ARG

@@ -13,6 +13,7 @@ LIB_PATH = os.path.join(_HERE, "libtss.so")
 
 TSS_OK, TSS_E_ARG, TSS_E_DTYPE, TSS_E_ALIGN, TSS_E_INFEASIBLE, TSS_E_HIP, TSS_E_UNSUPPORTED = 0, -1, -2, -3, -4, -5, -6
 TSS_F16, TSS_BF16, TSS_F32 = 1, 2, 3
+LDS_PATTERN = {"b32": 1, "b128": 2, "tr_b64": 3, "gemm_a": 4, "gemm_a_plain": 5, "gemm_b": 6, "gemm_b_plain": 7}
 INSTR = {"mfma32": 1, "mfma16": 2, "mma": 16, "wgmma": 17, "simt": 18}
 INSTR_NAME = {v: k for k, v in INSTR.items()}
 FAIL_BITS = ["C3_M", "C3_N", "C3_K", "C3_THREADS", "C3_MAXTHREADS", "C3_WAVEGRID", "C3_LOAD", "C1", "C2", "OCC0"]
@@ -59,7 +60,7 @@ class HwSlice(ctypes.Structure):
 EXPORTS = ["tss_device_gfx950", "tss_device_pages", "tss_device_query", "tss_evaluate", "tss_tile_plan",
            "tss_tile_plan_usage", "tss_hw_tile", "tss_gemm", "tss_conv2d", "tss_conv2d_tiled",
            "tss_conv2d_workspace_size", "tss_kernel_available", "tss_kernel_usage_query", "tss_tile_plan_measured",
-           "tss_gemm_default_config", "tss_status_string"]
+           "tss_lds_probe", "tss_gemm_default_config", "tss_status_string"]
 
 _lib = None
 
@@ -89,6 +90,7 @@ def lib():
     L.tss_kernel_available.argtypes = [P(TileConfig), i32, i32]
     L.tss_kernel_usage_query.argtypes = [P(TileConfig), i32, i32, P(KernelUsage)]
     L.tss_tile_plan_measured.argtypes = [i64, i64, i64, i64, i32, i32, P(Verdict), P(Verdict), i32, P(i32)]
+    L.tss_lds_probe.argtypes = [i32, i32, i32, i32, vp, vp]
     L.tss_gemm_default_config.argtypes = [i64, i64, i64, i64, i32, P(TileConfig)]
     L.tss_status_string.argtypes = [i32]
     L.tss_status_string.restype = ctypes.c_char_p

@@ -136,6 +136,22 @@ def tile_plan_measured(M: int, N: int, K: int, batch: int = 1, dtype: str = "f16
     return _plan_result(st, best, lst, cap, n, "tss_tile_plan_measured")
 
 
+def lds_probe(pattern: str, stride_words: int = 1, iters: int = 2000, blocks: int = 256, stream=None) -> float:
+    """tss_lds_probe: shader-clock cycles per LDS read instruction of one wave
+    (median over every wave of the launch) for an access pattern; see
+    LDS_PATTERN in _capi for the names.  Needs a GPU."""
+    if torch is None:
+        raise RuntimeError("lds_probe needs torch for its device buffer")
+    cycles = torch.zeros(blocks * 8, dtype=torch.int64, device="cuda")
+    C.check(C.lib().tss_lds_probe(C.LDS_PATTERN[pattern], stride_words, iters, blocks, cycles.data_ptr(),
+                                  _stream_ptr(stream)), "tss_lds_probe")
+    torch.cuda.synchronize()
+    c = cycles.cpu()
+    if bool((c <= 0).any()):
+        raise RuntimeError("lds_probe: a wave reported no cycles")
+    return float(c.double().median()) / (iters * 8)
+
+
 def hw_tile(H: int, kh: int, sh: int, pt: int, d: int, o0: int, o1: int) -> dict:
     s = C.HwSlice()
     C.check(C.lib().tss_hw_tile(H, kh, sh, pt, d, o0, o1, ctypes.byref(s)), "tss_hw_tile")

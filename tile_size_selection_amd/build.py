@@ -37,7 +37,7 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++20", "-fPIC", "-Wall", "-Wno-u
 
 
 def sources():
-    return ([os.path.join(CSRC, "planner.cpp"), os.path.join(CSRC, "api.cpp")]
+    return ([os.path.join(CSRC, "planner.cpp"), os.path.join(CSRC, "api.cpp"), os.path.join(CSRC, "lds_probe.hip")]
             + sorted(glob.glob(os.path.join(CSRC, "inst", "*.hip"))))
 
 

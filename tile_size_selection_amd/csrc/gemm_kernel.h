@@ -30,13 +30,14 @@
 //
 // The same kernel computes a convolution as an implicit GEMM (CONV = true):
 // A is the weight matrix Cout x (kh*kw*Cp) with K ordered (r, s, ci), loaded
-// exactly as the GEMM's A; B is the im2col matrix of one H-tile, stored in
-// LDS transposed (pixels x K, laid out like A) and copied HBM -> LDS from a
-// channel-last copy of the input, 16 bytes (8 channels of one input pixel)
-// per lane.  Both operand copies come from conv_layout.h.  The batch index
-// of the GEMM is the H-tile.  Each block derives its input slice and the
-// sub-operator pads from the Tiling page's H/W tiling formulas; chunks that
-// fall in a pad or outside the slice read as zero.
+// exactly as the GEMM's A; B is the im2col matrix of one output tile (images
+// x output rows x output columns), stored in LDS transposed (pixels x K, laid
+// out like A) and copied HBM -> LDS from a channel-last copy of the input, 16
+// bytes (8 channels of one input pixel) per lane.  Both operand copies come
+// from conv_layout.h.  The batch index of the GEMM is the tile.  Each block
+// derives its input rows and columns and the sub-operator pads from the
+// Tiling page's H/W tiling formulas; chunks that fall in a pad or outside the
+// slice read as zero.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -217,6 +218,27 @@ struct Geometry {
   static __device__ __forceinline__ int swz_b(int k) {
     int q = CB >= 16 ? 4 * (k % 4) : 4 * ((k / 2) % 2);
     return q ^ (2 * ((k / 8) % 2));
+  }
+
+  // Fragment addresses, bytes within an operand slot.
+  // K-contiguous rows (A; the conv's transposed B): a lane reads row
+  // row0 + lane % MF, logical chunk q*(FK/8) + lane/MF of MFMA K step q; the
+  // swizzle depends only on lane % MF, so MFMA tile i adds i*MF rows as an
+  // immediate.
+  static __device__ __forceinline__ uint32_t frag_k_rows(int row0, int lane, int q, bool swizzle = true) {
+    const int r = lane % MF;
+    const int lc = q * (FK / 8) + lane / MF;
+    return uint32_t((row0 + r) * BK * 2 + ((swizzle ? lc ^ swz_a(r) : lc) * 16));
+  }
+  // N-contiguous rows (the GEMM's B), read by the transpose read (4 k-rows x
+  // 16 columns per 16-lane group): source lane s = lane % 16 points at row
+  // kbase + s/4, columns col0 + 4*(s%4) .. +3; K step q adds q*FK rows.
+  static __device__ __forceinline__ uint32_t frag_n_rows(int col0, int lane, bool swizzle = true) {
+    const int g = lane / 16, s = lane % 16;
+    const int krow = MF == 32 ? (g / 2) * 8 + s / 4 : g * 8 + s / 4;
+    const int n = col0 + (MF == 32 ? (g % 2) * 16 + 4 * (s % 4) : 4 * (s % 4));
+    const int lc = n / 8;
+    return uint32_t(krow * BN * 2 + ((swizzle ? lc ^ swz_b(krow) : lc) * 16) + (n % 8) * 2);
   }
 };
 
@@ -580,50 +602,20 @@ __global__ __launch_bounds__(G::THREADS) void tiled_gemm_kernel(KernelArgs p) {
   };
 
   // -- per-lane fragment addresses (bytes within an A or B slot)
-  // A: lane reads row (lane % MF) of each MFMA tile, logical chunk
-  //    q*(FK/8) + lane/MF; the swizzle depends only on lane % MF (rows 16
-  //    apart share it), so MFMA tile i adds i*MF rows as an immediate.
-  uint32_t fa[G::KSUB];
-  {
-    const int r = lane % MF;
-    const int x = G::swz_a(r);
-#pragma unroll
-    for (int q = 0; q < G::KSUB; ++q) {
-      int lc = q * (G::FK / 8) + lane / MF;
-      fa[q] = uint32_t((wr * G::WTM + r) * G::BK * 2 + ((lc ^ x) * 16));
-    }
-  }
-  // B, GEMM (transpose read, 4 k-rows x 16 columns per 16-lane group): source
-  // lane s = lane % 16 points at row kbase + s/4, columns cbase + 4*(s%4) ..
-  // +3; one address per MFMA tile, K step q adds q*FK rows.
+  // A: one address per MFMA K step (MFMA tile i adds i*MF rows).
+  // B, GEMM: one address per MFMA tile (K step q adds q*FK rows).
   // B, conv (pixel rows, K-contiguous): read like A, one address per K step.
+  uint32_t fa[G::KSUB];
+#pragma unroll
+  for (int q = 0; q < G::KSUB; ++q) fa[q] = G::frag_k_rows(wr * G::WTM, lane, q);
   constexpr int NFB = CONV ? G::KSUB : G::TN;
   uint32_t fb[NFB];
   if constexpr (CONV) {
-    const int r = lane % MF;
-    const int x = G::swz_a(r);
 #pragma unroll
-    for (int q = 0; q < G::KSUB; ++q) {
-      int lc = q * (G::FK / 8) + lane / MF;
-      fb[q] = uint32_t((wc * G::WTN + r) * G::BK * 2 + ((lc ^ x) * 16));
-    }
+    for (int q = 0; q < G::KSUB; ++q) fb[q] = G::frag_k_rows(wc * G::WTN, lane, q);
   } else {
-    const int g = lane / 16, s = lane % 16;
-    int krow, ncol;
-    if (MF == 32) {
-      krow = (g / 2) * 8 + s / 4;
-      ncol = (g % 2) * 16 + 4 * (s % 4);
-    } else {
-      krow = g * 8 + s / 4;
-      ncol = 4 * (s % 4);
-    }
-    const int x = G::swz_b(krow);
 #pragma unroll
-    for (int nt = 0; nt < G::TN; ++nt) {
-      int n = wc * G::WTN + nt * MF + ncol;
-      int lc = n / 8;
-      fb[nt] = uint32_t(krow * G::BN * 2 + ((lc ^ x) * 16) + (n % 8) * 2);
-    }
+    for (int nt = 0; nt < G::TN; ++nt) fb[nt] = G::frag_n_rows(wc * G::WTN + nt * MF, lane);
   }
 
   Acc acc[G::TM][G::TN];
