@@ -185,3 +185,13 @@ def test_side_stream_and_errors():
         tss.gemm(A, B, cfg=tss.TileConfig(256, 256, 64, 3, 256, "mfma32"))   # C1 infeasible
     with pytest.raises(tss.TssError):
         tss.gemm(A[:, :60].contiguous(), B[:60].contiguous())                # K % 8
+    with pytest.raises(ValueError):
+        tss.gemm(A, B, out_dtype="f32", out=torch.empty(128, 128))             # output in host memory
+    with pytest.raises(ValueError):
+        tss.gemm(A.double(), B.double())                                      # fp64 operands
+    x = torch.zeros((1, 8, 9, 9), dtype=torch.float16, device=CUDA)
+    w = torch.zeros((8, 8, 3, 3), dtype=torch.float16, device=CUDA)
+    with pytest.raises(ValueError):
+        tss.conv2d(x, w, 1, 1, 1, out_dtype="f32", out=torch.empty(1, 8, 9, 9))
+    with pytest.raises(ValueError):
+        tss.conv2d(x, w, 1, 1, 1, workspace=torch.empty(1 << 20, dtype=torch.uint8))

@@ -172,13 +172,26 @@ _DT = {"f16": C.TSS_F16, "bf16": C.TSS_BF16, "f32": C.TSS_F32}
 
 
 def _dt_of(t) -> str:
-    return {torch.float16: "f16", torch.bfloat16: "bf16", torch.float32: "f32"}[t.dtype]
+    names = {torch.float16: "f16", torch.bfloat16: "bf16", torch.float32: "f32"}
+    if t.dtype not in names:
+        raise ValueError(f"unsupported dtype {t.dtype}")
+    return names[t.dtype]
 
 
 def _stream_ptr(stream) -> Optional[int]:
     if stream is None:
         return torch.cuda.current_stream().cuda_stream
     return getattr(stream, "cuda_stream", stream)
+
+
+def _same_device(*tensors):
+    """Every tensor a device tensor on one GPU; returns that device.  (A host
+    or other-device pointer handed to a kernel would fault.)"""
+    dev = tensors[0].device
+    for t in tensors:
+        if not t.is_cuda or t.device != dev:
+            raise ValueError("every tensor must be on the same GPU")
+    return dev
 
 
 def gemm(A, B, out_dtype: Optional[str] = None, cfg: Optional[TileConfig] = None, out=None, stream=None):
@@ -205,8 +218,9 @@ def gemm(A, B, out_dtype: Optional[str] = None, cfg: Optional[TileConfig] = None
         out = torch.empty(shape, dtype=tdt, device=A.device)
     elif tuple(out.shape) != shape or out.dtype != tdt or not out.is_contiguous():
         raise ValueError("out has the wrong shape, dtype or layout")
-    st = C.lib().tss_gemm(M, N, K, _DT[dt], A.data_ptr(), B.data_ptr(), out.data_ptr(), bt, _DT[od],
-                          ctypes.byref(cfg.c()) if cfg else None, _stream_ptr(stream))
+    with torch.cuda.device(_same_device(A, B, out)):
+        st = C.lib().tss_gemm(M, N, K, _DT[dt], A.data_ptr(), B.data_ptr(), out.data_ptr(), bt, _DT[od],
+                              ctypes.byref(cfg.c()) if cfg else None, _stream_ptr(stream))
     C.check(st, "tss_gemm")
     return out
 
@@ -257,9 +271,10 @@ def conv2d(x, w, stride: Union[int, Sequence[int]] = 1, padding: Union[int, Sequ
     elif not (workspace.is_cuda and workspace.is_contiguous() and workspace.numel() * workspace.element_size()
               >= ws_bytes):
         raise ValueError(f"workspace must be a contiguous device tensor of at least {ws_bytes} bytes")
-    st = C.lib().tss_conv2d_tiled(N, Ci, H, W, Co, kh, kw, sh, sw, ph, pw, dh, dw, tile_n or N, tile_oh or OH,
-                                  tile_ow or OW, _DT[dt], _DT[od], x.data_ptr(), w.data_ptr(), out.data_ptr(),
-                                  workspace.data_ptr(), workspace.numel() * workspace.element_size(),
-                                  ctypes.byref(cfg.c()) if cfg else None, _stream_ptr(stream))
+    with torch.cuda.device(_same_device(x, w, out, workspace)):
+        st = C.lib().tss_conv2d_tiled(N, Ci, H, W, Co, kh, kw, sh, sw, ph, pw, dh, dw, tile_n or N, tile_oh or OH,
+                                      tile_ow or OW, _DT[dt], _DT[od], x.data_ptr(), w.data_ptr(), out.data_ptr(),
+                                      workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                      ctypes.byref(cfg.c()) if cfg else None, _stream_ptr(stream))
     C.check(st, "tss_conv2d_tiled")
     return out
