@@ -75,6 +75,7 @@ int32_t planned_config(int64_t batch, int64_t M, int64_t N, int64_t K, tss_tile_
   if (st != TSS_OK) return st;
   {
     std::lock_guard<std::mutex> g(mu);
+    if (cache.size() >= 4096) cache.clear();  // bounded for long-running callers with many shapes
     cache[key] = best.cfg;
   }
   *out = best.cfg;

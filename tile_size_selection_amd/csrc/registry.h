@@ -7,6 +7,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "gemm_kernel.h"
 
 namespace tss {
@@ -50,11 +52,21 @@ KernelTable table_conv_f16_bm256_wide();
 KernelTable table_conv_bf16_bm128_wide();
 KernelTable table_conv_bf16_bm256_wide();
 
+// Dynamic LDS above 64 KiB needs a per-kernel attribute, which HIP keeps per
+// device: it is set on the first launch on each device (up to 64 devices).
 template <typename G, typename T, bool CONV>
 hipError_t launch_kernel(const KernelArgs &a, dim3 grid, int lds_bytes, hipStream_t s) {
-  static const hipError_t attr = hipFuncSetAttribute((const void *)tiled_gemm_kernel<G, T, CONV>,
-                                                     hipFuncAttributeMaxDynamicSharedMemorySize, 163840);
-  if (attr != hipSuccess) return attr;
+  static std::atomic<uint64_t> attr_set{0};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const uint64_t bit = dev < 64 ? uint64_t(1) << dev : 0;
+  if (!bit || !(attr_set.load(std::memory_order_acquire) & bit)) {
+    e = hipFuncSetAttribute((const void *)tiled_gemm_kernel<G, T, CONV>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            163840);
+    if (e != hipSuccess) return e;
+    attr_set.fetch_or(bit, std::memory_order_acq_rel);
+  }
   hipLaunchKernelGGL((tiled_gemm_kernel<G, T, CONV>), grid, dim3(G::THREADS), lds_bytes, s, a);
   return hipGetLastError();
 }
