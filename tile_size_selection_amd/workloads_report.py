@@ -9,7 +9,9 @@ device.  The launches of n back-to-back calls are captured in one HIP graph
 events on the stream time its replay: the median of 5 replays, divided by n.
 The graph's output is checked against the eager call's, bit for bit.  The
 convolution is the whole tss_conv2d call (operand layout pass + implicit
-GEMM).
+GEMM).  The 4096^3 GEMM is also timed cold: a 512 MB device write before
+every launch evicts its operands from the caches (L2 and the 256 MB cache in
+front of HBM), and HIP events bracket each launch alone (median of 30).
 """
 from __future__ import annotations
 
@@ -64,6 +66,25 @@ def _time_graph(fn, out, n: int, rounds: int) -> float:
     return statistics.median(times)
 
 
+def cold_gemm_us(w, n: int = 30) -> float:
+    A, B = w.make()
+    dA, dB = A.cuda(), B.cuda()
+    C = api.gemm(dA, dB, out_dtype=w.out_dtype)
+    flush = torch.empty(128 * 1024 * 1024, dtype=torch.float32, device="cuda")  # 512 MB
+    times = []
+    for i in range(n + 3):
+        flush.fill_(float(i))
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        api.gemm(dA, dB, out_dtype=w.out_dtype, out=C)
+        e1.record()
+        torch.cuda.synchronize()
+        if i >= 3:
+            times.append(e0.elapsed_time(e1) * 1e3)
+    return statistics.median(times)
+
+
 def run_one(w, rounds: int = 5):
     if isinstance(w, ConvWorkload):
         x, wt = w.make()
@@ -104,6 +125,10 @@ def main(argv=None):
         rows.append(r)
         print(f"{r['name']}: {r['us']:.2f} us, {r['tflops']:.1f} TFLOP/s ({100 * r['frac']:.1f}% of peak),"
               f" tile {r['tile']}", flush=True)
+    cold = cold_gemm_us(WORKLOADS[2])
+    warm = next(r for r in rows if r["name"] == WORKLOADS[2].name)
+    print(f"{WORKLOADS[2].name} cold (512 MB written before each launch): {cold:.2f} us "
+          f"({WORKLOADS[2].flops() / (cold * 1e-6) / 1e12:.1f} TFLOP/s)", flush=True)
     txt = ("# Every workload with the planner's tile\n\n"
            "Command (repository root, MI355X): `python3 -m tile_size_selection_amd.workloads_report"
            + (f" --out {a.out}" if a.out else "") + "`\n\n"
@@ -112,7 +137,10 @@ def main(argv=None):
            " TFLOP/s dense fp16/bf16 MFMA peak.\n\n"
            "| workload | tile | us | TFLOP/s | % of peak |\n|---|---|---|---|---|\n"
            + "\n".join(f"| {r['name']} | {r['tile']} | {r['us']:.2f} | {r['tflops']:.1f} | {100 * r['frac']:.1f} |"
-                       for r in rows) + "\n")
+                       for r in rows) + "\n\n"
+           f"{WORKLOADS[2].name} cold (512 MB written before each launch, one launch per event pair, median of 30):"
+           f" {cold:.2f} us = {WORKLOADS[2].flops() / (cold * 1e-6) / 1e12:.1f} TFLOP/s"
+           f" (warm, graph-timed: {warm['us']:.2f} us)\n")
     print(txt, flush=True)
     if a.out:
         with open(a.out, "w", encoding="utf-8") as f:
