@@ -84,15 +84,9 @@ constexpr uint32_t kOOB = 0x80000000u;  // voffset beyond any accepted buffer ra
 // that frees a stage (measured at 4096^3 and 8192^3: 2 rows ahead of 0 and 1).
 constexpr int kBarrierRows = 2;
 
-// s_waitcnt with vmcnt = n and the other counters left alone (gfx9 encoding:
-// vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] in bits [15:14]).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
-  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
-}
-
-// s_waitcnt vmcnt(n) lgkmcnt(0): the LDS writes of this wave are done too.
+// s_waitcnt vmcnt(n) lgkmcnt(0) (gfx9 encoding: vmcnt[3:0] | expcnt[6:4] |
+// lgkmcnt[11:8] | vmcnt[5:4] in bits [15:14]): at most n copies of this wave
+// still in flight, and its LDS accesses done.
 template <int N>
 __device__ __forceinline__ void wait_vmcnt_lgkm0() {
   static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
