@@ -1,10 +1,20 @@
-"""HBM traffic of the headline GEMM kernel from hardware counters.
+"""Hardware counters of the headline GEMM kernel: HBM traffic, MFMA
+utilisation and LDS bank conflicts.
 
-Two steps, each under its own rocprofv3 run (one counter per pass):
+HBM traffic, two rocprofv3 runs (one counter per pass):
 
     rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir>/fetch -o run -- python3 -m tile_size_selection_amd.counters run
     rocprofv3 --pmc WRITE_SIZE --output-format csv -d <dir>/write -o run -- python3 -m tile_size_selection_amd.counters run
     python3 -m tile_size_selection_amd.counters summarize <dir> [--trace <kernel_stats.csv>] > summary.md
+
+MFMA utilisation and LDS bank conflicts (the rocprofiler derived metrics
+MfmaUtil = sum(SQ_VALU_MFMA_BUSY_CYCLES) / (max(GRBM_GUI_ACTIVE) x SIMDs) and
+LdsBankConflict = conflict cycles per LDS access cycle), for the GEMM and for
+every pattern of the LDS bank table:
+
+    rocprofv3 --pmc MfmaUtil LdsBankConflict SQ_INSTS_LDS --output-format csv -d <dir>/util -o run -- python3 -m tile_size_selection_amd.counters run
+    rocprofv3 --pmc MfmaUtil LdsBankConflict SQ_INSTS_LDS --output-format csv -d <dir>/ldsutil -o run -- python3 -m tile_size_selection_amd.counters run-lds
+    python3 -m tile_size_selection_amd.counters summarize-util <dir> > summary.md
 
 `run` launches a plain elementwise pass over 256 MiB (y = -x: known bytes
 read and written) and then the 4096^3 fp16 GEMM in the configuration the
@@ -54,6 +64,66 @@ def run(launches: int = 5):
     torch.cuda.synchronize()
     cfg = api.default_config(w.M, w.N, w.K)
     print(f"config {cfg.bm}x{cfg.bn}x{cfg.bk}/s{cfg.stages}/t{cfg.threads}/{cfg.instr}", flush=True)
+
+
+def run_lds():
+    """Every pattern of the LDS bank table, one launch each, in table order."""
+    from . import api
+    from .ldsbench import ROWS
+    for p, stride, _ in ROWS:
+        api.lds_probe(p, stride, iters=2000, blocks=256)
+        print(f"lds pattern {p} stride {stride}", flush=True)
+
+
+def per_dispatch_all(csv_path: str):
+    """[(dispatch id, kernel name, {counter: value})] in dispatch order."""
+    acc = defaultdict(lambda: defaultdict(float))
+    names = {}
+    with open(csv_path) as f:
+        for r in csv.DictReader(f):
+            d = int(r["Dispatch_Id"])
+            acc[d][r["Counter_Name"]] += float(r["Counter_Value"])
+            names[d] = r["Kernel_Name"]
+    return [(d, names[d], dict(acc[d])) for d in sorted(acc)]
+
+
+def summarize_util(d: str) -> str:
+    from .ldsbench import ROWS, WHAT
+    util = glob.glob(os.path.join(d, "util", "**", "*counter_collection.csv"), recursive=True)
+    ldsu = glob.glob(os.path.join(d, "ldsutil", "**", "*counter_collection.csv"), recursive=True)
+    if not util or not ldsu:
+        raise SystemExit("counter files missing")
+    gemm = [c for _, k, c in per_dispatch_all(util[0]) if "tiled_gemm_kernel" in k]
+    probes = [c for _, k, c in per_dispatch_all(ldsu[0]) if "lds_probe_kernel" in k]
+    if not gemm or len(probes) != len(ROWS):
+        raise SystemExit(f"expected GEMM dispatches and {len(ROWS)} probe dispatches, got {len(gemm)}, {len(probes)}")
+    mean = lambda key: _mean([c.get(key, float("nan")) for c in gemm])
+    lines = [
+        "# MFMA utilisation and LDS bank conflicts (rocprofv3 derived metrics)",
+        "",
+        "Commands (from the repository root, on the MI355X):",
+        "",
+        "    rocprofv3 --pmc MfmaUtil LdsBankConflict SQ_INSTS_LDS --output-format csv -d <dir>/util -o run -- "
+        "python3 -m tile_size_selection_amd.counters run",
+        "    rocprofv3 --pmc MfmaUtil LdsBankConflict SQ_INSTS_LDS --output-format csv -d <dir>/ldsutil -o run -- "
+        "python3 -m tile_size_selection_amd.counters run-lds",
+        "    python3 -m tile_size_selection_amd.counters summarize-util <dir>",
+        "",
+        "MfmaUtil = sum(SQ_VALU_MFMA_BUSY_CYCLES) / (max(GRBM_GUI_ACTIVE) x SIMDs) x 100;"
+        " LdsBankConflict = SQ_LDS_BANK_CONFLICT / (SQ_LDS_IDX_ACTIVE - SQ_LDS_BANK_CONFLICT), conflict cycles per"
+        " conflict-free LDS access cycle.",
+        "",
+        f"4096^3 fp16 GEMM (planner's tile), mean of {len(gemm)} dispatches: MfmaUtil {mean('MfmaUtil'):.1f} %,"
+        f" LdsBankConflict {mean('LdsBankConflict'):.4f}, SQ_INSTS_LDS {mean('SQ_INSTS_LDS'):.0f}",
+        f"kernel_source_hash: {kernel_source_hash()}",
+        "",
+        "| LDS probe pattern | lane stride (4-byte words) | LdsBankConflict |",
+        "|---|---|---|",
+    ]
+    for (p, stride, _), c in zip(ROWS, probes):
+        st = "—" if p.startswith("gemm") else str(stride)
+        lines.append(f"| {WHAT[p]} | {st} | {c.get('LdsBankConflict', float('nan')):.3f} |")
+    return "\n".join(lines) + "\n"
 
 
 def per_dispatch(csv_path: str, counter: str):
@@ -142,12 +212,19 @@ def main():
     sub = ap.add_subparsers(dest="cmd", required=True)
     r = sub.add_parser("run")
     r.add_argument("--launches", type=int, default=5)
+    sub.add_parser("run-lds")
     s = sub.add_parser("summarize")
     s.add_argument("dir")
     s.add_argument("--trace", default=None)
+    u = sub.add_parser("summarize-util")
+    u.add_argument("dir")
     a = ap.parse_args()
     if a.cmd == "run":
         run(a.launches)
+    elif a.cmd == "run-lds":
+        run_lds()
+    elif a.cmd == "summarize-util":
+        sys.stdout.write(summarize_util(a.dir))
     else:
         sys.stdout.write(summarize(a.dir, a.trace))
     return 0
