@@ -306,7 +306,8 @@ __device__ __forceinline__ void store_tile(const Acc (&acc)[G::TM][G::TN], O *C,
         const i16x8 v = *(const lds_i16x8 *)(area + r * E::PITCH + cc * 16);
         const int row = m0 + wr * G::WTM + i * MF + r;
         const int col = n0 + wc * G::WTN + cc * ELEMS16;
-        if (row < M && col < N) *(i16x8 *)(C + int64_t(row) * N + col) = v;
+        // streaming store: the tile is written once and not read again here
+        if (row < M && col < N) __builtin_nontemporal_store(v, (i16x8 *)(C + int64_t(row) * N + col));
       }
     }
   } else {
