@@ -711,8 +711,14 @@ __global__ __launch_bounds__(G::THREADS) void tiled_gemm_kernel(KernelArgs p) {
             for (int j = b0; j < b1; ++j) read_b(nsb, nq, 1 - PB, j);
 #pragma unroll
             for (int a = a0; a < a1; ++a) read_a(nsa, nq, a);
-            __builtin_amdgcn_sched_group_barrier(0x008, G::TN, 0);                        // the row's MFMAs
-            __builtin_amdgcn_sched_group_barrier(0x100, BREADS * (b1 - b0) + (a1 - a0), 0);  // then its LDS reads
+            // the row's MFMAs with its LDS reads in between, one read after each MFMA
+            constexpr int NRD = BREADS * (b1 - b0) + (a1 - a0);
+            [&]<int... U>(std::integer_sequence<int, U...>) __attribute__((always_inline)) {
+              ((__builtin_amdgcn_sched_group_barrier(0x008, 1, 0),
+                (U < NRD ? __builtin_amdgcn_sched_group_barrier(0x100, 1, 0) : (void)0)),
+               ...);
+            }(std::make_integer_sequence<int, G::TN>{});
+            if constexpr (NRD > G::TN) __builtin_amdgcn_sched_group_barrier(0x100, NRD - G::TN, 0);
           }
           if constexpr (NC > 0) {
             __builtin_amdgcn_sched_barrier(0);
