@@ -143,6 +143,14 @@ def test_k_zero_and_empty_shapes():
     tss.gemm(A, B, out_dtype="f32", out=out)
     torch.cuda.synchronize()
     assert (out == 0).all().item()
+    # K == 0 over several tile rows and columns (and batches): every block's
+    # operand ranges are empty, so C is all zeros
+    A = torch.zeros((2, 300, 0), dtype=torch.float16, device=CUDA)
+    B = torch.zeros((2, 0, 520), dtype=torch.float16, device=CUDA)
+    out = torch.full((2, 300, 520), float("nan"), dtype=torch.float32, device=CUDA)
+    tss.gemm(A, B, out_dtype="f32", out=out)
+    torch.cuda.synchronize()
+    assert (out == 0).all().item()
     # M == 0: nothing launched, nothing written
     A0 = torch.zeros((0, 8), dtype=torch.float16, device=CUDA)
     B0 = torch.ones((8, 8), dtype=torch.float16, device=CUDA)

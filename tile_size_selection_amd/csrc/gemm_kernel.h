@@ -468,7 +468,8 @@ __global__ __launch_bounds__(G::THREADS) void tiled_gemm_kernel(KernelArgs p) {
     rsB4 = buffer_rsrc(p.B, uint32_t(p.Nb) * uint32_t(p.H) * uint32_t(p.W) * uint32_t(p.Cp) * 2u);
   } else {
     const T *Bb = reinterpret_cast<const T *>(p.B) + int64_t(bz) * p.batch_stride_b + n0;
-    rsB4 = buffer_rsrc(Bb, (uint32_t(K) * uint32_t(N) - uint32_t(n0)) * 2u);  // elements [n0, K*N)
+    // elements [n0, K*N); with K == 0 the range is empty (otherwise n0 < N <= K*N)
+    rsB4 = buffer_rsrc(Bb, K > 0 ? (uint32_t(K) * uint32_t(N) - uint32_t(n0)) * 2u : 0u);
   }
 
   // -- A copy plan: wave load j of a stage covers LDS chunks (j*NW+wave)*64 + lane
