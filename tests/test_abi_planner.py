@@ -279,3 +279,31 @@ def test_default_config_is_planner_best():
     for (b, M, N, K) in [(1, 4096, 4096, 4096), (4, 3000, 5000, 2048), (1, 256, 256, 256), (1, 8192, 8192, 8192)]:
         best, _, _ = tss.tile_plan(M, N, K, batch=b)
         assert tss.default_config(M, N, K, batch=b) == best["config"]
+
+
+def test_default_config_cache_under_concurrent_callers():
+    """tss_gemm_default_config from 8 threads at once (ctypes drops the GIL
+    around the call) over more distinct shapes than the plan cache holds, so
+    that it is cleared while other threads read and fill it: every answer is
+    still the uncached planner's best."""
+    import threading
+    rng = np.random.default_rng(5)
+    shapes = sorted({(int(b), int(m), int(n) * 8, int(k) * 8)
+                     for b, m, n, k in zip(rng.integers(1, 5, 6000), rng.integers(1, 9000, 6000),
+                                           rng.integers(1, 1200, 6000), rng.integers(1, 1200, 6000))})
+    assert len(shapes) > 4096
+    want = {s: tss.tile_plan(s[1], s[2], s[3], batch=s[0])[0]["config"] for s in shapes}
+    bad = []
+
+    def worker(part):
+        for s in part:
+            got = tss.default_config(s[1], s[2], s[3], batch=s[0])
+            if got != want[s]:
+                bad.append((s, got, want[s]))
+
+    threads = [threading.Thread(target=worker, args=(shapes[i::8],)) for i in range(8)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not bad, bad[:3]
