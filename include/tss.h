@@ -209,7 +209,10 @@ int32_t tss_tile_plan_usage(int64_t batch, int64_t M, int64_t N, int64_t K, int3
 /* One H-tile of a convolution ("Tiling（分块）" page, H/W tiling formulas):
    output rows [o0, o1) need input rows [in_start, in_end) (in_end exclusive,
    may exceed H), sub-operator pads pt' (top) and pb' (bottom), and share
-   halo rows with the next tile. */
+   halo rows with the next tile.  The slice read from the input is
+   [in_start, min(in_end, H)); it is empty (min(in_end, H) <= in_start) for a
+   tile whose windows lie wholly in the padding, and pt' + (min(in_end, H) -
+   in_start) + pb' is the tile's window span in every case. */
 typedef struct {
   int64_t o0, o1, in_start, in_end, in_span, pt, pb, halo;
 } tss_hw_slice;

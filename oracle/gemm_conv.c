@@ -132,6 +132,7 @@ int oracle_conv2d_htiled(int64_t N, int64_t Ci, int64_t H, int64_t W, int64_t Co
     if (sub_oh != o1 - o0) return -1; /* the slice does not produce the tile's rows */
     double *xs = (double *)calloc((size_t)(N * Ci * HP * WP), sizeof(double));
     if (!xs) return -2;
+    /* rows_in < 0: the tile's windows lie wholly in the padding (empty slice) */
     for (int64_t n = 0; n < N; ++n)
       for (int64_t ci = 0; ci < Ci; ++ci)
         for (int64_t r = 0; r < rows_in; ++r)
@@ -184,7 +185,10 @@ int oracle_conv2d_tiled(int64_t N, int64_t Ci, int64_t H, int64_t W, int64_t Co,
     int64_t nb = n1 - n0;
     double *xs = (double *)calloc((size_t)(nb * Ci * HP * WP), sizeof(double));
     if (!xs) return -2;
-    for (int64_t n = 0; n < nb; ++n)
+    /* A tile whose windows lie wholly in the padding has an empty slice: the
+     * formulas give min(end, size) <= start there (a negative count, which the
+     * pads' sum above still turns into the window span), and nothing is copied. */
+    for (int64_t n = 0; n < nb && cols_in > 0; ++n)
       for (int64_t ci = 0; ci < Ci; ++ci)
         for (int64_t r = 0; r < rows_in; ++r)
           memcpy(xs + ((n * Ci + ci) * HP + ptp + r) * WP + plp,

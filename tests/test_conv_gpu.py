@@ -53,6 +53,11 @@ CASES = [  # N, C, H, W, Co, kh, kw, stride, pad, dil, tile_oh
     # 6x6 outputs, one row per H-tile: groups of 4 pixels that are one aligned
     # run of y, that straddle two images, or that start misaligned
     (3, 16, 12, 12, 24, 3, 3, (2, 2), (1, 1), (1, 1), 1),
+    # pads of 2 at stride 3 (rows) and stride 2 (columns) with 1-tap windows:
+    # the first and last output rows or columns read only padding, so their
+    # tiles' input slices are empty and their outputs are zero
+    (3, 16, 3, 6, 68, 1, 4, (3, 3), (2, 2), (1, 2), 1),
+    (3, 27, 12, 5, 68, 5, 1, (2, 2), (0, 2), (2, 2), 2),
 ]
 
 
@@ -81,6 +86,8 @@ TILINGS = {  # case index in CASES -> (tile_n, tile_oh, tile_ow) triples, ragged
     3: [(1, 5, 3), (2, 7, 2), (1, 15, 1)],
     5: [(1, 1, 1), (2, 2, 2), (1, 3, 1)],
     9: [(2, 1, 4), (1, 6, 5), (3, 4, 6)],
+    10: [(1, 1, 2), (3, 1, 1), (2, 2, 1)],
+    11: [(2, 2, 1), (1, 1, 1), (3, 2, 5)],
 }
 
 

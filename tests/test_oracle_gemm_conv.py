@@ -144,6 +144,11 @@ def test_conv_htiled_equals_direct_bitwise(H, W, k, stride, pad, dil, toh):
     (13, 11, 3, 5, (1, 2), (1, 2), (1, 1), [(1, 3, 2), (2, 13, 1), (3, 1, 6)]),
     (15, 17, 3, 3, (2, 1), (2, 1), (2, 2), [(2, 4, 5), (1, 8, 17), (3, 2, 3)]),
     (11, 12, 2, 3, (3, 2), (0, 1), (1, 2), [(1, 1, 1), (2, 2, 3), (3, 4, 2)]),
+    # pads of 2 at stride 3 with 1-row / 1-column windows: the first and last
+    # output rows and columns read only padding, so their tiles' slices are
+    # empty (the formulas give min(in_end, H) <= in_start)
+    (3, 6, 1, 4, (3, 3), (2, 2), (1, 2), [(1, 1, 1), (3, 1, 2), (2, 2, 1)]),
+    (12, 5, 5, 1, (2, 2), (0, 2), (2, 2), [(1, 2, 1), (3, 1, 1), (2, 2, 5)]),
 ])
 def test_conv_tiled_equals_direct_bitwise(H, W, kh, kw, stride, pad, dil, tilings):
     """Tiles over images, output rows and output columns, the columns taking

@@ -45,11 +45,12 @@ def test_conv_workload_tile_table():
 def test_tiles_cover_every_window_brute_force():
     """For every small (H, kh, sh, pt, d, tile) the slice with pads pt'/pb'
     reproduces each output row's window, row for row, and yields exactly the
-    tile's output rows."""
-    n = 0
-    for Hh, kh, sh, pt, d in itertools.product(range(1, 12), (1, 2, 3, 5), (1, 2, 3), (0, 1, 2), (1, 2)):
-        if pt >= H.window_rows(kh, d):
-            continue
+    tile's output rows.  Pads as tall as the window or taller are included:
+    there a tile's windows can lie wholly in the padding; where the slice is
+    empty (min(in_end, H) <= in_start) every tap is padding, and pt' +
+    (min(in_end, H) - in_start) + pb' is still the window span."""
+    n = n_empty = 0
+    for Hh, kh, sh, pt, d in itertools.product(range(1, 12), (1, 2, 3, 5), (1, 2, 3), (0, 1, 2, 3, 4), (1, 2)):
         OH = H.out_size(Hh, kh, sh, pt, pt, d)
         if OH <= 0:
             continue
@@ -57,8 +58,13 @@ def test_tiles_cover_every_window_brute_force():
             for t in H.tile_table(Hh, kh, sh, pt, d, OH, toh):
                 rows_in = min(t.in_end, Hh) - t.in_start
                 sub_h = t.pt + rows_in + t.pb
+                assert sub_h == (t.o1 - 1 - t.o0) * sh + H.window_rows(kh, d)
                 assert (sub_h - H.window_rows(kh, d)) // sh + 1 == t.o1 - t.o0
                 assert t.in_start - t.pt == t.o0 * sh - pt
+                all_pad = all(not 0 <= o * sh - pt + r * d < Hh for o in range(t.o0, t.o1) for r in range(kh))
+                if rows_in <= 0:                 # an empty slice: every tap is padding
+                    assert all_pad               # (not conversely: dilated taps can straddle slice rows)
+                    n_empty += 1
                 for o in range(t.o0, t.o1):
                     for r in range(kh):
                         full = o * sh - pt + r * d                 # row in the unpadded image (may be pad)
@@ -72,7 +78,7 @@ def test_tiles_cover_every_window_brute_force():
                         want = full if 0 <= full < Hh else None
                         assert src == want
                 n += 1
-    assert n > 2000
+    assert n > 2000 and n_empty > 100
 
 
 def test_halo_sign_and_overlap():

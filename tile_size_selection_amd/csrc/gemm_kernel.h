@@ -452,11 +452,13 @@ __global__ __launch_bounds__(G::THREADS) void tiled_gemm_kernel(KernelArgs p) {
     in_start = max(0, o0 * p.sh - p.ph);                                // (1)
     const int in_end = (o1 - 1) * p.sh - p.ph + (p.kh - 1) * p.dh + 1;  // (2), exclusive
     pt_sub = max(0, p.ph - o0 * p.sh);                                  // (3)
-    rows_in = min(in_end, p.H) - in_start;                              // slice rows; (4) pads the rest
+    // slice rows; (4) pads the rest.  A tile whose windows all lie in the
+    // padding has an empty slice (the formulas give min(in_end, H) <= in_start)
+    rows_in = max(0, min(in_end, p.H) - in_start);
     w_start = max(0, q0 * p.sw - p.pw);
     const int w_end = (q1 - 1) * p.sw - p.pw + (p.kw - 1) * p.dw + 1;
     pl_sub = max(0, p.pw - q0 * p.sw);
-    cols_in = min(w_end, p.W) - w_start;
+    cols_in = max(0, min(w_end, p.W) - w_start);
   }
 
   const T *Ab = reinterpret_cast<const T *>(p.A) + (CONV ? 0 : int64_t(bz) * p.batch_stride_a) + int64_t(m0) * K;
