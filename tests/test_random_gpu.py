@@ -80,3 +80,63 @@ def test_random_conv_geometries_exact():
         if not np.array_equal(to_f64(got), ref):
             bad.append((idx, N, C, H, W, Co, kh, kw, st, pd, dl, toh, tow, tn, dtype))
     assert not bad, bad[:5]
+
+
+def _feasible_configs():
+    from oracle import planner as OP
+    g = OP.device_gfx950()
+    return [tss.TileConfig(c.block_m, c.block_n, c.block_k, c.stages, c.threads, c.instr)
+            for c in OP.candidates(g, 1 << 20, ["mfma32", "mfma16"]) if OP.evaluate(c, g).feasible]
+
+
+def test_every_conv_kernel_exact_on_ragged_tiles():
+    """Every compiled convolution kernel on one geometry that is ragged
+    everywhere (channels, output rows and columns, images, K tiles) and cut
+    into tiles of 1 image x 3 rows x 4 columns: exact for integer inputs."""
+    N, C, H, W, Co, kh, kw, st, pd, dl = 2, 20, 11, 9, 70, 3, 3, (2, 1), (1, 2), (1, 1)
+    x = draw((N, C, H, W), "int", -2, 2, "f16", 501)
+    w = draw((Co, C, kh, kw), "int", -2, 2, "f16", 502)
+    ref, _ = G.conv2d(x.double().numpy(), w.double().numpy(), st, pd, dl)
+    dx, dw = x.to(CUDA), w.to(CUDA)
+    bad = []
+    for cfg in _feasible_configs():
+        y = tss.conv2d(dx, dw, st, pd, dl, tile_oh=3, tile_ow=4, tile_n=1, out_dtype="f32", cfg=cfg)
+        torch.cuda.synchronize()
+        if not np.array_equal(to_f64(y), ref):
+            bad.append(cfg)
+    assert not bad, bad[:4]
+
+
+def test_random_conv_geometries_and_tile_configs_exact():
+    """Wider random geometries (up to 300 channels, 7x7 windows, stride 4,
+    dilation 3, pad 4), each with a random feasible tile configuration."""
+    rng = np.random.default_rng(2026)
+    cfgs = _feasible_configs()
+    bad = []
+    n = 0
+    while n < 40:
+        N, C, Co = int(rng.integers(1, 3)), int(rng.integers(1, 301)), int(rng.integers(1, 140))
+        H, W = int(rng.integers(1, 20)), int(rng.integers(1, 20))
+        kh, kw = int(rng.integers(1, 8)), int(rng.integers(1, 8))
+        st = (int(rng.integers(1, 5)), int(rng.integers(1, 5)))
+        pd = (int(rng.integers(0, 5)), int(rng.integers(0, 5)))
+        dl = (int(rng.integers(1, 4)), int(rng.integers(1, 4)))
+        if H + 2 * pd[0] < (kh - 1) * dl[0] + 1 or W + 2 * pd[1] < (kw - 1) * dl[1] + 1:
+            continue
+        OH = (H + 2 * pd[0] - (kh - 1) * dl[0] - 1) // st[0] + 1
+        OW = (W + 2 * pd[1] - (kw - 1) * dl[1] - 1) // st[1] + 1
+        toh, tow, tn = int(rng.integers(1, OH + 1)), int(rng.integers(1, OW + 1)), int(rng.integers(1, N + 1))
+        cfg = cfgs[int(rng.integers(0, len(cfgs)))]
+        dtype = ["f16", "bf16"][int(rng.integers(0, 2))]
+        case = (N, C, H, W, Co, kh, kw, st, pd, dl, toh, tow, tn, dtype, cfg)
+        print("conv case", n, case, flush=True)
+        x = draw((N, C, H, W), "int", -2, 2, dtype, 600 + n)
+        w = draw((Co, C, kh, kw), "int", -2, 2, dtype, 700 + n)
+        ref, _ = G.conv2d(x.double().numpy(), w.double().numpy(), st, pd, dl)
+        got = tss.conv2d(x.to(CUDA), w.to(CUDA), st, pd, dl, tile_oh=toh, tile_ow=tow, tile_n=tn, out_dtype="f32",
+                         cfg=cfg)
+        torch.cuda.synchronize()
+        if not np.array_equal(to_f64(got), ref):
+            bad.append(case)
+        n += 1
+    assert not bad, bad[:5]
