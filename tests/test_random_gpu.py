@@ -140,3 +140,25 @@ def test_random_conv_geometries_and_tile_configs_exact():
             bad.append(case)
         n += 1
     assert not bad, bad[:5]
+
+
+def test_random_gemm_shapes_and_tile_configs_exact():
+    """Random shapes, each with a random feasible tile configuration, both
+    input dtypes and fp32 output: exact for integer inputs."""
+    rng = np.random.default_rng(2027)
+    cfgs = _feasible_configs()
+    bad = []
+    for n in range(60):
+        bt, M = int(rng.integers(1, 4)), int(rng.integers(1, 600))
+        N, K = 8 * int(rng.integers(1, 80)), 8 * int(rng.integers(1, 70))
+        cfg = cfgs[int(rng.integers(0, len(cfgs)))]
+        dtype = ["f16", "bf16"][int(rng.integers(0, 2))]
+        print("gemm case", n, (bt, M, N, K, dtype, cfg), flush=True)
+        A = draw((bt, M, K), "int", -2, 2, dtype, 800 + n)
+        B = draw((bt, K, N), "int", -2, 2, dtype, 900 + n)
+        ref, _ = G.gemm(A.double().numpy(), B.double().numpy())
+        got = tss.gemm(A.to(CUDA), B.to(CUDA), out_dtype="f32", cfg=cfg)
+        torch.cuda.synchronize()
+        if not np.array_equal(to_f64(got), ref):
+            bad.append((n, bt, M, N, K, dtype, cfg))
+    assert not bad, bad[:5]
