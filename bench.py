@@ -62,9 +62,9 @@ def cpu_baseline(A, B, budget_s: float = 12.0):
     Bd = B.double().numpy()
     K, N = Bd.shape
     t0 = time.perf_counter()
-    G.gemm(Ad[:4], Bd)
+    G.gemm(Ad[:64], Bd)
     dt = max(time.perf_counter() - t0, 1e-6)
-    rows = int(min(A.shape[0], max(4, budget_s / dt * 4)))
+    rows = int(min(A.shape[0], max(64, budget_s / dt * 64)))
     t0 = time.perf_counter()
     G.gemm(Ad[:rows], Bd)
     dt = time.perf_counter() - t0
