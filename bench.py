@@ -71,7 +71,18 @@ def cpu_baseline(A, B, budget_s: float = 12.0):
     flops = 2.0 * rows * N * K
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": G.threads(), "kind": "oracle",
             "sample": f"first {rows} of {A.shape[0]} rows of the 4096^3 problem (C and sum|a*b| in fp64), "
-                      f"{dt:.1f} s wall"}
+                      f"{dt:.1f} s wall on {cpu_model()}"}
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo", encoding="utf-8") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "an unknown CPU"
 
 
 def main():
