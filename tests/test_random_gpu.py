@@ -162,3 +162,43 @@ def test_random_gemm_shapes_and_tile_configs_exact():
         if not np.array_equal(to_f64(got), ref):
             bad.append((n, bt, M, N, K, dtype, cfg))
     assert not bad, bad[:5]
+
+
+def test_random_low_precision_outputs_exact():
+    """fp16 and bf16 outputs on random shapes: with inputs in [-2, 2] and
+    K <= 512 (fp16) or K <= 64 (bf16) every exact result is at most 2048 or
+    256 in magnitude, an integer the output type holds exactly, so the stored
+    value must equal the oracle's; GEMM and convolution, planner's tiles."""
+    rng = np.random.default_rng(2028)
+    bad = []
+    for n in range(40):
+        dtype = ["f16", "bf16"][n % 2]
+        kmax = 512 if dtype == "f16" else 64
+        bt, M = int(rng.integers(1, 3)), int(rng.integers(1, 600))
+        N, K = 8 * int(rng.integers(1, 80)), 8 * int(rng.integers(1, kmax // 8 + 1))
+        A = draw((bt, M, K), "int", -2, 2, dtype, 1100 + n)
+        B = draw((bt, K, N), "int", -2, 2, dtype, 1200 + n)
+        ref, _ = G.gemm(A.double().numpy(), B.double().numpy())
+        got = tss.gemm(A.to(CUDA), B.to(CUDA))
+        torch.cuda.synchronize()
+        assert got.dtype == A.dtype
+        if not np.array_equal(to_f64(got), ref):
+            bad.append(("gemm", n, bt, M, N, K, dtype))
+    for n in range(30):
+        dtype = ["f16", "bf16"][n % 2]
+        N, Co = int(rng.integers(1, 3)), int(rng.integers(1, 100))
+        kh = kw = int(rng.integers(1, 4))
+        C = int(rng.integers(1, (512 if dtype == "f16" else 64) // (kh * kw) + 1))
+        H, W = int(rng.integers(kh, 20)), int(rng.integers(kw, 20))
+        st, pd = int(rng.integers(1, 3)), int(rng.integers(0, 2))
+        OH, OW = (H + 2 * pd - kh) // st + 1, (W + 2 * pd - kw) // st + 1
+        toh, tow = int(rng.integers(1, OH + 1)), int(rng.integers(1, OW + 1))
+        x = draw((N, C, H, W), "int", -2, 2, dtype, 1300 + n)
+        w = draw((Co, C, kh, kw), "int", -2, 2, dtype, 1400 + n)
+        ref, _ = G.conv2d(x.double().numpy(), w.double().numpy(), (st, st), (pd, pd), (1, 1))
+        got = tss.conv2d(x.to(CUDA), w.to(CUDA), st, pd, 1, tile_oh=toh, tile_ow=tow)
+        torch.cuda.synchronize()
+        assert got.dtype == x.dtype
+        if not np.array_equal(to_f64(got), ref):
+            bad.append(("conv", n, N, C, H, W, Co, kh, st, pd, toh, tow, dtype))
+    assert not bad, bad[:5]
