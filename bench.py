@@ -156,7 +156,7 @@ def main():
     conv_us = c0.elapsed_time(c1) / nconv * 1e3
     OH = OW = 28
     conv_flops = 2 * cw.N * cw.Co * OH * OW * cw.C * cw.kh * cw.kw
-    conv_cfg = tss.default_config(cw.Co, cw.N * OH * OW, cw.C * cw.kh * cw.kw)
+    conv_cfg = tss.conv2d_default_config(cw.N, cw.C, cw.H, cw.W, cw.Co, cw.kh, cw.kw, cw.stride, cw.pad, cw.dil)
 
     cfg_str = f"{cfg.bm}x{cfg.bn}x{cfg.bk}/s{cfg.stages}/t{cfg.threads}/{cfg.instr}"
     achieved = flops / (ms_per_step * 1e-3) / 1e12

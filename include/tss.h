@@ -181,6 +181,23 @@ int32_t tss_tile_plan(int64_t batch, int64_t M, int64_t N, int64_t K, int32_t el
                       tss_verdict *list, int32_t cap, int32_t *n_feasible);
 
 /*
+ * The gfx950 plan for a convolution computed as an implicit GEMM ("Tiling（分块）"
+ * page: a convolution is a GEMM with M = output channels, N = output pixels,
+ * K = C * kh * kw).  The kernel pads the channels of each tap to a multiple
+ * of the tile's K step, so a candidate with step BK computes
+ * K = taps * ceil(C / BK) * BK; each candidate is finished (C4, C0) with its
+ * own K, and the first term of the gfx950 ranking (per-tile panel traffic
+ * through the busiest CU) is taken with that K.  Where C is a multiple of 64
+ * (every BK of the space divides it) this is tss_tile_plan with K = taps * C.
+ * Cout: output channels (M); pixels: output pixels of the whole problem (N);
+ * C: input channels; taps: kh * kw.  best, list, cap, n_feasible as for
+ * tss_tile_plan (the verdicts' traffic uses each candidate's own K).
+ * Errors: TSS_E_ARG (C < 1, taps < 1, sizes out of range), TSS_E_INFEASIBLE.
+ */
+int32_t tss_conv_plan(int64_t Cout, int64_t pixels, int64_t C, int64_t taps, int32_t elem_bytes, tss_verdict *best,
+                      tss_verdict *list, int32_t cap, int32_t *n_feasible);
+
+/*
  * The planner with feedback from the compiled kernels.  The tile_decision.py
  * page's C2 counts only the accumulators, and its README lists the register
  * model as a known limitation.  Here each candidate takes what its compiled

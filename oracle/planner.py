@@ -410,6 +410,41 @@ def plan(m: int, n: int, k: int, dev: Optional[DeviceModel] = None, batch: int =
     return (res[0] if res else None), len(res)
 
 
+def conv_k(channels: int, taps: int, block_k: int) -> int:
+    """K of a convolution's implicit GEMM as a tile with K step block_k
+    computes it: each of the taps (kh * kw) runs over the channels padded up
+    to a whole number of K steps."""
+    return taps * _ceil_div(channels, block_k) * block_k
+
+
+def sweep_conv(cout: int, pixels: int, channels: int, taps: int, dev: Optional[DeviceModel] = None,
+               elem_bytes: int = 2) -> List[Verdict]:
+    """The gfx950 sweep for a convolution computed as a GEMM (the Tiling page:
+    M = output channels, N = output pixels, K = channels * kh * kw), where K
+    depends on the candidate: conv_k(channels, taps, block_k).  Each candidate
+    is finished with its own K (C4 does not use K; C0 does), and the first
+    term of the gfx950 rank key, the busiest CU's panel traffic counted in
+    units of K * b, is multiplied by that K before the candidates are
+    compared.  The other terms and the enumeration order are the GEMM
+    sweep's."""
+    dev = dev or device_gfx950()
+    assert dev.ranking != "pages"
+    instrs = [s for s, _ in dev.instr_shapes]
+    keyed = []
+    # conv_k(...) >= block_k for every candidate, so no K step is skipped
+    for cfg in candidates(dev, 1 << 62, instrs):
+        v = evaluate(cfg, dev, elem_bytes=elem_bytes)
+        if not v.feasible:
+            continue
+        k = conv_k(channels, taps, cfg.block_k)
+        finish_parallelism(v, cout, pixels, dev, 1)
+        v.traffic = dram_traffic(cout, pixels, k, cfg, elem_bytes, 1)
+        key = rank_key(v, dev)
+        keyed.append(((key[0] * k,) + tuple(key[1:]), v))
+    keyed.sort(key=lambda kv: kv[0])
+    return [v for _, v in keyed]
+
+
 # ---------------------------------------------------------------------------
 # Text report in the pages' format (used to compare with their printed output)
 # ---------------------------------------------------------------------------

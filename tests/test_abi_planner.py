@@ -307,3 +307,31 @@ def test_default_config_cache_under_concurrent_callers():
     for t in threads:
         t.join()
     assert not bad, bad[:3]
+
+
+@pytest.mark.parametrize("seed", [4, 5])
+def test_conv_plan_bit_exact(seed):
+    """tss_conv_plan against the oracle's sweep_conv, every verdict in rank
+    order (each with its candidate's own padded K), on random convolutions and
+    on the conv workload."""
+    rng = np.random.default_rng(seed)
+    probs = [(256, 6272, 256, 9), (64, 8 * 112 * 112, 3, 9)]
+    probs += [(int(rng.integers(1, 600)), int(rng.integers(1, 20000)), int(rng.integers(1, 300)),
+               int(rng.choice([1, 4, 9, 25, 49]))) for _ in range(6)]
+    for co, px, c, taps in probs:
+        ores = OP.sweep_conv(co, px, c, taps)
+        best, lst, n = tss.conv_plan(co, px, c, taps, cap=len(ores) + 5)
+        assert n == len(ores) == len(lst)
+        for vc, vo in zip(lst, ores):
+            _same(vc, vo)
+        _same(best, ores[0])
+
+
+def test_conv_default_config_is_the_conv_plan():
+    from tile_size_selection_amd.inputs import WORKLOADS
+    cw = WORKLOADS[5]
+    cfg = tss.conv2d_default_config(cw.N, cw.C, cw.H, cw.W, cw.Co, cw.kh, cw.kw, cw.stride, cw.pad, cw.dil)
+    assert cfg == tss.conv_plan(cw.Co, cw.N * 28 * 28, cw.C, cw.kh * cw.kw)[0]["config"]
+    assert cfg == tss.TileConfig(128, 64, 64, 4, 512, "mfma16")
+    with pytest.raises(tss.TssError):
+        tss.conv_plan(64, 100, 0, 9)

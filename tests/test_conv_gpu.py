@@ -17,7 +17,7 @@ CUDA = torch.device("cuda:0")
 def test_conv_workload_full_parity():
     w = WORKLOADS[5]
     x, wt = w.make()
-    cfg = tss.default_config(w.Co, w.N * 28 * 28, w.C * w.kh * w.kw)
+    cfg = tss.conv2d_default_config(w.N, w.C, w.H, w.W, w.Co, w.kh, w.kw, w.stride, w.pad, w.dil)
     print("planner choice for", w.name, cfg, flush=True)
     y = tss.conv2d(x.to(CUDA), wt.to(CUDA), w.stride, w.pad, w.dil, tile_oh=w.tile_oh, out_dtype=w.out_dtype)
     ref, S = G.conv2d(x.double().numpy(), wt.double().numpy(), w.stride, w.pad, w.dil)

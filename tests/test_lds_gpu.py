@@ -38,5 +38,8 @@ def test_gemm_fragment_reads_conflict_free_with_swizzle():
     b, b_plain = _c("gemm_b"), _c("gemm_b_plain")
     print(f"A fragment {a:.2f} (no swizzle {a_plain:.2f}, contiguous b128 {b128:.2f}); "
           f"B fragment {b:.2f} (no swizzle {b_plain:.2f}, contiguous tr {tr:.2f})", flush=True)
-    assert a < 1.25 * b128 and b < 1.25 * tr
+    # a two-way conflict costs about 1.5x (the stride-2 row of the table); the
+    # swizzled reads stay below that, and the same reads without the swizzle
+    # (3-4x) cost more than twice as much
+    assert a < 1.4 * b128 and b < 1.4 * tr
     assert a_plain > 2 * a and b_plain > 2 * b

@@ -252,3 +252,40 @@ def test_pages_register_granule_closed_form():
     assert (v.accum_per_thread, v.regs_per_thread, v.regs_per_block, v.blocks_by_regs) == (8, 8, 1024, 64)
     v = P.evaluate(P.TileConfig(48, 24, 16, 2, 128, "simt"), dev)      # 1152 / 128 = 9 accumulators
     assert (v.accum_per_thread, v.regs_per_thread) == (9, 16)
+
+
+def test_conv_sweep_pins():
+    """The convolution's sweep, where each candidate computes
+    K = taps * ceil(C / BK) * BK (the kernel pads a tap's channels to whole
+    K steps):
+    * K's closed forms (C = 3 and 96 over the gfx950 K steps);
+    * with C a multiple of 64 every K step divides C, K is taps * C for every
+      candidate, and the order is the GEMM sweep's with that K;
+    * of two candidates that differ only in BK, the one that pads less never
+      ranks after the other once its traffic terms are lower (padding is
+      never preferred);
+    * a first-layer convolution (C = 3, 3x3) takes the 16-wide K step (144
+      of K instead of 576)."""
+    assert [P.conv_k(3, 9, bk) for bk in (16, 32, 64)] == [144, 288, 576]
+    assert [P.conv_k(96, 9, bk) for bk in (16, 32, 64)] == [864, 864, 1152]
+    g = P.device_gfx950()
+    ins = [s for s, _ in g.instr_shapes]
+    for co, px, c, taps in [(256, 6272, 256, 9), (128, 3000, 64, 1), (96, 20000, 128, 25)]:
+        conv = [v.config for v in P.sweep_conv(co, px, c, taps)]
+        gemm = [v.config for v in P.sweep(co, px, taps * c, g, ins)]
+        assert conv == gemm
+    res = P.sweep_conv(64, 8 * 112 * 112, 3, 9)
+    pos = {v.config: i for i, v in enumerate(res)}
+    n_pairs = 0
+    for v in res:
+        c = v.config
+        for bk in (16, 32, 64):
+            if bk >= c.block_k:
+                continue
+            other = P.TileConfig(c.block_m, c.block_n, bk, c.stages, c.threads, c.instr)
+            if other in pos:
+                # same tile but the shorter K step: less padding, so less traffic
+                assert res[pos[other]].traffic < v.traffic and pos[other] < pos[c]
+                n_pairs += 1
+    assert n_pairs > 50
+    assert res[0].config.block_k == 16

@@ -57,7 +57,7 @@ class HwSlice(ctypes.Structure):
     _fields_ = [(n, i64) for n in ("o0", "o1", "in_start", "in_end", "in_span", "pt", "pb", "halo")]
 
 
-EXPORTS = ["tss_device_gfx950", "tss_device_pages", "tss_device_query", "tss_evaluate", "tss_tile_plan",
+EXPORTS = ["tss_device_gfx950", "tss_device_pages", "tss_device_query", "tss_evaluate", "tss_tile_plan", "tss_conv_plan",
            "tss_tile_plan_usage", "tss_hw_tile", "tss_gemm", "tss_conv2d", "tss_conv2d_tiled",
            "tss_conv2d_workspace_size", "tss_kernel_available", "tss_kernel_usage_query", "tss_tile_plan_measured",
            "tss_lds_probe", "tss_gemm_default_config", "tss_status_string"]
@@ -80,6 +80,7 @@ def lib():
     L.tss_device_query.argtypes = [i32, P(Device)]
     L.tss_evaluate.argtypes = [P(TileConfig), P(Device), i64, i64, i64, i64, i32, P(Verdict)]
     L.tss_tile_plan.argtypes = [i64, i64, i64, i64, i32, P(Device), i32, P(Verdict), P(Verdict), i32, P(i32)]
+    L.tss_conv_plan.argtypes = [i64, i64, i64, i64, i32, P(Verdict), P(Verdict), i32, P(i32)]
     L.tss_tile_plan_usage.argtypes = [i64, i64, i64, i64, i32, P(MeasuredUsage), i32, P(Verdict), P(Verdict), i32,
                                       P(i32)]
     L.tss_hw_tile.argtypes = [i64, i64, i64, i64, i64, i64, i64, P(HwSlice)]

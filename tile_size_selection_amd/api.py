@@ -94,6 +94,35 @@ def tile_plan(M: int, N: int, K: int, batch: int = 1, elem_bytes: int = 2, dev: 
     return verdict_dict(best), [verdict_dict(lst[i]) for i in range(min(cap, n.value))], n.value
 
 
+def conv_plan(Cout: int, pixels: int, channels: int, taps: int, elem_bytes: int = 2,
+              cap: int = 0) -> Tuple[Optional[dict], List[dict], int]:
+    """tss_conv_plan: the gfx950 plan of a convolution's implicit GEMM (M =
+    Cout, N = output pixels), each candidate with the K its kernel computes,
+    taps * ceil(channels / BK) * BK.  (best or None, first `cap` ranked, n
+    feasible)."""
+    best = C.Verdict()
+    lst = (C.Verdict * max(cap, 1))()
+    n = C.i32(0)
+    st = C.lib().tss_conv_plan(Cout, pixels, channels, taps, elem_bytes, ctypes.byref(best), lst if cap else None,
+                               cap, ctypes.byref(n))
+    return _plan_result(st, best, lst, cap, n, "tss_conv_plan")
+
+
+def conv2d_default_config(N: int, channels: int, H: int, W: int, Cout: int, kh: int, kw: int,
+                          stride: Union[int, Sequence[int]] = 1, padding: Union[int, Sequence[int]] = 0,
+                          dilation: Union[int, Sequence[int]] = 1) -> TileConfig:
+    """The tile conv2d launches when no cfg is given: tss_conv_plan over the
+    whole problem's output pixels."""
+    pair = lambda v: (v, v) if isinstance(v, int) else tuple(v)
+    (sh, sw), (ph, pw), (dh, dw) = pair(stride), pair(padding), pair(dilation)
+    OH = (H + 2 * ph - (kh - 1) * dh - 1) // sh + 1
+    OW = (W + 2 * pw - (kw - 1) * dw - 1) // sw + 1
+    best, _, _ = conv_plan(Cout, N * OH * OW, channels, kh * kw)
+    if best is None:
+        raise RuntimeError("no feasible tile for this convolution")
+    return best["config"]
+
+
 def _plan_result(st, best, lst, cap, n, where):
     if st == C.TSS_E_INFEASIBLE:
         return None, [], 0

@@ -75,7 +75,7 @@ def sweep_conv(iters: int = 20, warmup: int = 3, rounds: int = 2) -> Tuple[List[
     OH = (cw.H + 2 * cw.pad[0] - cw.kh) // cw.stride[0] + 1
     OW = (cw.W + 2 * cw.pad[1] - cw.kw) // cw.stride[1] + 1
     M, N, K = cw.Co, cw.N * OH * OW, cw.C * cw.kh * cw.kw
-    best, ranked, n = api.tile_plan(M, N, K, cap=1024)
+    best, ranked, n = api.conv_plan(cw.Co, N, cw.C, cw.kh * cw.kw, cap=1024)
     x, w = cw.make()
     x, w = x.cuda(), w.cuda()
     y = torch.empty((cw.N, cw.Co, OH, OW), dtype=torch.float32, device="cuda")

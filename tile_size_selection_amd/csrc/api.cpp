@@ -57,11 +57,13 @@ const KernelEntry *find_kernel(const tss_tile_config &c, int32_t dtype, int32_t 
 }
 
 // Planner choice per problem, cached (planning evaluates every candidate).
-int32_t planned_config(int64_t batch, int64_t M, int64_t N, int64_t K, tss_tile_config *out) {
-  using PKey = std::tuple<int64_t, int64_t, int64_t, int64_t>;
+// conv = false: the GEMM (a, b, c, d) = (batch, M, N, K); conv = true: the
+// implicit GEMM of a convolution, (Cout, pixels, C, taps).
+int32_t planned_config(bool conv, int64_t a, int64_t b, int64_t c, int64_t d, tss_tile_config *out) {
+  using PKey = std::tuple<bool, int64_t, int64_t, int64_t, int64_t>;
   static std::mutex mu;
   static std::map<PKey, tss_tile_config> cache;
-  PKey key{batch, M, N, K};
+  PKey key{conv, a, b, c, d};
   {
     std::lock_guard<std::mutex> g(mu);
     auto it = cache.find(key);
@@ -71,7 +73,8 @@ int32_t planned_config(int64_t batch, int64_t M, int64_t N, int64_t K, tss_tile_
     }
   }
   tss_verdict best{};
-  int32_t st = tss_tile_plan(batch, M, N, K, 2, nullptr, 0, &best, nullptr, 0, nullptr);
+  int32_t st = conv ? tss_conv_plan(a, b, c, d, 2, &best, nullptr, 0, nullptr)
+                    : tss_tile_plan(a, b, c, d, 2, nullptr, 0, &best, nullptr, 0, nullptr);
   if (st != TSS_OK) return st;
   {
     std::lock_guard<std::mutex> g(mu);
@@ -194,7 +197,7 @@ int32_t tss_gemm_default_config(int64_t batch, int64_t M, int64_t N, int64_t K, 
                                 tss_tile_config *out) {
   if (!out || batch < 1 || M < 0 || N < 0 || K < 0) return TSS_E_ARG;
   if (dtype != TSS_F16 && dtype != TSS_BF16) return TSS_E_DTYPE;
-  return planned_config(batch, M, N, K, out);
+  return planned_config(false, batch, M, N, K, out);
 }
 
 int32_t tss_gemm(int64_t M, int64_t N, int64_t K, int32_t dtype, const void *A, const void *B, void *C,
@@ -214,7 +217,7 @@ int32_t tss_gemm(int64_t M, int64_t N, int64_t K, int32_t dtype, const void *A, 
     int32_t st = check_config(c);
     if (st != TSS_OK) return st;
   } else {
-    int32_t st = planned_config(batch, M, N, K, &c);
+    int32_t st = planned_config(false, batch, M, N, K, &c);
     if (st != TSS_OK) return st;
   }
   const KernelEntry *e = find_kernel(c, dtype, 0);
@@ -284,9 +287,9 @@ int32_t tss_conv2d_tiled(int64_t N, int64_t C, int64_t H, int64_t W, int64_t Cou
     int32_t st = check_config(c);
     if (st != TSS_OK) return st;
   } else {
-    // The implicit GEMM: M = Cout, N = every output pixel, K = kh*kw*C
-    // (channels rounded up to 8 for the plan; the tile's BK pads them next).
-    int32_t st = planned_config(1, Cout, N * OH * OW, kh * kw * ((C + 7) / 8 * 8), &c);
+    // The implicit GEMM: M = Cout, N = every output pixel, K = kh*kw*C with
+    // the channels padded to the candidate's K step (tss_conv_plan).
+    int32_t st = planned_config(true, Cout, N * OH * OW, C, kh * kw, &c);
     if (st != TSS_OK) return st;
   }
   const KernelEntry *e = find_kernel(c, dtype, 1);

@@ -24,32 +24,53 @@ bool valid_config(const tss_tile_config &c, const tss_device &d) {
 }
 
 
+// K of the problem for a candidate: a plain GEMM's K (the same for every
+// candidate), or the implicit GEMM of a convolution whose channels the kernel
+// pads to a multiple of the candidate's K step: taps * ceil(C / BK) * BK.
+struct FixedK {
+  int64_t K;
+  int64_t operator()(int32_t) const { return K; }
+  static constexpr bool varies = false;
+};
+struct ConvK {
+  int64_t C, taps;
+  int64_t operator()(int32_t bk) const { return taps * ((C + bk - 1) / bk) * bk; }
+  static constexpr bool varies = true;
+};
+
 // The shared sweep: every candidate of the device's space that passes
 // C3/C1/C2/occupancy, finished for the problem and ranked.  usage_of (may be
 // null) gives the compiled kernel's measured usage for a configuration (null
-// to leave the candidate out).
-template <typename UsageOf>
-int32_t plan_sweep(int64_t batch, int64_t M, int64_t N, int64_t K, int32_t elem_bytes, const tss_device &d,
+// to leave the candidate out).  k_of gives each candidate's K; where it
+// varies between candidates, the busiest-CU term of the rank key, which
+// otherwise counts per-tile panel traffic in units of K * b bytes, is scaled
+// by the candidate's own K.
+template <typename UsageOf, typename KOf>
+int32_t plan_sweep(int64_t batch, int64_t M, int64_t N, const KOf &k_of, int32_t elem_bytes, const tss_device &d,
                    int32_t instr_filter, const UsageOf *usage_of, tss_verdict *best, tss_verdict *list, int32_t cap,
                    int32_t *n_feasible) {
+  const int64_t K = k_of(1);
   if (batch < 1 || M < 0 || N < 0 || K < 0 || elem_bytes < 1 || elem_bytes > 8 || cap < 0) return TSS_E_ARG;
   if (M > (int64_t(1) << 40) || N > (int64_t(1) << 40) || K > (int64_t(1) << 40) || batch > (int64_t(1) << 20))
     return TSS_E_ARG;
   if (!valid_device(d)) return TSS_E_ARG;
   if (instr_filter && !instr_on_device(instr_filter, d)) return TSS_E_ARG;
   const Space s = space_for(d, instr_filter);
-  // A K step longer than K is skipped, unless K is shorter than every
-  // candidate step: then the shortest one is kept (its tail is masked).
-  const int64_t bk_cap = K > s.bk[0] ? K : s.bk[0];
   std::vector<tss_verdict> feas;
+  std::vector<int64_t> feas_k;
   feas.reserve(512);
+  feas_k.reserve(512);
   for (int ii = 0; ii < s.ninstr; ++ii) {
     Shape sh{};
     instr_shape(s.instr[ii], sh);
     for (int a = 0; a < s.nbm; ++a)
       for (int b = 0; b < s.nbn; ++b)
         for (int c = 0; c < s.nbk; ++c) {
-          if (s.bk[c] > bk_cap) continue;
+          // A K step longer than K is skipped, unless K is shorter than every
+          // candidate step: then the shortest one is kept (its tail is masked).
+          const int64_t Kc = k_of(s.bk[c]);
+          if (Kc > (int64_t(1) << 40)) return TSS_E_ARG;
+          if (s.bk[c] > (Kc > s.bk[0] ? Kc : s.bk[0])) continue;
           for (int e = 0; e < s.nst; ++e)
             for (int f = 0; f < s.nthr; ++f) {
               if (s.threads[f] % sh.threads) continue;
@@ -64,19 +85,26 @@ int32_t plan_sweep(int64_t batch, int64_t M, int64_t N, int64_t K, int32_t elem_
               }
               tss_verdict v = evaluate_block(cfg, d, elem_bytes, regs, scratch);
               if (v.failures) continue;
-              finish(v, d, batch, M, N, K, elem_bytes);
+              finish(v, d, batch, M, N, Kc, elem_bytes);
               feas.push_back(v);
+              feas_k.push_back(Kc);
             }
         }
   }
-  std::stable_sort(feas.begin(), feas.end(), [&](const tss_verdict &x, const tss_verdict &y) {
-    return key_less(rank_key(x, d), rank_key(y, d));
-  });
+  std::vector<int32_t> order(feas.size());
+  for (size_t i = 0; i < order.size(); ++i) order[i] = int32_t(i);
+  auto key_of = [&](int32_t i) {
+    Key k = rank_key(feas[i], d);
+    if (KOf::varies && d.ranking != TSS_RANK_PAGES) k.k[0] *= feas_k[i];
+    return k;
+  };
+  std::stable_sort(order.begin(), order.end(),
+                   [&](int32_t x, int32_t y) { return key_less(key_of(x), key_of(y)); });
   if (n_feasible) *n_feasible = int32_t(feas.size());
   if (list)
-    for (int32_t i = 0; i < cap && i < int32_t(feas.size()); ++i) list[i] = feas[i];
+    for (int32_t i = 0; i < cap && i < int32_t(feas.size()); ++i) list[i] = feas[order[i]];
   if (feas.empty()) return TSS_E_INFEASIBLE;
-  if (best) *best = feas[0];
+  if (best) *best = feas[order[0]];
   return TSS_OK;
 }
 
@@ -118,7 +146,15 @@ int32_t tss_tile_plan(int64_t batch, int64_t M, int64_t N, int64_t K, int32_t el
                       int32_t instr_filter, tss_verdict *best, tss_verdict *list, int32_t cap,
                       int32_t *n_feasible) {
   const tss_device d = dev ? *dev : gfx950_device();
-  return plan_sweep<NoUsage>(batch, M, N, K, elem_bytes, d, instr_filter, nullptr, best, list, cap, n_feasible);
+  return plan_sweep<NoUsage>(batch, M, N, FixedK{K}, elem_bytes, d, instr_filter, nullptr, best, list, cap,
+                             n_feasible);
+}
+
+int32_t tss_conv_plan(int64_t Cout, int64_t pixels, int64_t C, int64_t taps, int32_t elem_bytes, tss_verdict *best,
+                      tss_verdict *list, int32_t cap, int32_t *n_feasible) {
+  if (C < 1 || taps < 1 || C > (int64_t(1) << 30) || taps > (int64_t(1) << 20)) return TSS_E_ARG;
+  return plan_sweep<NoUsage>(1, Cout, pixels, ConvK{C, taps}, elem_bytes, gfx950_device(), 0, nullptr, best, list,
+                             cap, n_feasible);
 }
 
 int32_t tss_tile_plan_usage(int64_t batch, int64_t M, int64_t N, int64_t K, int32_t elem_bytes,
@@ -136,7 +172,7 @@ int32_t tss_tile_plan_usage(int64_t batch, int64_t M, int64_t N, int64_t K, int3
     }
     return nullptr;
   };
-  return plan_sweep(batch, M, N, K, elem_bytes, gfx950_device(), 0, &usage_of, best, list, cap, n_feasible);
+  return plan_sweep(batch, M, N, FixedK{K}, elem_bytes, gfx950_device(), 0, &usage_of, best, list, cap, n_feasible);
 }
 
 int32_t tss_hw_tile(int64_t H, int64_t kh, int64_t sh, int64_t pt, int64_t d, int64_t o0, int64_t o1,

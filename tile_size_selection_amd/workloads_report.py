@@ -94,7 +94,7 @@ def run_one(w, rounds: int = 5):
         y = api.conv2d(dx, dw, w.stride, w.pad, w.dil, tile_oh=w.tile_oh, out_dtype=w.out_dtype, workspace=ws)
         OH, OW = y.shape[2], y.shape[3]
         flops = 2 * w.N * w.Co * OH * OW * w.C * w.kh * w.kw
-        cfg = api.default_config(w.Co, w.N * OH * OW, w.C * w.kh * w.kw)
+        cfg = api.conv2d_default_config(w.N, w.C, w.H, w.W, w.Co, w.kh, w.kw, w.stride, w.pad, w.dil)
         out = y
         fn = lambda: api.conv2d(dx, dw, w.stride, w.pad, w.dil, tile_oh=w.tile_oh, out_dtype=w.out_dtype,
                                 workspace=ws, out=y)
