@@ -187,8 +187,11 @@ int32_t tss_tile_plan(int64_t batch, int64_t M, int64_t N, int64_t K, int32_t el
  * of the tile's K step, so a candidate with step BK computes
  * K = taps * ceil(C / BK) * BK; each candidate is finished (C4, C0) with its
  * own K, and the first term of the gfx950 ranking (per-tile panel traffic
- * through the busiest CU) is taken with that K.  Where C is a multiple of 64
- * (every BK of the space divides it) this is tss_tile_plan with K = taps * C.
+ * through the busiest CU) is taken with that K's loop cost, K + 22 * K / BK
+ * (each K step costs about 22 K elements' worth beyond its BK, as measured
+ * for this kernel), so a shorter K step is chosen only where the padding it
+ * saves outweighs the steps it adds.  Where C is a multiple of 64 every BK
+ * gives K = taps * C.
  * Cout: output channels (M); pixels: output pixels of the whole problem (N);
  * C: input channels; taps: kh * kw.  best, list, cap, n_feasible as for
  * tss_tile_plan (the verdicts' traffic uses each candidate's own K).

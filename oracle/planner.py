@@ -410,6 +410,13 @@ def plan(m: int, n: int, k: int, dev: Optional[DeviceModel] = None, batch: int =
     return (res[0] if res else None), len(res)
 
 
+# The gfx950 kernel's cost per K step in K elements is about BK + 22: the
+# barrier, the waits and the fragment pipeline's restart cost as much as 22
+# more elements of work (measured: at equal K the 32- and 16-wide steps of the
+# conv workload take 1.24x and 1.76x the 64-wide step's time per FLOP).
+STEP_OVERHEAD_K = 22
+
+
 def conv_k(channels: int, taps: int, block_k: int) -> int:
     """K of a convolution's implicit GEMM as a tile with K step block_k
     computes it: each of the taps (kh * kw) runs over the channels padded up
@@ -424,9 +431,9 @@ def sweep_conv(cout: int, pixels: int, channels: int, taps: int, dev: Optional[D
     depends on the candidate: conv_k(channels, taps, block_k).  Each candidate
     is finished with its own K (C4 does not use K; C0 does), and the first
     term of the gfx950 rank key, the busiest CU's panel traffic counted in
-    units of K * b, is multiplied by that K before the candidates are
-    compared.  The other terms and the enumeration order are the GEMM
-    sweep's."""
+    units of K * b, is multiplied by the K loop's cost, K + STEP_OVERHEAD_K
+    per K step, before the candidates are compared.  The other terms and the
+    enumeration order are the GEMM sweep's."""
     dev = dev or device_gfx950()
     assert dev.ranking != "pages"
     instrs = [s for s, _ in dev.instr_shapes]
@@ -440,7 +447,7 @@ def sweep_conv(cout: int, pixels: int, channels: int, taps: int, dev: Optional[D
         finish_parallelism(v, cout, pixels, dev, 1)
         v.traffic = dram_traffic(cout, pixels, k, cfg, elem_bytes, 1)
         key = rank_key(v, dev)
-        keyed.append(((key[0] * k,) + tuple(key[1:]), v))
+        keyed.append(((key[0] * (k + STEP_OVERHEAD_K * (k // cfg.block_k)),) + tuple(key[1:]), v))
     keyed.sort(key=lambda kv: kv[0])
     return [v for _, v in keyed]
 

@@ -38,13 +38,22 @@ struct ConvK {
   static constexpr bool varies = true;
 };
 
+// Cost of a tile's K loop in units of K elements: each K step of BK elements
+// costs about BK + kStepOverheadK (the barrier, the waits and the restart of
+// the fragment pipeline; fitted to the conv workload's measured sweep, where
+// the 32- and 16-wide steps take 1.24x and 1.76x the 64-wide step's time per
+// FLOP at equal K).  Used where K depends on BK (the convolution), so that a
+// shorter step is taken only when the channel padding it saves outweighs the
+// steps it adds.
+constexpr int64_t kStepOverheadK = 22;
+
 // The shared sweep: every candidate of the device's space that passes
 // C3/C1/C2/occupancy, finished for the problem and ranked.  usage_of (may be
 // null) gives the compiled kernel's measured usage for a configuration (null
 // to leave the candidate out).  k_of gives each candidate's K; where it
 // varies between candidates, the busiest-CU term of the rank key, which
 // otherwise counts per-tile panel traffic in units of K * b bytes, is scaled
-// by the candidate's own K.
+// by the candidate's K-loop cost, K + kStepOverheadK * (K / BK).
 template <typename UsageOf, typename KOf>
 int32_t plan_sweep(int64_t batch, int64_t M, int64_t N, const KOf &k_of, int32_t elem_bytes, const tss_device &d,
                    int32_t instr_filter, const UsageOf *usage_of, tss_verdict *best, tss_verdict *list, int32_t cap,
@@ -95,7 +104,8 @@ int32_t plan_sweep(int64_t batch, int64_t M, int64_t N, const KOf &k_of, int32_t
   for (size_t i = 0; i < order.size(); ++i) order[i] = int32_t(i);
   auto key_of = [&](int32_t i) {
     Key k = rank_key(feas[i], d);
-    if (KOf::varies && d.ranking != TSS_RANK_PAGES) k.k[0] *= feas_k[i];
+    if (KOf::varies && d.ranking != TSS_RANK_PAGES)
+      k.k[0] *= feas_k[i] + kStepOverheadK * (feas_k[i] / feas[i].cfg.bk);
     return k;
   };
   std::stable_sort(order.begin(), order.end(),
