@@ -275,8 +275,9 @@ int32_t tss_gemm(int64_t M, int64_t N, int64_t K, int32_t dtype, const void *A, 
  * its contents are scratch and are overwritten on every call (calls that
  * share a workspace must be ordered on one stream).
  * dtype TSS_F16 / TSS_BF16, fp32 accumulation, out_dtype TSS_F32 or dtype.
- * tile_oh in [1, OH]; cfg NULL = planner's choice for the GEMM
- * (Cout x N*OH*OW x kh*kw*Cp).  x, w, y 16-byte aligned.
+ * tile_oh in [1, OH]; cfg NULL = tss_conv_plan's choice for the implicit
+ * GEMM (Cout x N*OH*OW, K = kh*kw*C with C padded to each candidate's K
+ * step).  x, w, y 16-byte aligned.
  * Errors: TSS_E_ARG (also for a missing or too small workspace), TSS_E_DTYPE,
  * TSS_E_ALIGN, TSS_E_INFEASIBLE, TSS_E_UNSUPPORTED, TSS_E_HIP.
  */
@@ -299,8 +300,8 @@ int32_t tss_conv2d(int64_t N, int64_t C, int64_t H, int64_t W, int64_t Cout, int
  * the same cfg.
  * tile_n in [1, N], tile_oh in [1, OH], tile_ow in [1, OW], and
  * tile_n * tile_oh * tile_ow < 2^31.  Everything else as tss_conv2d (one
- * GEMM batch entry per tile; cfg NULL = the planner's choice for the whole
- * Cout x N*OH*OW x kh*kw*Cp GEMM).
+ * GEMM batch entry per tile; cfg NULL = tss_conv_plan's choice for the
+ * whole problem, Cout x N*OH*OW).
  * Errors: as tss_conv2d.
  */
 int32_t tss_conv2d_tiled(int64_t N, int64_t C, int64_t H, int64_t W, int64_t Cout, int64_t kh,
