@@ -8,9 +8,12 @@ the tile decision (the planner's choice, cached per shape after its first
 evaluation) and the tiled GEMM kernel it selects, launched through the C ABI
 on the current stream.  Prints one JSON line.
 
+Warm-up runs at least `warmup` launches and at least one second of GPU work.
 The timed region holds exactly `steps` launches, bracketed by
 torch.cuda.synchronize(); HIP events recorded on the launch stream give the
-average kernel duration the roofline figure uses.  Beside it: the convolution
+average kernel duration the roofline figure uses.  The launches are queued
+behind a GPU-side spin so that the interval between the events is the
+kernels running back to back, not the host's per-call cost.  Beside it: the convolution
 workload (8x256x56x56, 3x3, stride 2, pad 1, H-tiles of 8 output rows) timed
 the same way, and the oracle timed on the host cores on a bounded sample.
 """
@@ -85,6 +88,48 @@ def cpu_model() -> str:
     return "an unknown CPU"
 
 
+def warm_up(launch, n_min: int, min_s: float = 1.0):
+    """At least n_min launches and at least min_s seconds of GPU work (the
+    engine clock settles under sustained load, not in a few launches).
+    Returns the launches made and the host's enqueue cost per launch (us)."""
+    import torch
+    n, t0 = 0, time.perf_counter()
+    enq_s, enq_n = 0.0, 0
+    while n < n_min or time.perf_counter() - t0 < min_s:
+        t1 = time.perf_counter()
+        for _ in range(20):
+            launch()
+        enq_s += time.perf_counter() - t1
+        enq_n += 20
+        n += 20
+        torch.cuda.synchronize()
+    return n, enq_s / enq_n * 1e6
+
+
+def timed(launch, steps: int, host_us: float, stream):
+    """Exactly `steps` launches between two HIP events on the launch stream.
+    The launches are queued behind a GPU-side spin long enough for the host
+    to enqueue all of them, so the events see the kernels run back to back
+    rather than the host's per-call cost (Python marshalling of the call);
+    the spin itself lies before the first event.  Returns (ms per step,
+    wall seconds of the bracketed region, spin cycles)."""
+    import torch
+    torch.cuda.synchronize()
+    spin_us = min(max(2000.0, 1.5 * steps * host_us), 2.0e6)
+    cycles = int(spin_us * 2400)          # at most 2.4 GHz: the spin lasts at least spin_us
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    torch.cuda._sleep(cycles)
+    e0.record(stream)
+    for _ in range(steps):
+        launch()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return e0.elapsed_time(e1) / steps, wall, cycles
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -108,23 +153,11 @@ def main():
     cfg = tss.default_config(w.M, w.N, w.K, w.batch, w.dtype)
     stream = torch.cuda.current_stream()
 
-    # warm-up (also brings the clocks up)
-    for _ in range(args.warmup):
-        tss.gemm(dA, dB, out=out)
-    torch.cuda.synchronize()
-
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    e0.record(stream)
-    for _ in range(args.steps):
+    def launch():
         tss.gemm(dA, dB, out=out)          # planner choice (cached) + kernel
-    e1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ev_ms = e0.elapsed_time(e1)
-    ms_per_step = ev_ms / args.steps
+
+    warm_n, host_us = warm_up(launch, args.warmup)
+    ms_per_step, wall, _ = timed(launch, args.steps, host_us, stream)
     flops = w.flops()
     tflops = flops / (ms_per_step * 1e-3) / 1e12
 
@@ -142,18 +175,16 @@ def main():
     x, wt = cw.make()
     dx, dwt = x.to("cuda:0"), wt.to("cuda:0")
     y = tss.conv2d(dx, dwt, cw.stride, cw.pad, cw.dil, tile_oh=cw.tile_oh, out_dtype=cw.out_dtype)
-    for _ in range(10):
-        tss.conv2d(dx, dwt, cw.stride, cw.pad, cw.dil, tile_oh=cw.tile_oh, out_dtype=cw.out_dtype, out=y)
-    torch.cuda.synchronize()
-    c0 = torch.cuda.Event(enable_timing=True)
-    c1 = torch.cuda.Event(enable_timing=True)
-    nconv = 100
-    c0.record(stream)
-    for _ in range(nconv):
-        tss.conv2d(dx, dwt, cw.stride, cw.pad, cw.dil, tile_oh=cw.tile_oh, out_dtype=cw.out_dtype, out=y)
-    c1.record(stream)
-    torch.cuda.synchronize()
-    conv_us = c0.elapsed_time(c1) / nconv * 1e3
+    ws = torch.empty(tss.conv2d_workspace_size(cw.N, cw.C, cw.H, cw.W, cw.Co, cw.kh, cw.kw), dtype=torch.uint8,
+                     device="cuda:0")
+
+    def launch_conv():
+        tss.conv2d(dx, dwt, cw.stride, cw.pad, cw.dil, tile_oh=cw.tile_oh, out_dtype=cw.out_dtype, out=y,
+                   workspace=ws)
+
+    _, conv_host_us = warm_up(launch_conv, 10, min_s=0.2)
+    conv_ms, _, _ = timed(launch_conv, 200, conv_host_us, stream)
+    conv_us = conv_ms * 1e3
     OH = OW = 28
     conv_flops = 2 * cw.N * cw.Co * OH * OW * cw.C * cw.kh * cw.kw
     conv_cfg = tss.conv2d_default_config(cw.N, cw.C, cw.H, cw.W, cw.Co, cw.kh, cw.kw, cw.stride, cw.pad, cw.dil)
@@ -177,6 +208,11 @@ def main():
                                "(seeds 2000/2001), fp32 accumulation, fp16 output",
                    "tile": cfg_str, "parallelism": "single GPU", "wall_s": round(wall, 4),
                    "sampled_parity_ok": parity_ok},
+        "timing": {"warmup_launches": warm_n, "timed_launches": args.steps,
+                   "host_enqueue_us_per_call": round(host_us, 2),
+                   "method": "HIP events on the launch stream around the timed launches, queued behind a "
+                             "GPU-side spin so that the host's per-call cost is not in the interval; warm-up "
+                             "runs at least --warmup launches and at least 1 s of GPU work"},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_F16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_F16_TFLOPS, 4),
                      "traffic": profiled_traffic(cfg_str)},

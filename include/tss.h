@@ -94,6 +94,20 @@ typedef struct {
   int32_t wave_grid_rule;         /* 1: block must split into whole MFMA tiles per wave */
   int32_t load_bytes_per_lane;    /* >0: each wave issues whole 64-lane loads per stage */
   int32_t ranking;                /* TSS_RANK_* */
+  /* Cost parameters of the gfx950 ranking (ignored by the pages' ranking),
+     in units of K elements of one tile's K loop:
+     step_cost_k: what one K step costs beyond its BK elements of work (the
+       barrier, the waits, the restart of the fragment pipeline); a tile's
+       K loop of n steps of BK costs n * (BK + step_cost_k).  gfx950 model:
+       22, the value at which a fixed per-step cost reproduces the measured
+       time per FLOP of the 32- and 16-wide K steps relative to the 64-wide
+       step at equal K (1.24x and 1.76x, convolution workload).  0 turns the
+       term off: the loop then costs its padded K alone.
+     tile_cost_k: the fixed cost of one round of co-resident tiles on a CU
+       (prologue, epilogue, output write), as a K-loop length of the same
+       tile.  0 turns it off. */
+  int32_t step_cost_k;
+  int32_t tile_cost_k;
 } tss_device;
 
 /* One tile configuration (block tile BM x BN, K step BK, pipeline stages,
@@ -131,6 +145,11 @@ typedef struct {
   int32_t pad_;
 } tss_verdict;
 
+/* The multiples an instruction shape imposes (C3): out[0..3] = block M, block
+   N and block K multiples and the thread-count multiple (the lanes that issue
+   it).  Errors: TSS_E_ARG (out NULL, unknown instr). */
+int32_t tss_instr_shape(int32_t instr, int32_t out[4]);
+
 /* The MI355X (gfx950) model: 256 CUs, 160 KiB LDS per CU and per block,
    wave64, 4 SIMDs x 8 waves, 512-deep unified VGPR file (256 accumulation
    registers), 32 blocks per CU.  out: non-null. */
@@ -166,14 +185,20 @@ int32_t tss_evaluate(const tss_tile_config *cfg, const tss_device *dev, int64_t 
  *   gfx950 model: BM, BN in {256, 128, 64} (largest first), BK in
  *                 {16, 32, 64}, stages 2..4, threads {128, 256, 512}, both
  *                 MFMA shapes, 16x16x32 first (or the one in instr_filter);
- *                 key (ceil(grid / CUs) * (BM + BN), round(traffic), -BK,
- *                 -u, -u * waves/block, -stages, LDS bytes) with
- *                 u = min(blocks/CU, ceil(grid / CUs)), the blocks a CU can
- *                 actually hold: the first term is the C0 panel traffic of
- *                 the busiest CU.
+ *                 key (T, round(traffic), -BK, -u, -u * waves/block,
+ *                 -stages, LDS bytes).  T is the busiest CU's time in units
+ *                 of streamed panel elements: with W = ceil(grid / CUs)
+ *                 tiles on that CU, u = min(blocks/CU, W) of them resident
+ *                 at once (R = ceil(W / u) rounds) and n = ceil(K / BK) K
+ *                 steps per tile,
+ *                   T = W * (BM + BN) * n * (BK + dev->step_cost_k)
+ *                     + R * (BM + BN) * dev->tile_cost_k.
  * instr_filter: 0 = every shape of the device, else one TSS_INSTR_*.
  * best (nullable) receives the top verdict; list (nullable) the first
  * min(cap, n) verdicts in rank order; *n_feasible (nullable) the count.
+ * Sizes: batch in [1, 2^20], M, N, K in [0, 2^40], batch * M * N <= 2^62
+ * (TSS_E_ARG otherwise); traffic_rounded saturates at 2^64 - 1 (the exact
+ * value stays in traffic_num / traffic_den and ranks the candidates).
  * Returns TSS_E_INFEASIBLE when nothing is feasible (best then untouched).
  */
 int32_t tss_tile_plan(int64_t batch, int64_t M, int64_t N, int64_t K, int32_t elem_bytes,
@@ -185,20 +210,22 @@ int32_t tss_tile_plan(int64_t batch, int64_t M, int64_t N, int64_t K, int32_t el
  * page: a convolution is a GEMM with M = output channels, N = output pixels,
  * K = C * kh * kw).  The kernel pads the channels of each tap to a multiple
  * of the tile's K step, so a candidate with step BK computes
- * K = taps * ceil(C / BK) * BK; each candidate is finished (C4, C0) with its
- * own K, and the first term of the gfx950 ranking (per-tile panel traffic
- * through the busiest CU) is taken with that K's loop cost, K + 22 * K / BK
- * (each K step costs about 22 K elements' worth beyond its BK, as measured
- * for this kernel), so a shorter K step is chosen only where the padding it
- * saves outweighs the steps it adds.  Where C is a multiple of 64 every BK
+ * K = taps * ceil(C / BK) * BK; each candidate is finished (C4, C0) and
+ * ranked (tss_tile_plan's gfx950 key) with its own K.  With the step cost
+ * (dev->step_cost_k) a shorter K step is chosen only where the padding it
+ * saves outweighs the steps it adds; with step_cost_k = 0 a candidate's K
+ * loop costs its padded K alone.  Where C is a multiple of 64 every BK
  * gives K = taps * C.
  * Cout: output channels (M); pixels: output pixels of the whole problem (N);
- * C: input channels; taps: kh * kw.  best, list, cap, n_feasible as for
+ * C: input channels; taps: kh * kw; dev: a device with the gfx950 ranking
+ * (NULL = tss_device_gfx950).  best, list, cap, n_feasible as for
  * tss_tile_plan (the verdicts' traffic uses each candidate's own K).
- * Errors: TSS_E_ARG (C < 1, taps < 1, sizes out of range), TSS_E_INFEASIBLE.
+ * Errors: TSS_E_ARG (C < 1, taps < 1, sizes out of range, dev not ranked
+ * the gfx950 way), TSS_E_INFEASIBLE.
  */
-int32_t tss_conv_plan(int64_t Cout, int64_t pixels, int64_t C, int64_t taps, int32_t elem_bytes, tss_verdict *best,
-                      tss_verdict *list, int32_t cap, int32_t *n_feasible);
+int32_t tss_conv_plan(int64_t Cout, int64_t pixels, int64_t C, int64_t taps, int32_t elem_bytes,
+                      const tss_device *dev, tss_verdict *best, tss_verdict *list, int32_t cap,
+                      int32_t *n_feasible);
 
 /*
  * The planner with feedback from the compiled kernels.  The tile_decision.py

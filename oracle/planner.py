@@ -64,6 +64,11 @@ class DeviceModel:
     wave_grid_rule: bool = False    # gfx950: block splits into whole MFMA tiles per wave
     load_bytes_per_lane: int = 0    # gfx950: operand tiles are whole wave-wide loads
     ranking: str = "pages"
+    # cost parameters of the gfx950 ranking, in K elements of a tile's K loop
+    # (see busiest_core_time); the pages' ranking does not use them
+    step_cost_k: int = 0            # a K step's cost beyond its BK elements
+    tile_cost_k: int = 0            # a round of co-resident tiles' fixed cost
+    core_name: str = "SM"           # how messages name a core
 
     def shape(self, instr: str) -> Tuple[int, int, int, int]:
         for k, v in self.instr_shapes:
@@ -101,6 +106,17 @@ def device_pages(sm_count: int = 132, smem_kb: int = 228) -> DeviceModel:
         instr_shapes=NVIDIA_SHAPES, ranking="pages")
 
 
+# The gfx950 model's cost parameters.  They are properties of the kernels
+# (measured), not of the pages: a K step costs about 22 K elements beyond its
+# BK (with that fixed cost per step, the 32- and 16-wide steps take 1.24x and
+# 1.76x the 64-wide step's time per FLOP at equal K, as measured on the
+# convolution workload); the per-round fixed cost is left at zero.  The
+# functions below take them from the device record, so any other values can
+# be given through dataclasses.replace.
+GFX950_STEP_COST_K = 22
+GFX950_TILE_COST_K = 0
+
+
 def device_gfx950() -> DeviceModel:
     """MI355X (gfx950).  Values confirmed on the device through hipDeviceProp_t:
     256 CUs, 163840 B LDS per CU and per block, 2048 threads per CU, 1024 per
@@ -115,7 +131,8 @@ def device_gfx950() -> DeviceModel:
         lane_count=64, reg_granule_per_lane=8, acc_regs_max=256, reg_overhead=32,
         reg_model=REG_PER_SIMD, simds_per_core=4, regs_per_lane_per_simd=512,
         max_waves_per_simd=8, instr_shapes=GFX950_SHAPES,
-        wave_grid_rule=True, load_bytes_per_lane=16, ranking="gfx950")
+        wave_grid_rule=True, load_bytes_per_lane=16, ranking="gfx950",
+        step_cost_k=GFX950_STEP_COST_K, tile_cost_k=GFX950_TILE_COST_K, core_name="CU")
 
 
 # Wave grids (rows x cols of waves) a block of n waves is split into.
@@ -152,6 +169,7 @@ class Verdict:
     waves: int = 0
     fill: Fraction = Fraction(0)
     traffic: Fraction = Fraction(0)
+    k_loop: int = 0                                     # the K the candidate's loop runs over
     failures: List[str] = field(default_factory=list)   # constraint codes, in check order
     messages: List[str] = field(default_factory=list)   # human-readable FAIL text
     warnings: List[str] = field(default_factory=list)   # C4 codes: "tail", "idle"
@@ -204,7 +222,7 @@ def evaluate(cfg: TileConfig, dev: DeviceModel, elem_bytes: int = 2, accum_bytes
         if grid is None or bm % (grid[0] * im) or bn % (grid[1] * inn):
             v.failures.append("C3_WAVEGRID")
             v.messages.append(f"C3 block ({bm},{bn}) does not split into whole {im}x{inn} tiles"
-                              f" over a {grid} wave grid")
+                              f" per wave for {thr // dev.lane_count} waves")
     if dev.load_bytes_per_lane:
         # every wave of the block copies the same whole number of wave-wide
         # loads (load_bytes_per_lane per lane) of each operand tile per stage
@@ -281,7 +299,8 @@ def finish_parallelism(v: Verdict, m: int, n: int, dev: DeviceModel, batch: int 
                            f"({v.grid} tiles / {resident} resident): tail effect")
     if v.grid < dev.cores:
         v.warnings.append("idle")
-        v.warn_text.append(f"C4 only {v.grid} tiles for {dev.cores} SMs: more than half the machine is idle")
+        v.warn_text.append(f"C4 only {v.grid} tiles for {dev.cores} {dev.core_name}s: more than half the machine"
+                           f" is idle")
     return v
 
 
@@ -321,29 +340,46 @@ GFX950_SPACE = dict(bm=(256, 128, 64), bn=(256, 128, 64), bk=(16, 32, 64),
                     stages=(2, 3, 4), threads=(128, 256, 512))
 
 
-def busiest_core_traffic(v: Verdict, dev: DeviceModel) -> int:
-    """C0's per-tile traffic (BM + BN) * K * b, times the number of tiles the
-    busiest SM/CU streams once C4 has dealt the grid out in waves over the
-    cores: ceil(grid / cores) * (BM + BN), in units of K * b bytes.  Every
-    candidate tile's intensity 2*BM*BN / ((BM + BN) * b) (Tiling page) is below
-    the device's ridge (gfx950: 2516.6 TFLOP/s over 8 TB/s, about 315 FLOP/B),
-    so this is the time the busiest core needs."""
+def busiest_core_time(v: Verdict, dev: DeviceModel, k_loop: Optional[int] = None) -> int:
+    """The time the busiest CU needs, in units of streamed panel elements,
+    for a finished gfx950 candidate whose K loop runs over k_loop elements.
+
+    C4 deals the grid out over the cores, so the busiest one gets
+    W = ceil(grid / cores) tiles, of which at most u = min(blocks_per_core, W)
+    are resident at once: R = ceil(W / u) rounds.  Each tile streams the C0
+    panels of its K loop, BM + BN elements per K element, over
+    n = ceil(k_loop / BK) steps that cost BK + step_cost_k each, and each
+    round pays tile_cost_k more K elements' worth of its panels:
+
+        T = W * (BM + BN) * n * (BK + step_cost_k) + R * (BM + BN) * tile_cost_k
+
+    Every candidate tile's intensity 2*BM*BN / ((BM + BN) * b) (Tiling page)
+    is below the device ridge (gfx950: 2516.6 TFLOP/s over 8 TB/s, about 315
+    FLOP/B), which is why streamed panel elements measure time."""
     c = v.config
-    return _ceil_div(v.grid, dev.cores) * (c.block_m + c.block_n)
+    k = v.k_loop if k_loop is None else k_loop
+    w = _ceil_div(v.grid, dev.cores)
+    if w == 0:
+        return 0
+    u = min(v.blocks_per_core, w)
+    rounds = _ceil_div(w, max(u, 1))
+    steps = _ceil_div(k, c.block_k)
+    panel = c.block_m + c.block_n
+    return w * panel * steps * (c.block_k + dev.step_cost_k) + rounds * panel * dev.tile_cost_k
 
 
-def rank_key(v: Verdict, dev: DeviceModel):
+def rank_key(v: Verdict, dev: DeviceModel, k_loop: Optional[int] = None):
     """Order of preference among feasible candidates.
 
     pages: least modelled DRAM traffic, then most resident blocks, then least
     shared memory (the tile_decision.py page's shortlist order).
-    gfx950: least traffic through the busiest CU (C0 per tile under C4's wave
-    quantization), then least total traffic (C0); then, as the Tiling page's
-    rules of thumb advise when on-chip memory has room, the larger block_K;
-    then most resident blocks and most resident waves per CU (occupancy, that
-    page's third constraint), counting only the blocks the grid can supply
-    (a CU never holds more than ceil(grid / cores) blocks at once); then the
-    deeper pipeline; then less LDS.
+    gfx950: least time on the busiest CU (busiest_core_time: C0 per tile
+    under C4's dealing of the grid over the cores), then least total traffic
+    (C0); then, as the Tiling page's rules of thumb advise when on-chip memory
+    has room, the larger block_K; then most resident blocks and most resident
+    waves per CU (occupancy, that page's third constraint), counting only the
+    blocks the grid can supply (a CU never holds more than ceil(grid / cores)
+    blocks at once); then the deeper pipeline; then less LDS.
     """
     t = round_half_even(v.traffic)
     if dev.ranking == "pages":
@@ -351,7 +387,7 @@ def rank_key(v: Verdict, dev: DeviceModel):
     c = v.config
     usable = min(v.blocks_per_core, _ceil_div(v.grid, dev.cores))
     resident_waves = usable * (c.threads // dev.lane_count)
-    return (busiest_core_traffic(v, dev), t, -c.block_k, -usable, -resident_waves, -c.stages, v.smem_total)
+    return (busiest_core_time(v, dev, k_loop), t, -c.block_k, -usable, -resident_waves, -c.stages, v.smem_total)
 
 
 def candidates(dev: DeviceModel, k: int, instrs: Sequence[str]):
@@ -396,6 +432,7 @@ def sweep(m: int, n: int, k: int, dev: DeviceModel, instrs: Sequence[str], batch
                 continue
         finish_parallelism(v, m, n, dev, batch)
         v.traffic = dram_traffic(m, n, k, cfg, elem_bytes, batch)
+        v.k_loop = k
         out.append(v)
     out.sort(key=lambda x: rank_key(x, dev))
     return out
@@ -410,13 +447,6 @@ def plan(m: int, n: int, k: int, dev: Optional[DeviceModel] = None, batch: int =
     return (res[0] if res else None), len(res)
 
 
-# The gfx950 kernel's cost per K step in K elements is about BK + 22: the
-# barrier, the waits and the fragment pipeline's restart cost as much as 22
-# more elements of work (measured: at equal K the 32- and 16-wide steps of the
-# conv workload take 1.24x and 1.76x the 64-wide step's time per FLOP).
-STEP_OVERHEAD_K = 22
-
-
 def conv_k(channels: int, taps: int, block_k: int) -> int:
     """K of a convolution's implicit GEMM as a tile with K step block_k
     computes it: each of the taps (kh * kw) runs over the channels padded up
@@ -428,16 +458,13 @@ def sweep_conv(cout: int, pixels: int, channels: int, taps: int, dev: Optional[D
                elem_bytes: int = 2) -> List[Verdict]:
     """The gfx950 sweep for a convolution computed as a GEMM (the Tiling page:
     M = output channels, N = output pixels, K = channels * kh * kw), where K
-    depends on the candidate: conv_k(channels, taps, block_k).  Each candidate
-    is finished with its own K (C4 does not use K; C0 does), and the first
-    term of the gfx950 rank key, the busiest CU's panel traffic counted in
-    units of K * b, is multiplied by the K loop's cost, K + STEP_OVERHEAD_K
-    per K step, before the candidates are compared.  The other terms and the
-    enumeration order are the GEMM sweep's."""
+    depends on the candidate: conv_k(channels, taps, block_k).  Each
+    candidate is finished (C4, C0) and ranked (rank_key) with its own K; the
+    enumeration order is the GEMM sweep's."""
     dev = dev or device_gfx950()
     assert dev.ranking != "pages"
     instrs = [s for s, _ in dev.instr_shapes]
-    keyed = []
+    out = []
     # conv_k(...) >= block_k for every candidate, so no K step is skipped
     for cfg in candidates(dev, 1 << 62, instrs):
         v = evaluate(cfg, dev, elem_bytes=elem_bytes)
@@ -446,10 +473,10 @@ def sweep_conv(cout: int, pixels: int, channels: int, taps: int, dev: Optional[D
         k = conv_k(channels, taps, cfg.block_k)
         finish_parallelism(v, cout, pixels, dev, 1)
         v.traffic = dram_traffic(cout, pixels, k, cfg, elem_bytes, 1)
-        key = rank_key(v, dev)
-        keyed.append(((key[0] * (k + STEP_OVERHEAD_K * (k // cfg.block_k)),) + tuple(key[1:]), v))
-    keyed.sort(key=lambda kv: kv[0])
-    return [v for _, v in keyed]
+        v.k_loop = k
+        out.append(v)
+    out.sort(key=lambda x: rank_key(x, dev))
+    return out
 
 
 # ---------------------------------------------------------------------------
@@ -501,5 +528,5 @@ def diagnose(cfg: TileConfig, dev: DeviceModel, m: int, n: int, batch: int = 1) 
 __all__ = ["DeviceModel", "TileConfig", "Verdict", "device_pages", "device_gfx950", "evaluate",
            "finish_parallelism", "dram_traffic", "round_half_even", "sweep", "plan", "rank_key",
            "sweep_rows", "sweep_summary", "diagnose_lines", "diagnose", "candidates", "WAVE_GRIDS",
-           "busiest_core_traffic",
+           "busiest_core_time", "conv_k", "sweep_conv", "GFX950_STEP_COST_K", "GFX950_TILE_COST_K",
            "replace"]

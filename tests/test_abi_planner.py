@@ -335,3 +335,69 @@ def test_conv_default_config_is_the_conv_plan():
     assert cfg == tss.TileConfig(128, 64, 64, 4, 512, "mfma16")
     with pytest.raises(tss.TssError):
         tss.conv_plan(64, 100, 0, 9)
+
+
+def _with_costs(step, tile):
+    d = tss.device_gfx950()
+    d.step_cost_k, d.tile_cost_k = step, tile
+    return d, OP.replace(OP.device_gfx950(), step_cost_k=step, tile_cost_k=tile)
+
+
+@pytest.mark.parametrize("step,tile", [(0, 0), (22, 0), (10, 300), (40, 2000)])
+def test_ranking_cost_parameters_bit_exact(step, tile):
+    """The gfx950 ranking's cost parameters come from the device record on
+    both sides: with any values, the C++ plans equal the oracle's, GEMM and
+    convolution, every verdict in rank order."""
+    cd, od = _with_costs(step, tile)
+    ins = [s for s, _ in od.instr_shapes]
+    for (b, M, N, K) in [(1, 4096, 4096, 4096), (1, 4096, 4096, 72), (1, 2048, 8192, 136), (4, 3000, 5000, 2048),
+                         (1, 256, 256, 256), (1, 8192, 1024, 8192)]:
+        ores = OP.sweep(M, N, K, od, ins, batch=b)
+        best, lst, n = tss.tile_plan(M, N, K, batch=b, dev=cd, cap=len(ores) + 5)
+        assert n == len(ores) == len(lst)
+        for vc, vo in zip(lst, ores):
+            _same(vc, vo)
+    for co, px, c, taps in [(256, 6272, 256, 9), (64, 8 * 112 * 112, 3, 9), (128, 8 * 56 * 56, 96, 9)]:
+        ores = OP.sweep_conv(co, px, c, taps, dev=od)
+        best, lst, n = tss.conv_plan(co, px, c, taps, cap=len(ores) + 5, dev=cd)
+        assert n == len(ores) == len(lst)
+        for vc, vo in zip(lst, ores):
+            _same(vc, vo)
+
+
+def test_planner_at_the_edge_of_its_size_bounds():
+    """batch * M * N up to 2^62 and K up to 2^40 are planned exactly (C0's
+    numerator near 2^115, the time term near 2^105): the plans equal the
+    oracle's, whose integers are unbounded; one past a bound is an argument
+    error, as is a device with a negative cost parameter."""
+    g = OP.device_gfx950()
+    ins = [s for s, _ in g.instr_shapes]
+    for (b, M, N, K) in [(1, 1 << 31, 1 << 31, 1 << 40), (1 << 20, 1 << 21, 1 << 21, 1 << 40),
+                         (3, (1 << 30) + 7, (1 << 30) + 1, (1 << 40) - 3)]:
+        ores = OP.sweep(M, N, K, g, ins, batch=b)
+        best, lst, n = tss.tile_plan(M, N, K, batch=b, cap=len(ores))
+        assert n == len(ores)
+        for vc, vo in zip(lst, ores):
+            c, o = vc["config"], vo.config
+            assert (c.bm, c.bn, c.bk, c.stages, c.threads, c.instr) == \
+                (o.block_m, o.block_n, o.block_k, o.stages, o.threads, o.instr)
+            assert (vc["grid"], vc["waves"], vc["fill"], vc["traffic"]) == (vo.grid, vo.waves, vo.fill, vo.traffic)
+            r = OP.round_half_even(vo.traffic)
+            assert vc["traffic_rounded"] == min(r, (1 << 64) - 1)
+    # conv plan at the edge: K = 512 taps * 2^30 channels = 2^39
+    ores = OP.sweep_conv(1 << 31, 1 << 31, 1 << 30, 512)
+    best, lst, n = tss.conv_plan(1 << 31, 1 << 31, 1 << 30, 512, cap=len(ores))
+    assert n == len(ores) and [v["config"] for v in lst] == [_tc(v.config) for v in ores]
+    L = C.lib()
+    v = C.Verdict()
+    for args in [(1, 1 << 31, (1 << 31) + 1, 64), (1 << 20, 1 << 21, (1 << 21) + 1, 64), (1, 8, 8, (1 << 40) + 1),
+                 ((1 << 20) + 1, 1, 1, 1), (1, (1 << 40) + 1, 1, 1)]:
+        assert L.tss_tile_plan(*args, 2, None, 0, ctypes.byref(v), None, 0, None) == C.TSS_E_ARG, args
+    cfg = tss.TileConfig(256, 256, 64, 2, 512, "mfma16").c()
+    assert L.tss_evaluate(ctypes.byref(cfg), None, 1, 1 << 31, (1 << 31) + 1, 64, 2, ctypes.byref(v)) == C.TSS_E_ARG
+    assert L.tss_conv_plan(1 << 31, (1 << 31) + 1, 64, 9, 2, None, ctypes.byref(v), None, 0, None) == C.TSS_E_ARG
+    d = tss.device_gfx950()
+    d.step_cost_k = -1
+    assert L.tss_tile_plan(1, 64, 64, 64, 2, ctypes.byref(d), 0, ctypes.byref(v), None, 0, None) == C.TSS_E_ARG
+    pages = tss.device_pages()
+    assert L.tss_conv_plan(64, 64, 64, 9, 2, ctypes.byref(pages), ctypes.byref(v), None, 0, None) == C.TSS_E_ARG

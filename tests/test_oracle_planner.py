@@ -208,23 +208,49 @@ def test_gfx950_rank_prefers_occupancy_then_bigger_k_step():
     res = P.sweep(4096, 4096, 4096, g, [s for s, _ in g.instr_shapes])
     c = res[0].config
     assert (c.block_m, c.block_n, c.block_k, c.stages, c.threads, c.instr) == (256, 256, 64, 2, 512, "mfma16")
-    assert P.rank_key(res[0], g)[:1] == (512,) and P.rank_key(res[0], g)[4] == -8
+    # one tile per CU, 256 + 256 panel rows, 64 K steps of 64 + 22
+    assert P.rank_key(res[0], g)[:1] == (1 * 512 * 64 * (64 + 22),) == (2818048,)
+    assert P.rank_key(res[0], g)[4] == -8
     d = res[1].config    # the 32x32x16 twin ties on every key and follows it
     assert (d.block_m, d.block_n, d.block_k, d.stages, d.threads, d.instr) == (256, 256, 64, 2, 512, "mfma32")
 
 
-def test_gfx950_busiest_core_traffic_closed_forms():
-    g = P.device_gfx950()
-    ev = lambda bm, bn, M, N, b=1: P.finish_parallelism(P.evaluate(P.TileConfig(bm, bn, 64, 2, 256, "mfma32"), g),
-                                                        M, N, g, b)
-    # conv workload as a GEMM (256 x 6272): 128x64 tiles -> 196 tiles, one per
-    # CU at most: 1 * (128 + 64); 64x64 -> 392 tiles, two on some CUs: 2 * 128
-    assert P.busiest_core_traffic(ev(128, 64, 256, 6272), g) == 192
-    assert P.busiest_core_traffic(ev(64, 64, 256, 6272), g) == 256
-    assert P.busiest_core_traffic(ev(256, 256, 256, 6272), g) == 512     # 25 tiles, one CU each
-    # ragged batch: 4 x 12 x 20 = 960 tiles of 256x256 -> 4 per CU
-    assert P.busiest_core_traffic(ev(256, 256, 3000, 5000, 4), g) == 4 * 512
-    assert P.busiest_core_traffic(ev(128, 128, 3000, 5000, 4), g) == 15 * 256   # 3840 tiles
+def test_gfx950_busiest_core_time_closed_forms():
+    """T = W*(BM+BN)*n*(BK+s) + R*(BM+BN)*f, worked by hand (W tiles on the
+    busiest CU, u = min(blocks/CU, W) resident, R = ceil(W/u) rounds,
+    n = ceil(K/BK) steps) with the cost parameters s and f set explicitly."""
+    g0 = P.replace(P.device_gfx950(), step_cost_k=0, tile_cost_k=0)
+    ev = lambda bm, bn, M, N, b=1, bk=64, st=2, thr=256: P.finish_parallelism(
+        P.evaluate(P.TileConfig(bm, bn, bk, st, thr, "mfma32"), g0), M, N, g0, b)
+    T = P.busiest_core_time
+    # s = f = 0: the busiest CU's C0 panel traffic, (BM + BN) * K per tile.
+    # conv workload as a GEMM (256 x 6272, K = 2304): 128x64 -> 196 tiles, at
+    # most one per CU; 64x64 -> 392 tiles, two on some CUs
+    assert T(ev(128, 64, 256, 6272), g0, 2304) == 1 * 192 * 2304
+    assert T(ev(64, 64, 256, 6272), g0, 2304) == 2 * 128 * 2304
+    assert T(ev(256, 256, 256, 6272), g0, 2304) == 1 * 512 * 2304      # 25 tiles
+    # ragged batch: 4 x 12 x 20 = 960 tiles of 256x256 -> 4 per CU; K = 2048
+    assert T(ev(256, 256, 3000, 5000, 4), g0, 2048) == 4 * 512 * 2048
+    assert T(ev(128, 128, 3000, 5000, 4), g0, 2048) == 15 * 256 * 2048   # 3840 tiles
+    # a ragged K runs whole steps: K = 200 with BK = 64 -> 4 steps = 256
+    assert T(ev(256, 256, 4096, 4096), g0, 200) == 512 * 256
+    assert T(ev(256, 256, 4096, 4096, bk=16), g0, 200) == 512 * 13 * 16
+    # step cost s = 22: each step costs BK + 22
+    g1 = P.replace(g0, step_cost_k=22)
+    v = ev(256, 256, 4096, 4096)
+    assert T(v, g1, 200) == 512 * 4 * (64 + 22) == 176128
+    assert T(v, g1, 4096) == 512 * 64 * 86 == 2818048
+    # round cost f = 100: 128x128x64 at 2 stages holds 2 blocks per CU (LDS
+    # 64 KiB of 160; registers: 64 + 32 = 96 per lane -> 5 waves per SIMD,
+    # 5 blocks of 4 waves); 4096^2 -> 1024 tiles, W = 4, u = 2, R = 2
+    g2 = P.replace(g0, step_cost_k=22, tile_cost_k=100)
+    v = ev(128, 128, 4096, 4096)
+    assert (v.blocks_per_core, v.grid) == (2, 1024)
+    assert T(v, g2, 4096) == 4 * 256 * 64 * 86 + 2 * 256 * 100
+    v = ev(256, 256, 4096, 4096)
+    assert T(v, g2, 4096) == 512 * 64 * 86 + 1 * 512 * 100
+    # no tiles (N = 0): no time
+    assert T(ev(256, 256, 4096, 0), g2, 4096) == 0
 
 
 def test_gfx950_conv_and_small_shape_choices():
@@ -257,13 +283,12 @@ def test_pages_register_granule_closed_form():
 def test_conv_sweep_pins():
     """The convolution's sweep, where each candidate computes
     K = taps * ceil(C / BK) * BK (the kernel pads a tap's channels to whole
-    K steps) and its K loop costs K + 22 per step:
+    K steps):
     * K's closed forms (C = 3 and 96 over the gfx950 K steps);
     * with C a multiple of 64 every K step gives K = taps * C, and the plan's
       choice is the GEMM plan's (a 64-wide step);
-    * the K step chosen is the one that ran fastest when all three were
-      measured on the GPU (first-layer C = 3 -> 16; C = 96 -> 32; C = 48, 100
-      and 200 -> 64; 3x3 convolutions with the output sizes given)."""
+    * the rank key's time term worked by hand for C = 3 and C = 96 at each K
+      step, and the K step it makes the plan take."""
     assert [P.conv_k(3, 9, bk) for bk in (16, 32, 64)] == [144, 288, 576]
     assert [P.conv_k(96, 9, bk) for bk in (16, 32, 64)] == [864, 864, 1152]
     g = P.device_gfx950()
@@ -272,7 +297,34 @@ def test_conv_sweep_pins():
         conv = P.sweep_conv(co, px, c, taps)[0].config
         gemm = P.sweep(co, px, taps * c, g, ins)[0].config
         assert conv == gemm and conv.block_k == 64
-    measured = [((64, 8 * 112 * 112, 3, 9), 16), ((128, 8 * 56 * 56, 96, 9), 32), ((128, 8 * 56 * 56, 48, 9), 64),
-                ((128, 8 * 56 * 56, 100, 9), 64), ((256, 8 * 28 * 28, 200, 9), 64), ((256, 8 * 28 * 28, 160, 9), 64)]
-    for (co, px, c, taps), bk in measured:
-        assert P.sweep_conv(co, px, c, taps)[0].config.block_k == bk, (c, bk)
+    # First layer, 64 output channels over 8 x 112 x 112 pixels, C = 3, 3x3:
+    # a 128x128 tile, 2 stages, 256 threads (mfma32 for every K step): grid
+    # 1 x 784 tiles -> W = 4 on the busiest CU (784 / 256), all resident
+    # (u = 4: 2 blocks by LDS at BK = 64 ... at most 4 useful), 256 panel rows.
+    res = {v.config: v for v in P.sweep_conv(64, 8 * 112 * 112, 3, 9)}
+    keys = {bk: P.rank_key(res[P.TileConfig(128, 128, bk, 2, 256, "mfma32")], g)[0] for bk in (16, 32, 64)}
+    assert keys == {16: 4 * 256 * 9 * (16 + 22), 32: 4 * 256 * 9 * (32 + 22), 64: 4 * 256 * 9 * (64 + 22)}
+    assert keys == {16: 350208, 32: 497664, 64: 792576}
+    # C = 96 (8 x 56 x 56 pixels, 128 output channels): BK = 16 and 32 both
+    # pad nothing (K = 864) but 16 takes 54 steps against 27; BK = 64 pads
+    # to 1152 in 18 steps.  Same tile: W = ceil(196 / 256) = 1.
+    res = {v.config: v for v in P.sweep_conv(128, 8 * 56 * 56, 96, 9)}
+    keys = {bk: P.rank_key(res[P.TileConfig(128, 128, bk, 2, 256, "mfma32")], g)[0] for bk in (16, 32, 64)}
+    assert keys == {16: 256 * 54 * 38, 32: 256 * 27 * 54, 64: 256 * 18 * 86}
+    assert min(keys, key=keys.get) == 32
+
+
+def test_conv_plan_without_step_cost_never_pads_more():
+    """With the step cost set to zero, a candidate's K loop costs its padded
+    K alone, and the time term is W * (BM + BN) * K(BK) with W independent of
+    BK: the plan's K step is one of those that pad least for its tile shape
+    (no BK with a smaller padded K is feasible for the same BM, BN,
+    threads and instruction), whatever the channel count."""
+    g0 = P.replace(P.device_gfx950(), step_cost_k=0, tile_cost_k=0)
+    for c in (1, 3, 8, 20, 48, 72, 96, 100, 160, 200, 256, 333):
+        best = P.sweep_conv(128, 8 * 28 * 28, c, 9, dev=g0)[0]
+        b = best.config
+        same_shape = [v for v in P.sweep_conv(128, 8 * 28 * 28, c, 9, dev=g0)
+                      if (v.config.block_m, v.config.block_n, v.config.threads, v.config.instr)
+                      == (b.block_m, b.block_n, b.threads, b.instr)]
+        assert P.conv_k(c, 9, b.block_k) == min(P.conv_k(c, 9, v.config.block_k) for v in same_shape), c

@@ -1,0 +1,62 @@
+"""Measured checks of the gfx950 ranking's policy: the planner's choices
+timed against the alternatives they were chosen over, on this GPU.
+
+These are not parity tests (the oracle cannot say which tile runs fastest);
+they check the cost parameters of the gfx950 model against the kernels.
+Each candidate is timed as the best of three rounds of 10 launches (HIP
+events), after a warm-up, and the planner's choice must be within 5% of the
+fastest of its alternatives."""
+import pytest
+import torch
+
+import tile_size_selection_amd as tss
+from tile_size_selection_amd.inputs import draw
+
+pytestmark = pytest.mark.gpu
+
+CUDA = torch.device("cuda:0")
+
+
+def _time(fn, n=10, rounds=3):
+    for _ in range(3):
+        fn()
+    torch.cuda.synchronize()
+    best = float("inf")
+    for _ in range(rounds):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        best = min(best, e0.elapsed_time(e1) / n * 1e3)
+    return best
+
+
+# (N, C, H, W, Cout, stride): 3x3, pad 1.  A first layer (C = 3), and
+# channel counts that are not multiples of 64 (C = 48, 96, 100, 160, 200),
+# where the K step decides how much each tap's channels are padded.
+CONVS = [(8, 3, 224, 224, 64, 2), (8, 96, 56, 56, 128, 1), (8, 48, 56, 56, 128, 1), (8, 100, 56, 56, 128, 1),
+         (8, 200, 56, 56, 256, 2), (8, 160, 56, 56, 256, 2)]
+
+
+@pytest.mark.parametrize("conv", CONVS, ids=[f"C{c[1]}" for c in CONVS])
+def test_conv_k_step_choice_within_5pct_of_the_fastest(conv):
+    """The convolution plan's K step (step cost 22 K elements per step)
+    against the same tile with the other K steps of the candidate space."""
+    N, Ci, H, W, Co, s = conv
+    x = draw((N, Ci, H, W), "uniform", -1, 1, "f16", 71).to(CUDA)
+    w = draw((Co, Ci, 3, 3), "normal", 0, 0.05, "f16", 72).to(CUDA)
+    chosen = tss.conv2d_default_config(N, Ci, H, W, Co, 3, 3, s, 1, 1)
+    ws = torch.empty(tss.conv2d_workspace_size(N, Ci, H, W, Co, 3, 3), dtype=torch.uint8, device=CUDA)
+    y = tss.conv2d(x, w, s, 1, 1, out_dtype="f32", cfg=chosen, workspace=ws)
+    times = {}
+    for bk in (16, 32, 64):
+        cfg = tss.TileConfig(chosen.bm, chosen.bn, bk, chosen.stages, chosen.threads, chosen.instr)
+        if not tss.kernel_available(cfg, "f16", "conv"):
+            continue
+        times[cfg] = _time(lambda: tss.conv2d(x, w, s, 1, 1, out_dtype="f32", cfg=cfg, out=y, workspace=ws))
+    fastest = min(times.values())
+    print(f"C={Ci}: chosen {chosen} {times[chosen]:.1f} us; "
+          + ", ".join(f"BK {c.bk}: {t:.1f}" for c, t in times.items()), flush=True)
+    assert times[chosen] <= 1.05 * fastest

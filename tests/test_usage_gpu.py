@@ -64,3 +64,29 @@ def test_measured_plan_is_the_usage_table_plan():
               f"(regs {best_m['regs_per_thread']}, blocks/CU {best_m['blocks_per_core']}); "
               f"model plan {plain['config']} (regs {plain['regs_per_thread']}, "
               f"blocks/CU {plain['blocks_per_core']})", flush=True)
+
+
+def test_measured_plan_equals_the_oracle_with_the_kernels_table():
+    """tss_tile_plan_measured (C++, table read from the code objects through
+    the HIP runtime) against the oracle's sweep given the same table: the
+    same candidates in the same order, with the same occupancy, grid and C0."""
+    g = OP.device_gfx950()
+    ins = [s for s, _ in g.instr_shapes]
+    for (b, M, N, K), dt, op in [((1, 4096, 4096, 4096), "f16", "gemm"), ((1, 256, 6272, 2304), "f16", "conv"),
+                                 ((4, 3000, 5000, 2048), "bf16", "gemm"), ((1, 4096, 4096, 72), "f16", "gemm")]:
+        regs = {}
+        for cfg, _ in _configs():
+            u = tss.kernel_usage(cfg, dt, op)
+            regs[OP.TileConfig(cfg.bm, cfg.bn, cfg.bk, cfg.stages, cfg.threads, cfg.instr)] = \
+                (u["regs_per_lane"], u["scratch_bytes"])
+        ores = OP.sweep(M, N, K, g, ins, batch=b, regs=regs)
+        best, lst, n = tss.tile_plan_measured(M, N, K, batch=b, dtype=dt, op=op, cap=len(ores) + 5)
+        assert n == len(ores) == len(lst)
+        for vc, vo in zip(lst, ores):
+            c, o = vc["config"], vo.config
+            assert (c.bm, c.bn, c.bk, c.stages, c.threads, c.instr) == \
+                (o.block_m, o.block_n, o.block_k, o.stages, o.threads, o.instr)
+            assert (vc["regs_per_thread"], vc["blocks_per_core"], vc["grid"], vc["waves"], vc["fill"],
+                    vc["traffic"]) == (vo.regs_per_thread, vo.blocks_per_core, vo.grid, vo.waves, vo.fill,
+                                       vo.traffic)
+        print(f"{op} {dt} {b}x{M}x{N}x{K}: measured plan {best['config']} equals the oracle's", flush=True)

@@ -95,16 +95,17 @@ def tile_plan(M: int, N: int, K: int, batch: int = 1, elem_bytes: int = 2, dev: 
 
 
 def conv_plan(Cout: int, pixels: int, channels: int, taps: int, elem_bytes: int = 2,
-              cap: int = 0) -> Tuple[Optional[dict], List[dict], int]:
+              cap: int = 0, dev: Optional[C.Device] = None) -> Tuple[Optional[dict], List[dict], int]:
     """tss_conv_plan: the gfx950 plan of a convolution's implicit GEMM (M =
     Cout, N = output pixels), each candidate with the K its kernel computes,
-    taps * ceil(channels / BK) * BK.  (best or None, first `cap` ranked, n
-    feasible)."""
+    taps * ceil(channels / BK) * BK.  dev: a gfx950-ranked device (its cost
+    parameters), None = the gfx950 model.  (best or None, first `cap`
+    ranked, n feasible)."""
     best = C.Verdict()
     lst = (C.Verdict * max(cap, 1))()
     n = C.i32(0)
-    st = C.lib().tss_conv_plan(Cout, pixels, channels, taps, elem_bytes, ctypes.byref(best), lst if cap else None,
-                               cap, ctypes.byref(n))
+    st = C.lib().tss_conv_plan(Cout, pixels, channels, taps, elem_bytes, ctypes.byref(dev) if dev is not None else None,
+                               ctypes.byref(best), lst if cap else None, cap, ctypes.byref(n))
     return _plan_result(st, best, lst, cap, n, "tss_conv_plan")
 
 

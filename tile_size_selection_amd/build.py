@@ -1,10 +1,14 @@
 """Build libtss.so (planner, C ABI and every gfx950 kernel) in-tree.
 
-    python -m tile_size_selection_amd.build [--incremental] [--jobs N]
+    python -m tile_size_selection_amd.build [--incremental] [--jobs N] [--units NAME ...]
 
 Each instantiation unit under csrc/inst is compiled by its own hipcc process
 for --offload-arch=gfx950; the objects are linked into
 tile_size_selection_amd/libtss.so, which is what the Python binding loads.
+The planner's command line, csrc/tss_plan.c, is built against that library
+into tile_size_selection_amd/tss_plan (a host program: gcc, C ABI only).
+--units recompiles only the sources whose file names contain one of the
+given strings (the other objects are linked as they are).
 """
 from __future__ import annotations
 
@@ -22,6 +26,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OUT_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libtss.so")
+CLI = os.path.join(PKG, "tss_plan")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # -packed-fp32-ops off: compiler-made v_pk_{add,mul,fma}_f32 are avoided.
@@ -91,12 +96,29 @@ def _compile(src, obj):
     return src, time.time() - t0
 
 
-def build(incremental: bool = False, jobs: int = 0, verbose: bool = True) -> str:
+def build_cli(verbose: bool = True) -> str:
+    """tss_plan: the planner's command line, linked to libtss.so beside it."""
+    tmp = CLI + ".tmp"
+    cmd = ["gcc", "-O2", "-std=c11", "-Wall", "-Wextra", "-I", os.path.join(ROOT, "include"),
+           os.path.join(CSRC, "tss_plan.c"), "-o", tmp, "-L", PKG, "-l:libtss.so", "-Wl,-rpath,$ORIGIN"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"gcc failed for tss_plan.c:\n{r.stderr}")
+    os.replace(tmp, CLI)
+    if verbose:
+        print(f"built {os.path.relpath(CLI, ROOT)}", flush=True)
+    return CLI
+
+
+def build(incremental: bool = False, jobs: int = 0, verbose: bool = True, units=None) -> str:
     os.makedirs(OUT_DIR, exist_ok=True)
     todo = []
     for s in sources():
         o = _obj(s)
-        if incremental and _up_to_date(s, o):
+        if units is not None:
+            if not any(u in os.path.basename(s) for u in units) and os.path.exists(o):
+                continue
+        elif incremental and _up_to_date(s, o):
             continue
         todo.append((s, o))
     jobs = jobs or min(16, os.cpu_count() or 4)
@@ -115,6 +137,7 @@ def build(incremental: bool = False, jobs: int = 0, verbose: bool = True) -> str
     if verbose:
         print(f"built {os.path.relpath(LIB, ROOT)} ({len(todo)} units compiled) in {time.time() - t0:.1f}s",
               flush=True)
+    build_cli(verbose)
     return LIB
 
 
@@ -123,10 +146,11 @@ def main():
     ap.add_argument("--incremental", action="store_true")
     ap.add_argument("--jobs", type=int, default=0)
     ap.add_argument("--clean", action="store_true")
+    ap.add_argument("--units", nargs="+", default=None)
     a = ap.parse_args()
     if a.clean and os.path.isdir(OUT_DIR):
         shutil.rmtree(OUT_DIR)
-    build(a.incremental, a.jobs)
+    build(a.incremental, a.jobs, units=a.units)
     return 0
 
 

@@ -73,7 +73,7 @@ int32_t planned_config(bool conv, int64_t a, int64_t b, int64_t c, int64_t d, ts
     }
   }
   tss_verdict best{};
-  int32_t st = conv ? tss_conv_plan(a, b, c, d, 2, &best, nullptr, 0, nullptr)
+  int32_t st = conv ? tss_conv_plan(a, b, c, d, 2, nullptr, &best, nullptr, 0, nullptr)
                     : tss_tile_plan(a, b, c, d, 2, nullptr, 0, &best, nullptr, 0, nullptr);
   if (st != TSS_OK) return st;
   {

@@ -11,7 +11,8 @@ namespace {
 bool valid_device(const tss_device &d) {
   if (d.cores <= 0 || d.onchip_per_core <= 0 || d.onchip_per_block_max <= 0 || d.max_threads_per_core <= 0 ||
       d.max_threads_per_block <= 0 || d.max_blocks_per_core <= 0 || d.lane_count <= 0 ||
-      d.reg_granule_per_lane <= 0 || d.acc_regs_max <= 0 || d.reg_overhead < 0)
+      d.reg_granule_per_lane <= 0 || d.acc_regs_max <= 0 || d.reg_overhead < 0 || d.step_cost_k < 0 ||
+      d.tile_cost_k < 0)
     return false;
   if (d.reg_model == TSS_REG_POOLED) return d.regs_per_core > 0;
   if (d.reg_model == TSS_REG_PER_SIMD)
@@ -30,38 +31,34 @@ bool valid_config(const tss_tile_config &c, const tss_device &d) {
 struct FixedK {
   int64_t K;
   int64_t operator()(int32_t) const { return K; }
-  static constexpr bool varies = false;
 };
 struct ConvK {
   int64_t C, taps;
   int64_t operator()(int32_t bk) const { return taps * ((C + bk - 1) / bk) * bk; }
-  static constexpr bool varies = true;
 };
 
-// Cost of a tile's K loop in units of K elements: each K step of BK elements
-// costs about BK + kStepOverheadK (the barrier, the waits and the restart of
-// the fragment pipeline; fitted to the conv workload's measured sweep, where
-// the 32- and 16-wide steps take 1.24x and 1.76x the 64-wide step's time per
-// FLOP at equal K).  Used where K depends on BK (the convolution), so that a
-// shorter step is taken only when the channel padding it saves outweighs the
-// steps it adds.
-constexpr int64_t kStepOverheadK = 22;
+constexpr int64_t kLim40 = int64_t(1) << 40;
+
+// Sizes every planner entry point accepts: batch <= 2^20, M, N, K <= 2^40
+// and batch * M * N <= 2^62, so that the grid fits 64 bits and C0's
+// numerator 128 bits.
+bool sizes_ok(int64_t batch, int64_t M, int64_t N, int64_t K) {
+  if (batch < 1 || M < 0 || N < 0 || K < 0) return false;
+  if (M > kLim40 || N > kLim40 || K > kLim40 || batch > (int64_t(1) << 20)) return false;
+  const unsigned __int128 bmn = (unsigned __int128)batch * (unsigned __int128)M * (unsigned __int128)N;
+  return bmn <= ((unsigned __int128)1 << 62);
+}
 
 // The shared sweep: every candidate of the device's space that passes
-// C3/C1/C2/occupancy, finished for the problem and ranked.  usage_of (may be
-// null) gives the compiled kernel's measured usage for a configuration (null
-// to leave the candidate out).  k_of gives each candidate's K; where it
-// varies between candidates, the busiest-CU term of the rank key, which
-// otherwise counts per-tile panel traffic in units of K * b bytes, is scaled
-// by the candidate's K-loop cost, K + kStepOverheadK * (K / BK).
+// C3/C1/C2/occupancy, finished for the problem with its own K (k_of) and
+// ranked by rank_key.  usage_of (may be null) gives the compiled kernel's
+// measured usage for a configuration (null to leave the candidate out).
 template <typename UsageOf, typename KOf>
 int32_t plan_sweep(int64_t batch, int64_t M, int64_t N, const KOf &k_of, int32_t elem_bytes, const tss_device &d,
                    int32_t instr_filter, const UsageOf *usage_of, tss_verdict *best, tss_verdict *list, int32_t cap,
                    int32_t *n_feasible) {
   const int64_t K = k_of(1);
-  if (batch < 1 || M < 0 || N < 0 || K < 0 || elem_bytes < 1 || elem_bytes > 8 || cap < 0) return TSS_E_ARG;
-  if (M > (int64_t(1) << 40) || N > (int64_t(1) << 40) || K > (int64_t(1) << 40) || batch > (int64_t(1) << 20))
-    return TSS_E_ARG;
+  if (!sizes_ok(batch, M, N, K) || elem_bytes < 1 || elem_bytes > 8 || cap < 0) return TSS_E_ARG;
   if (!valid_device(d)) return TSS_E_ARG;
   if (instr_filter && !instr_on_device(instr_filter, d)) return TSS_E_ARG;
   const Space s = space_for(d, instr_filter);
@@ -78,7 +75,7 @@ int32_t plan_sweep(int64_t batch, int64_t M, int64_t N, const KOf &k_of, int32_t
           // A K step longer than K is skipped, unless K is shorter than every
           // candidate step: then the shortest one is kept (its tail is masked).
           const int64_t Kc = k_of(s.bk[c]);
-          if (Kc > (int64_t(1) << 40)) return TSS_E_ARG;
+          if (Kc > kLim40) return TSS_E_ARG;
           if (s.bk[c] > (Kc > s.bk[0] ? Kc : s.bk[0])) continue;
           for (int e = 0; e < s.nst; ++e)
             for (int f = 0; f < s.nthr; ++f) {
@@ -102,12 +99,7 @@ int32_t plan_sweep(int64_t batch, int64_t M, int64_t N, const KOf &k_of, int32_t
   }
   std::vector<int32_t> order(feas.size());
   for (size_t i = 0; i < order.size(); ++i) order[i] = int32_t(i);
-  auto key_of = [&](int32_t i) {
-    Key k = rank_key(feas[i], d);
-    if (KOf::varies && d.ranking != TSS_RANK_PAGES)
-      k.k[0] *= feas_k[i] + kStepOverheadK * (feas_k[i] / feas[i].cfg.bk);
-    return k;
-  };
+  auto key_of = [&](int32_t i) { return rank_key(feas[i], d, feas_k[i]); };
   std::stable_sort(order.begin(), order.end(),
                    [&](int32_t x, int32_t y) { return key_less(key_of(x), key_of(y)); });
   if (n_feasible) *n_feasible = int32_t(feas.size());
@@ -126,6 +118,16 @@ struct NoUsage {
 
 extern "C" {
 
+int32_t tss_instr_shape(int32_t instr, int32_t out[4]) {
+  Shape s{};
+  if (!out || !instr_shape(instr, s)) return TSS_E_ARG;
+  out[0] = s.m;
+  out[1] = s.n;
+  out[2] = s.k;
+  out[3] = s.threads;
+  return TSS_OK;
+}
+
 int32_t tss_device_gfx950(tss_device *out) {
   if (!out) return TSS_E_ARG;
   *out = gfx950_device();
@@ -141,10 +143,8 @@ int32_t tss_device_pages(int32_t sm_count, int32_t smem_kb, tss_device *out) {
 int32_t tss_evaluate(const tss_tile_config *cfg, const tss_device *dev, int64_t batch, int64_t M, int64_t N,
                      int64_t K, int32_t elem_bytes, tss_verdict *out) {
   const tss_device d = dev ? *dev : gfx950_device();
-  if (!cfg || !out || batch < 1 || M < 0 || N < 0 || K < 0 || elem_bytes < 1 || elem_bytes > 8) return TSS_E_ARG;
+  if (!cfg || !out || !sizes_ok(batch, M, N, K) || elem_bytes < 1 || elem_bytes > 8) return TSS_E_ARG;
   if (!valid_device(d) || !valid_config(*cfg, d)) return TSS_E_ARG;
-  if (M > (int64_t(1) << 40) || N > (int64_t(1) << 40) || K > (int64_t(1) << 40) || batch > (int64_t(1) << 20))
-    return TSS_E_ARG;
   tss_verdict v = evaluate_block(*cfg, d, elem_bytes);
   finish(v, d, batch, M, N, K, elem_bytes);
   *out = v;
@@ -160,11 +160,14 @@ int32_t tss_tile_plan(int64_t batch, int64_t M, int64_t N, int64_t K, int32_t el
                              n_feasible);
 }
 
-int32_t tss_conv_plan(int64_t Cout, int64_t pixels, int64_t C, int64_t taps, int32_t elem_bytes, tss_verdict *best,
-                      tss_verdict *list, int32_t cap, int32_t *n_feasible) {
+int32_t tss_conv_plan(int64_t Cout, int64_t pixels, int64_t C, int64_t taps, int32_t elem_bytes,
+                      const tss_device *dev, tss_verdict *best, tss_verdict *list, int32_t cap,
+                      int32_t *n_feasible) {
+  const tss_device d = dev ? *dev : gfx950_device();
   if (C < 1 || taps < 1 || C > (int64_t(1) << 30) || taps > (int64_t(1) << 20)) return TSS_E_ARG;
-  return plan_sweep<NoUsage>(1, Cout, pixels, ConvK{C, taps}, elem_bytes, gfx950_device(), 0, nullptr, best, list,
-                             cap, n_feasible);
+  if (d.ranking != TSS_RANK_GFX950 || d.lane_count != 64) return TSS_E_ARG;
+  return plan_sweep<NoUsage>(1, Cout, pixels, ConvK{C, taps}, elem_bytes, d, 0, nullptr, best, list, cap,
+                             n_feasible);
 }
 
 int32_t tss_tile_plan_usage(int64_t batch, int64_t M, int64_t N, int64_t K, int32_t elem_bytes,

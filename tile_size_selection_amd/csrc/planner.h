@@ -73,6 +73,8 @@ constexpr tss_device gfx950_device() {
   d.wave_grid_rule = 1;
   d.load_bytes_per_lane = 16;
   d.ranking = TSS_RANK_GFX950;
+  d.step_cost_k = 22;
+  d.tile_cost_k = 0;
   return d;
 }
 
@@ -91,6 +93,8 @@ constexpr tss_device pages_device(int32_t sm_count, int32_t smem_kb) {
   d.reg_model = TSS_REG_POOLED;
   d.regs_per_core = 65536;
   d.ranking = TSS_RANK_PAGES;
+  d.step_cost_k = 0;
+  d.tile_cost_k = 0;
   return d;
 }
 
@@ -177,7 +181,15 @@ constexpr u128 gcd128(u128 a, u128 b) {
   return a;
 }
 
+constexpr u128 round_half_even(u128 num, u128 den) {
+  u128 q = num / den, r = num % den;
+  if (2 * r > den || (2 * r == den && (q & 1))) q += 1;
+  return q;
+}
+
 // C4 and C0 for one problem (the verdict must come from evaluate_block).
+// The caller keeps batch * M * N <= 2^62 and K <= 2^40, so that the grid fits
+// int64 and C0's numerator (below 2^62 * 8 * 2^40 * 2^10) fits 128 bits.
 constexpr void finish(tss_verdict &v, const tss_device &d, int64_t batch, int64_t M, int64_t N,
                       int64_t K, int32_t eb) {
   const tss_tile_config &c = v.cfg;
@@ -212,9 +224,15 @@ constexpr void finish(tss_verdict &v, const tss_device &d, int64_t batch, int64_
   v.traffic_num_hi = uint64_t(num >> 64);
   v.traffic_num_lo = uint64_t(num);
   v.traffic_den = uint64_t(den);
-  u128 q = num / den, r = num % den;
-  if (2 * r > den || (2 * r == den && (q & 1))) q += 1;  // round half to even
-  v.traffic_rounded = uint64_t(q);
+  const u128 q = round_half_even(num, den);
+  v.traffic_rounded = q > u128(UINT64_MAX) ? UINT64_MAX : uint64_t(q);  // saturated; exact in num / den
+}
+
+// C0 of a finished verdict, rounded half to even, without the saturation of
+// traffic_rounded.
+constexpr u128 traffic_rounded_exact(const tss_verdict &v) {
+  const u128 num = (u128(v.traffic_num_hi) << 64) | u128(v.traffic_num_lo);
+  return round_half_even(num, u128(v.traffic_den));
 }
 
 // ---- candidate space -------------------------------------------------------
@@ -260,28 +278,54 @@ constexpr Space space_for(const tss_device &d, int32_t instr_filter) {
   return s;
 }
 
-// Lexicographic rank key; smaller is preferred.
+// Lexicographic rank key; smaller is preferred.  128-bit terms: the
+// traffic and time terms of problems near the accepted bounds exceed 64 bits.
+using i128 = __int128;
 struct Key {
-  int64_t k[7];
+  i128 k[7];
 };
 
-constexpr Key rank_key(const tss_verdict &v, const tss_device &d) {
+// The gfx950 time term of a candidate whose K loop runs over K elements
+// (K_loop: the GEMM's K, or the convolution's K with each tap's channels
+// padded to whole K steps).  On the busiest CU, C4 deals out
+// W = ceil(grid / CUs) tiles, at most u = min(blocks per CU, W) of them
+// resident at once, so in R = ceil(W / u) rounds.  Each tile streams its
+// C0 panels, (BM + BN) elements per K element (the README page's per-tile
+// traffic), over n = ceil(K_loop / BK) K steps, each step costing
+// BK + step_cost_k K elements; each round pays tile_cost_k more (prologue,
+// epilogue, output write):
+//   T = W * (BM + BN) * n * (BK + step_cost_k) + R * (BM + BN) * tile_cost_k.
+// Every candidate's intensity 2*BM*BN / ((BM + BN) * b) (the Tiling page's
+// tiled-intensity formula, at most 128 FLOP/B) is below MI355X's ridge
+// (2516.6 TFLOP/s over 8 TB/s, about 315 FLOP/B), which is why panel
+// traffic is the unit of time.
+constexpr i128 busiest_core_time(const tss_verdict &v, const tss_device &d, int64_t K_loop) {
+  const tss_tile_config &c = v.cfg;
+  const int64_t W = cdiv(v.grid, d.cores);
+  if (W == 0) return 0;
+  const int64_t u = v.blocks_per_core < W ? v.blocks_per_core : W;
+  const int64_t R = cdiv(W, u > 0 ? u : 1);
+  const int64_t n = cdiv(K_loop, c.bk);
+  const i128 panel = i128(c.bm + c.bn);
+  return i128(W) * panel * i128(n) * i128(c.bk + d.step_cost_k) + i128(R) * panel * i128(d.tile_cost_k);
+}
+
+constexpr Key rank_key(const tss_verdict &v, const tss_device &d, int64_t K_loop) {
   Key r{};
-  int64_t t = int64_t(v.traffic_rounded);
+  const i128 t = i128(traffic_rounded_exact(v));
   if (d.ranking == TSS_RANK_PAGES) {
     r.k[0] = t;
     r.k[1] = -v.blocks_per_core;
     r.k[2] = v.smem_total;
   } else {
-    // least traffic through the busiest CU: C0's per-tile panels (BM + BN)
-    // times the tiles a CU streams once the grid is dealt out in waves (every
-    // candidate's intensity is below the device ridge, ~315 FLOP/B); then
-    // total C0, larger BK, most resident blocks, most resident waves, deeper
-    // pipeline, less LDS.  Residency counts only the blocks the grid can
-    // supply: with ceil(grid / CUs) waves of tiles no CU ever holds more
-    // than that many blocks at once, whatever its capacity.
-    const int64_t usable = v.blocks_per_core < cdiv(v.grid, d.cores) ? v.blocks_per_core : cdiv(v.grid, d.cores);
-    r.k[0] = cdiv(v.grid, d.cores) * (v.cfg.bm + v.cfg.bn);
+    // the busiest CU's time (above); then total C0, larger BK, most resident
+    // blocks, most resident waves, deeper pipeline, less LDS.  Residency
+    // counts only the blocks the grid can supply: with ceil(grid / CUs) waves
+    // of tiles no CU ever holds more than that many blocks at once, whatever
+    // its capacity.
+    const int64_t W = cdiv(v.grid, d.cores);
+    const int64_t usable = v.blocks_per_core < W ? v.blocks_per_core : W;
+    r.k[0] = busiest_core_time(v, d, K_loop);
     r.k[1] = t;
     r.k[2] = -v.cfg.bk;
     r.k[3] = -usable;
