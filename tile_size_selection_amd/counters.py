@@ -16,6 +16,11 @@ every pattern of the LDS bank table:
     rocprofv3 --pmc MfmaUtil LdsBankConflict SQ_INSTS_LDS --output-format csv -d <dir>/ldsutil -o run -- python3 -m tile_size_selection_amd.counters run-lds
     python3 -m tile_size_selection_amd.counters summarize-util <dir> > summary.md
 
+Kernel durations of any rocprofv3 --kernel-trace run (its results database
+or kernel_trace.csv), with the mean of each kernel's last N launches:
+
+    python3 -m tile_size_selection_amd.counters trace-summary <dir>/run_results.db --last 20
+
 `run` launches a plain elementwise pass over 256 MiB (y = -x: known bytes
 read and written) and then the 4096^3 fp16 GEMM in the configuration the
 benchmark times.  That pass calibrates the counters: the GEMM's FETCH_SIZE / WRITE_SIZE (KiB per
@@ -207,6 +212,38 @@ def summarize(d: str, trace: str = None) -> str:
     return "\n".join(lines) + "\n"
 
 
+def trace_summary(path: str, last: int = 0) -> str:
+    """Per-kernel durations of a rocprofv3 kernel trace: the run's results
+    database (<dir>/<name>_results.db, the default output) or its
+    kernel_trace.csv.  last > 0 adds, per kernel, the mean of its last `last`
+    launches (the timed region of a benchmark run) and the mean gap between
+    them."""
+    rows = []   # (name, start_ns, end_ns)
+    if path.endswith(".db"):
+        import sqlite3
+        con = sqlite3.connect(path)
+        rows = list(con.execute("select name, start, end from kernels order by start"))
+    else:
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                rows.append((r["Kernel_Name"], int(r["Start_Timestamp"]), int(r["End_Timestamp"])))
+        rows.sort(key=lambda r: r[1])
+    by = defaultdict(list)
+    for name, st, en in rows:
+        by[name].append((st, en))
+    out = ["| kernel | launches | average us | min us | max us |" + (f" last {last}: average us | gap us |" if last else ""),
+           "|---|---|---|---|---|" + ("---|---|" if last else "")]
+    for name, ev in sorted(by.items(), key=lambda kv: -sum(e - s for s, e in kv[1])):
+        d = [e - s for s, e in ev]
+        line = f"| `{name[:100]}` | {len(d)} | {_mean(d) / 1e3:.2f} | {min(d) / 1e3:.2f} | {max(d) / 1e3:.2f} |"
+        if last:
+            tail = ev[-last:]
+            gaps = [tail[i + 1][0] - tail[i][1] for i in range(len(tail) - 1)]
+            line += f" {_mean([e - s for s, e in tail]) / 1e3:.2f} | {(_mean(gaps) if gaps else 0) / 1e3:.2f} |"
+        out.append(line)
+    return "\n".join(out) + "\n"
+
+
 def main():
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -218,7 +255,13 @@ def main():
     s.add_argument("--trace", default=None)
     u = sub.add_parser("summarize-util")
     u.add_argument("dir")
+    t = sub.add_parser("trace-summary")
+    t.add_argument("path")
+    t.add_argument("--last", type=int, default=0)
     a = ap.parse_args()
+    if a.cmd == "trace-summary":
+        sys.stdout.write(trace_summary(a.path, a.last))
+        return 0
     if a.cmd == "run":
         run(a.launches)
     elif a.cmd == "run-lds":
