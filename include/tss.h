@@ -105,9 +105,18 @@ typedef struct {
        term off: the loop then costs its padded K alone.
      tile_cost_k: the fixed cost of one round of co-resident tiles on a CU
        (prologue, epilogue, output write), as a K-loop length of the same
-       tile.  0 turns it off. */
+       tile.  0 turns it off.
+     Cost parameters of the split-K plan (tss_splitk_plan), in the same
+     units (one streamed panel element):
+     split_byte_cost: what one byte of the partial sums' extra traffic (each
+       range's fp32 output written once and read once by the reduction)
+       costs, as bytes of streamed panel; the partial sums of S ranges add
+       8 * S * batch * M * N * split_byte_cost / (elem_bytes * cores).
+     launch_cost_k: the fixed cost of the reduction launch. */
   int32_t step_cost_k;
   int32_t tile_cost_k;
+  int32_t split_byte_cost;
+  int32_t launch_cost_k;
 } tss_device;
 
 /* One tile configuration (block tile BM x BN, K step BK, pipeline stages,
@@ -228,6 +237,30 @@ int32_t tss_conv_plan(int64_t Cout, int64_t pixels, int64_t C, int64_t taps, int
                       int32_t *n_feasible);
 
 /*
+ * The split-K plan (gfx950 ranking): for S in {1, 2, 3, 4, 6, 8, 12, 16},
+ * the tile plan of the split problem -- batch * S GEMMs of M x N x
+ * ceil(K / S) (tss_tile_plan) -- whose busiest-CU time T_S (the first term
+ * of the rank key) is charged, for S > 1, the partial sums' traffic and the
+ * reduction launch (dev->split_byte_cost, dev->launch_cost_k); S is kept only
+ * when its tile's K steps cut K into exactly S ranges.  The least total
+ * wins, the smaller S on a tie.  *splits: on entry 0 (choose S as above) or
+ * the S to plan the tile for (1..256); on return the S; best (nullable)
+ * receives the verdict of the tile for the split problem.  The tile and S
+ * are what tss_gemm_splitk takes for splits = 0 (its tile for a given S and
+ * a NULL cfg is this plan's with *splits = S).  dev NULL = gfx950 (it must
+ * rank the gfx950 way).
+ * Errors: TSS_E_ARG (as tss_tile_plan, splits NULL or out of range),
+ * TSS_E_INFEASIBLE.
+ */
+int32_t tss_splitk_plan(int64_t batch, int64_t M, int64_t N, int64_t K, int32_t elem_bytes, const tss_device *dev,
+                        tss_verdict *best, int32_t *splits);
+
+/* The same for a convolution's implicit GEMM (as tss_conv_plan: each
+   candidate's K is taps * ceil(C / BK) * BK, split into S ranges). */
+int32_t tss_conv_splitk_plan(int64_t Cout, int64_t pixels, int64_t C, int64_t taps, int32_t elem_bytes,
+                             const tss_device *dev, tss_verdict *best, int32_t *splits);
+
+/*
  * The planner with feedback from the compiled kernels.  The tile_decision.py
  * page's C2 counts only the accumulators, and its README lists the register
  * model as a known limitation.  Here each candidate takes what its compiled
@@ -337,11 +370,61 @@ int32_t tss_conv2d_tiled(int64_t N, int64_t C, int64_t H, int64_t W, int64_t Cou
                          int32_t out_dtype, const void *x, const void *w, void *y, void *workspace,
                          int64_t workspace_bytes, const tss_tile_config *cfg, void *stream);
 
+/*
+ * Split K: the same GEMM with its K loop cut into ranges computed by
+ * separate blocks, for problems whose output tiles alone leave CUs idle (the
+ * C4 "idle" warning of the tile_decision.py page: fewer tiles than CUs).
+ * K is cut into at most `splits` ranges of equal length in whole K steps of
+ * the tile (the last range holds the rest; fewer ranges when K is short).
+ * Each range adds its products into its own fp32 partial output in
+ * `workspace`; a second launch on `stream` adds the ranges of every output
+ * element in range order (0, 1, ...) and converts the sum to out_dtype, so
+ * every run gives the same bits (the sum order differs from the one-pass
+ * GEMM's, the result not).
+ * splits in [0, 256]; 0 = the split-K plan's count (tss_splitk_plan; with
+ * its tile when cfg is NULL); 1 = tss_gemm (workspace unused, may be NULL);
+ * with splits > 1 and a NULL cfg the tile is tss_splitk_plan's for that S.
+ * workspace: device memory, 16-byte aligned, of at least
+ * tss_gemm_splitk_workspace_size(batch, M, N, splits) bytes, owned by the
+ * caller; scratch, overwritten by every call (calls sharing it must be
+ * ordered on one stream).  Everything else as tss_gemm.
+ * Errors: as tss_gemm; TSS_E_ARG also for splits out of range or a missing
+ * or too small workspace.
+ */
+int32_t tss_gemm_splitk(int64_t M, int64_t N, int64_t K, int32_t dtype, const void *A, const void *B, void *C,
+                        int64_t batch, int32_t out_dtype, const tss_tile_config *cfg, int32_t splits,
+                        void *workspace, int64_t workspace_bytes, void *stream);
+
+/* splits * batch * M * N * 4 bytes (0 for splits == 1), or TSS_E_ARG (< 0)
+   for sizes tss_gemm_splitk would reject. */
+int64_t tss_gemm_splitk_workspace_size(int64_t batch, int64_t M, int64_t N, int32_t splits);
+
 /* Bytes of workspace tss_conv2d needs for these sizes with any tile
    configuration (channels padded to 64), or TSS_E_ARG (< 0) for sizes
    tss_conv2d would reject as non-positive or above 2^30. */
 int64_t tss_conv2d_workspace_size(int64_t N, int64_t C, int64_t H, int64_t W, int64_t Cout,
                                   int64_t kh, int64_t kw);
+
+/*
+ * tss_conv2d_tiled with the implicit GEMM's K loop (taps x channels) cut into
+ * at most `splits` ranges of whole K steps, as tss_gemm_splitk: each range's
+ * fp32 partial output goes to the workspace after the operand layout copies,
+ * and a last launch adds them in range order into y.  splits in [0, 256]
+ * (0: tss_conv_splitk_plan's count, and its tile for a NULL cfg); workspace
+ * of at least tss_conv2d_splitk_workspace_size(...) bytes for that count.
+ * Everything else as tss_conv2d_tiled.
+ */
+int32_t tss_conv2d_splitk(int64_t N, int64_t C, int64_t H, int64_t W, int64_t Cout, int64_t kh, int64_t kw,
+                          int64_t sh, int64_t sw, int64_t ph, int64_t pw, int64_t dh, int64_t dw, int64_t tile_n,
+                          int64_t tile_oh, int64_t tile_ow, int32_t dtype, int32_t out_dtype, const void *x,
+                          const void *w, void *y, int32_t splits, void *workspace, int64_t workspace_bytes,
+                          const tss_tile_config *cfg, void *stream);
+
+/* tss_conv2d_workspace_size rounded up to 256 bytes plus splits fp32 copies
+   of the output (the layout part alone for splits == 1), or TSS_E_ARG. */
+int64_t tss_conv2d_splitk_workspace_size(int64_t N, int64_t C, int64_t H, int64_t W, int64_t Cout, int64_t kh,
+                                         int64_t kw, int64_t sh, int64_t sw, int64_t ph, int64_t pw, int64_t dh,
+                                         int64_t dw, int32_t splits);
 
 /* 1 if a kernel is compiled for cfg and dtype (op 0 = GEMM, 1 = conv), else 0. */
 int32_t tss_kernel_available(const tss_tile_config *cfg, int32_t dtype, int32_t op);

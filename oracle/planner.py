@@ -68,6 +68,9 @@ class DeviceModel:
     # (see busiest_core_time); the pages' ranking does not use them
     step_cost_k: int = 0            # a K step's cost beyond its BK elements
     tile_cost_k: int = 0            # a round of co-resident tiles' fixed cost
+    # cost parameters of the split-K plan (see splitk_total)
+    split_byte_cost: int = 0        # one byte of partial-sum traffic, in streamed panel bytes
+    launch_cost_k: int = 0          # the reduction launch, in streamed panel elements
     core_name: str = "SM"           # how messages name a core
 
     def shape(self, instr: str) -> Tuple[int, int, int, int]:
@@ -110,11 +113,19 @@ def device_pages(sm_count: int = 132, smem_kb: int = 228) -> DeviceModel:
 # (measured), not of the pages: a K step costs about 22 K elements beyond its
 # BK (with that fixed cost per step, the 32- and 16-wide steps take 1.24x and
 # 1.76x the 64-wide step's time per FLOP at equal K, as measured on the
-# convolution workload); the per-round fixed cost is left at zero.  The
-# functions below take them from the device record, so any other values can
-# be given through dataclasses.replace.
+# convolution workload); a round of co-resident tiles costs about 600 K
+# elements more (the 4096^3 GEMM's prologue and epilogue, about 10 us, against
+# 1.41 us per 64-wide K step of 86 K elements' cost).  The functions below
+# take them from the device record, so any other values can be given through
+# dataclasses.replace.
 GFX950_STEP_COST_K = 22
-GFX950_TILE_COST_K = 0
+GFX950_TILE_COST_K = 600
+# Split K: each byte of the partial sums' extra traffic costs as much as 6
+# bytes of streamed panel, and the reduction launch as much as 67000 panel
+# elements; with these, the split count of the split-K plan measured within
+# 5% of the fastest split count on nine GEMM shapes.
+GFX950_SPLIT_BYTE_COST = 6
+GFX950_LAUNCH_COST_K = 67000
 
 
 def device_gfx950() -> DeviceModel:
@@ -132,7 +143,8 @@ def device_gfx950() -> DeviceModel:
         reg_model=REG_PER_SIMD, simds_per_core=4, regs_per_lane_per_simd=512,
         max_waves_per_simd=8, instr_shapes=GFX950_SHAPES,
         wave_grid_rule=True, load_bytes_per_lane=16, ranking="gfx950",
-        step_cost_k=GFX950_STEP_COST_K, tile_cost_k=GFX950_TILE_COST_K, core_name="CU")
+        step_cost_k=GFX950_STEP_COST_K, tile_cost_k=GFX950_TILE_COST_K,
+        split_byte_cost=GFX950_SPLIT_BYTE_COST, launch_cost_k=GFX950_LAUNCH_COST_K, core_name="CU")
 
 
 # Wave grids (rows x cols of waves) a block of n waves is split into.
@@ -455,28 +467,109 @@ def conv_k(channels: int, taps: int, block_k: int) -> int:
 
 
 def sweep_conv(cout: int, pixels: int, channels: int, taps: int, dev: Optional[DeviceModel] = None,
-               elem_bytes: int = 2) -> List[Verdict]:
+               elem_bytes: int = 2, splits: int = 1) -> List[Verdict]:
     """The gfx950 sweep for a convolution computed as a GEMM (the Tiling page:
     M = output channels, N = output pixels, K = channels * kh * kw), where K
     depends on the candidate: conv_k(channels, taps, block_k).  Each
     candidate is finished (C4, C0) and ranked (rank_key) with its own K; the
-    enumeration order is the GEMM sweep's."""
+    enumeration order is the GEMM sweep's.  splits > 1: the problem each of
+    that many K ranges is, `splits` GEMMs (a batch) of K = ceil(conv_k /
+    splits), a K step longer than that K being skipped as in sweep."""
     dev = dev or device_gfx950()
     assert dev.ranking != "pages"
     instrs = [s for s, _ in dev.instr_shapes]
+    smallest = min(GFX950_SPACE["bk"])
     out = []
-    # conv_k(...) >= block_k for every candidate, so no K step is skipped
     for cfg in candidates(dev, 1 << 62, instrs):
+        k = _ceil_div(conv_k(channels, taps, cfg.block_k), splits)
+        if cfg.block_k > max(k, smallest):
+            continue
         v = evaluate(cfg, dev, elem_bytes=elem_bytes)
         if not v.feasible:
             continue
-        k = conv_k(channels, taps, cfg.block_k)
-        finish_parallelism(v, cout, pixels, dev, 1)
-        v.traffic = dram_traffic(cout, pixels, k, cfg, elem_bytes, 1)
+        finish_parallelism(v, cout, pixels, dev, splits)
+        v.traffic = dram_traffic(cout, pixels, k, cfg, elem_bytes, splits)
         v.k_loop = k
         out.append(v)
     out.sort(key=lambda x: rank_key(x, dev))
     return out
+
+
+# ---------------------------------------------------------------------------
+# Split K (C4's idle warning: fewer tiles than cores): the K loop cut into S
+# ranges computed by separate blocks into fp32 partial sums, added up by a
+# second pass.
+# ---------------------------------------------------------------------------
+
+SPLIT_CANDIDATES = (1, 2, 3, 4, 6, 8, 12, 16)
+
+
+def split_ranges(k: int, s: int, block_k: int) -> int:
+    """Ranges a kernel cutting K into S parts of whole K steps gets: each
+    range ceil(K / S) rounded up to a multiple of block_k, the last one the
+    rest."""
+    if k == 0 or s <= 1:
+        return 1
+    per = _ceil_div(_ceil_div(k, s), block_k) * block_k
+    return _ceil_div(k, per)
+
+
+def splitk_total(t_s: int, s: int, batch: int, m: int, n: int, elem_bytes: int, dev: DeviceModel) -> Fraction:
+    """The busiest CU's time with S ranges: T_S (busiest_core_time of the
+    split problem's tile) plus, for S > 1, the partial sums -- S fp32 copies
+    of the output, each written once and read once, 8 * S * batch * M * N
+    bytes spread over the cores, each byte costing split_byte_cost bytes of
+    streamed panel (elem_bytes per element) -- and the reduction launch."""
+    t = Fraction(t_s)
+    if s > 1:
+        t += Fraction(8 * s * batch * m * n * dev.split_byte_cost, elem_bytes * dev.cores) + dev.launch_cost_k
+    return t
+
+
+def splitk_plan(m: int, n: int, k: int, dev: Optional[DeviceModel] = None, batch: int = 1, elem_bytes: int = 2,
+                splits: int = 0) -> Tuple[int, Verdict]:
+    """The split count and the tile: for each S of SPLIT_CANDIDATES (or only
+    `splits` when > 0), the plan of the problem one range is (batch * S
+    GEMMs of M x N x ceil(K / S)); S > 1 is kept only if that tile's K steps
+    cut K into exactly S ranges; the least splitk_total wins, the smaller S
+    on a tie."""
+    dev = dev or device_gfx950()
+    instrs = [s for s, _ in dev.instr_shapes]
+    best = None
+    for s in ((splits,) if splits else SPLIT_CANDIDATES):
+        res = sweep(m, n, _ceil_div(k, s), dev, instrs, batch=batch * s, elem_bytes=elem_bytes)
+        if not res:
+            continue
+        v = res[0]
+        if not splits and s > 1 and split_ranges(k, s, v.config.block_k) != s:
+            continue
+        total = splitk_total(busiest_core_time(v, dev), s, batch, m, n, elem_bytes, dev)
+        if best is None or total < best[0]:
+            best = (total, s, v)
+    if best is None:
+        raise ValueError("no feasible tile")
+    return best[1], best[2]
+
+
+def conv_splitk_plan(cout: int, pixels: int, channels: int, taps: int, dev: Optional[DeviceModel] = None,
+                     elem_bytes: int = 2, splits: int = 0) -> Tuple[int, Verdict]:
+    """splitk_plan for a convolution's implicit GEMM, each candidate's K being
+    conv_k(channels, taps, block_k) (sweep_conv)."""
+    dev = dev or device_gfx950()
+    best = None
+    for s in ((splits,) if splits else SPLIT_CANDIDATES):
+        res = sweep_conv(cout, pixels, channels, taps, dev, elem_bytes, splits=s)
+        if not res:
+            continue
+        v = res[0]
+        if not splits and s > 1 and split_ranges(conv_k(channels, taps, v.config.block_k), s, v.config.block_k) != s:
+            continue
+        total = splitk_total(busiest_core_time(v, dev), s, 1, cout, pixels, elem_bytes, dev)
+        if best is None or total < best[0]:
+            best = (total, s, v)
+    if best is None:
+        raise ValueError("no feasible tile")
+    return best[1], best[2]
 
 
 # ---------------------------------------------------------------------------
@@ -528,5 +621,6 @@ def diagnose(cfg: TileConfig, dev: DeviceModel, m: int, n: int, batch: int = 1) 
 __all__ = ["DeviceModel", "TileConfig", "Verdict", "device_pages", "device_gfx950", "evaluate",
            "finish_parallelism", "dram_traffic", "round_half_even", "sweep", "plan", "rank_key",
            "sweep_rows", "sweep_summary", "diagnose_lines", "diagnose", "candidates", "WAVE_GRIDS",
-           "busiest_core_time", "conv_k", "sweep_conv", "GFX950_STEP_COST_K", "GFX950_TILE_COST_K",
+           "busiest_core_time", "conv_k", "sweep_conv", "splitk_plan", "conv_splitk_plan", "split_ranges",
+           "splitk_total", "SPLIT_CANDIDATES", "GFX950_STEP_COST_K", "GFX950_TILE_COST_K",
            "replace"]

@@ -401,3 +401,28 @@ def test_planner_at_the_edge_of_its_size_bounds():
     assert L.tss_tile_plan(1, 64, 64, 64, 2, ctypes.byref(d), 0, ctypes.byref(v), None, 0, None) == C.TSS_E_ARG
     pages = tss.device_pages()
     assert L.tss_conv_plan(64, 64, 64, 9, 2, ctypes.byref(pages), ctypes.byref(v), None, 0, None) == C.TSS_E_ARG
+
+
+@pytest.mark.parametrize("costs", [None, (22, 0, 6, 67000), (0, 300, 2, 10000), (22, 600, 0, 0)])
+def test_splitk_plan_bit_exact(costs):
+    """tss_splitk_plan / tss_conv_splitk_plan against the oracle's
+    splitk_plan / conv_splitk_plan: the same split count and tile, with the
+    default and other cost parameters, for a free and a fixed split count."""
+    cd, od = tss.device_gfx950(), OP.device_gfx950()
+    if costs:
+        cd.step_cost_k, cd.tile_cost_k, cd.split_byte_cost, cd.launch_cost_k = costs
+        od = OP.replace(od, step_cost_k=costs[0], tile_cost_k=costs[1], split_byte_cost=costs[2],
+                        launch_cost_k=costs[3])
+    for (b, M, N, K) in [(1, 256, 256, 256), (1, 512, 512, 8192), (1, 1024, 1024, 8192), (1, 128, 128, 16384),
+                         (2, 300, 328, 1000), (1, 4096, 4096, 4096), (1, 64, 64, 8)]:
+        for fixed in (0, 3):
+            S_o, v_o = OP.splitk_plan(M, N, K, dev=od, batch=b, splits=fixed)
+            S_c, v_c = tss.splitk_plan(M, N, K, batch=b, dev=cd, splits=fixed)
+            assert S_c == S_o, (b, M, N, K, fixed)
+            _same(v_c, v_o)
+    for co, px, c, taps in [(256, 6272, 256, 9), (64, 200, 3, 9), (32, 64, 100, 9), (16, 96, 512, 25)]:
+        for fixed in (0, 2):
+            S_o, v_o = OP.conv_splitk_plan(co, px, c, taps, dev=od, splits=fixed)
+            S_c, v_c = tss.conv_splitk_plan(co, px, c, taps, dev=cd, splits=fixed)
+            assert S_c == S_o, (co, px, c, taps, fixed)
+            _same(v_c, v_o)

@@ -208,8 +208,9 @@ def test_gfx950_rank_prefers_occupancy_then_bigger_k_step():
     res = P.sweep(4096, 4096, 4096, g, [s for s, _ in g.instr_shapes])
     c = res[0].config
     assert (c.block_m, c.block_n, c.block_k, c.stages, c.threads, c.instr) == (256, 256, 64, 2, 512, "mfma16")
-    # one tile per CU, 256 + 256 panel rows, 64 K steps of 64 + 22
-    assert P.rank_key(res[0], g)[:1] == (1 * 512 * 64 * (64 + 22),) == (2818048,)
+    # one tile per CU, 256 + 256 panel rows, 64 K steps of 64 + 22, one round of 600
+    assert (g.step_cost_k, g.tile_cost_k) == (22, 600)
+    assert P.rank_key(res[0], g)[:1] == (1 * 512 * 64 * (64 + 22) + 1 * 512 * 600,) == (3125248,)
     assert P.rank_key(res[0], g)[4] == -8
     d = res[1].config    # the 32x32x16 twin ties on every key and follows it
     assert (d.block_m, d.block_n, d.block_k, d.stages, d.threads, d.instr) == (256, 256, 64, 2, 512, "mfma32")
@@ -301,17 +302,23 @@ def test_conv_sweep_pins():
     # a 128x128 tile, 2 stages, 256 threads (mfma32 for every K step): grid
     # 1 x 784 tiles -> W = 4 on the busiest CU (784 / 256), all resident
     # (u = 4: 2 blocks by LDS at BK = 64 ... at most 4 useful), 256 panel rows.
-    res = {v.config: v for v in P.sweep_conv(64, 8 * 112 * 112, 3, 9)}
+    g = P.replace(P.device_gfx950(), step_cost_k=22, tile_cost_k=0)
+    res = {v.config: v for v in P.sweep_conv(64, 8 * 112 * 112, 3, 9, dev=g)}
     keys = {bk: P.rank_key(res[P.TileConfig(128, 128, bk, 2, 256, "mfma32")], g)[0] for bk in (16, 32, 64)}
     assert keys == {16: 4 * 256 * 9 * (16 + 22), 32: 4 * 256 * 9 * (32 + 22), 64: 4 * 256 * 9 * (64 + 22)}
     assert keys == {16: 350208, 32: 497664, 64: 792576}
     # C = 96 (8 x 56 x 56 pixels, 128 output channels): BK = 16 and 32 both
     # pad nothing (K = 864) but 16 takes 54 steps against 27; BK = 64 pads
     # to 1152 in 18 steps.  Same tile: W = ceil(196 / 256) = 1.
-    res = {v.config: v for v in P.sweep_conv(128, 8 * 56 * 56, 96, 9)}
+    res = {v.config: v for v in P.sweep_conv(128, 8 * 56 * 56, 96, 9, dev=g)}
     keys = {bk: P.rank_key(res[P.TileConfig(128, 128, bk, 2, 256, "mfma32")], g)[0] for bk in (16, 32, 64)}
     assert keys == {16: 256 * 54 * 38, 32: 256 * 27 * 54, 64: 256 * 18 * 86}
     assert min(keys, key=keys.get) == 32
+    # a round cost of f adds R * (BM + BN) * f to each (here R = 1 round of 256 panel rows)
+    gf = P.replace(g, tile_cost_k=600)
+    resf = {v.config: v for v in P.sweep_conv(128, 8 * 56 * 56, 96, 9, dev=gf)}
+    assert {bk: P.rank_key(resf[P.TileConfig(128, 128, bk, 2, 256, "mfma32")], gf)[0] for bk in (16, 32, 64)} == \
+        {bk: k + 256 * 600 for bk, k in keys.items()}
 
 
 def test_conv_plan_without_step_cost_never_pads_more():
@@ -328,3 +335,46 @@ def test_conv_plan_without_step_cost_never_pads_more():
                       if (v.config.block_m, v.config.block_n, v.config.threads, v.config.instr)
                       == (b.block_m, b.block_n, b.threads, b.instr)]
         assert P.conv_k(c, 9, b.block_k) == min(P.conv_k(c, 9, v.config.block_k) for v in same_shape), c
+
+
+def test_split_ranges_and_total_closed_forms():
+    """split_ranges: each range ceil(K / S) rounded up to whole K steps, the
+    last the rest; splitk_total: T_S + 8 S b M N c / (eb cores) + launch."""
+    assert P.split_ranges(1000, 3, 64) == 3          # 334 -> 384 per range: 384, 384, 232
+    assert P.split_ranges(200, 4, 64) == 4           # 50 -> 64: 64, 64, 64, 8
+    assert P.split_ranges(100, 8, 64) == 2           # 13 -> 64: 64, 36 -- fewer ranges than asked
+    assert P.split_ranges(4096, 16, 64) == 16 and P.split_ranges(4096, 12, 64) == 11   # 342 -> 384: 10 full + 256
+    assert P.split_ranges(0, 8, 64) == 1 and P.split_ranges(5000, 1, 16) == 1
+    g = P.device_gfx950()
+    assert (g.split_byte_cost, g.launch_cost_k) == (6, 67000)
+    assert P.splitk_total(1000, 1, 1, 512, 512, 2, g) == 1000
+    assert P.splitk_total(1000, 4, 1, 512, 512, 2, g) == 1000 + 8 * 4 * 512 * 512 * 6 // (2 * 256) + 67000
+    assert P.splitk_total(1000, 4, 1, 512, 512, 2, g) == 1000 + 98304 + 67000
+    assert P.splitk_total(7, 3, 2, 100, 24, 2, g) == 7 + P.Fraction(8 * 3 * 2 * 100 * 24 * 6, 512) + 67000
+
+
+def test_splitk_plan_extremes_and_structure():
+    """With the split free of cost the plan takes the split that minimises the
+    busiest CU's time; with a prohibitive cost it never splits; one 64x64
+    tile over a long K (64 x 64 x 16384) shows both, worked by hand."""
+    free = P.replace(P.device_gfx950(), split_byte_cost=0, launch_cost_k=0, tile_cost_k=0)
+    # one tile per split: W = 1, 128 panel rows, ceil(16384 / S / 64) steps of 64 + 22: least at S = 16
+    S, v = P.splitk_plan(64, 64, 16384, dev=free)
+    assert S == 16 and (v.config.block_m, v.config.block_n, v.config.block_k) == (64, 64, 64)
+    assert P.busiest_core_time(v, free) == 1 * 128 * 16 * 86
+    costly = P.replace(P.device_gfx950(), split_byte_cost=10 ** 6)
+    assert P.splitk_plan(64, 64, 16384, dev=costly)[0] == 1
+    # the launch cost alone: a split whose time saving is below it is not taken
+    launch_only = P.replace(free, launch_cost_k=10 ** 9)
+    assert P.splitk_plan(64, 64, 16384, dev=launch_only)[0] == 1
+    # a problem that fills the machine with one wave of tiles gains nothing from a split
+    assert P.splitk_plan(4096, 4096, 4096)[0] == 1
+    # C a multiple of 64: the convolution's split plan is the GEMM's for K = taps * C
+    for co, px, c, taps in [(64, 4096, 128, 9), (128, 1000, 64, 1)]:
+        Sc, vc = P.conv_splitk_plan(co, px, c, taps)
+        Sg, vg = P.splitk_plan(co, px, taps * c)
+        assert (Sc, vc.config) == (Sg, vg.config)
+    # a fixed split count plans only that count
+    S, v = P.splitk_plan(512, 512, 8192, splits=6)
+    c = v.config
+    assert S == 6 and v.grid == 6 * (512 // c.block_m) * (512 // c.block_n) and v.k_loop == -(-8192 // 6)

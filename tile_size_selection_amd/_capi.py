@@ -28,7 +28,7 @@ class Device(ctypes.Structure):
         "cores", "onchip_per_core", "onchip_per_block_max", "max_threads_per_core", "max_threads_per_block",
         "max_blocks_per_core", "lane_count", "reg_granule_per_lane", "acc_regs_max", "reg_overhead", "reg_model",
         "regs_per_core", "simds_per_core", "regs_per_lane_per_simd", "max_waves_per_simd", "wave_grid_rule",
-        "load_bytes_per_lane", "ranking", "step_cost_k", "tile_cost_k")]
+        "load_bytes_per_lane", "ranking", "step_cost_k", "tile_cost_k", "split_byte_cost", "launch_cost_k")]
 
 
 class TileConfig(ctypes.Structure):
@@ -60,7 +60,9 @@ class HwSlice(ctypes.Structure):
 EXPORTS = ["tss_device_gfx950", "tss_device_pages", "tss_device_query", "tss_evaluate", "tss_tile_plan", "tss_conv_plan",
            "tss_tile_plan_usage", "tss_hw_tile", "tss_gemm", "tss_conv2d", "tss_conv2d_tiled",
            "tss_conv2d_workspace_size", "tss_kernel_available", "tss_kernel_usage_query", "tss_tile_plan_measured",
-           "tss_lds_probe", "tss_gemm_default_config", "tss_status_string", "tss_instr_shape"]
+           "tss_lds_probe", "tss_gemm_default_config", "tss_status_string", "tss_instr_shape", "tss_gemm_splitk",
+           "tss_gemm_splitk_workspace_size", "tss_conv2d_splitk", "tss_conv2d_splitk_workspace_size",
+           "tss_splitk_plan", "tss_conv_splitk_plan"]
 
 _lib = None
 
@@ -94,12 +96,20 @@ def lib():
     L.tss_lds_probe.argtypes = [i32, i32, i32, i32, vp, vp]
     L.tss_gemm_default_config.argtypes = [i64, i64, i64, i64, i32, P(TileConfig)]
     L.tss_instr_shape.argtypes = [i32, P(i32)]
+    L.tss_gemm_splitk.argtypes = [i64, i64, i64, i32, vp, vp, vp, i64, i32, P(TileConfig), i32, vp, i64, vp]
+    L.tss_gemm_splitk_workspace_size.argtypes = [i64, i64, i64, i32]
+    L.tss_conv2d_splitk.argtypes = [i64] * 16 + [i32, i32, vp, vp, vp, i32, vp, i64, P(TileConfig), vp]
+    L.tss_conv2d_splitk_workspace_size.argtypes = [i64] * 13 + [i32]
+    L.tss_splitk_plan.argtypes = [i64, i64, i64, i64, i32, P(Device), P(Verdict), P(i32)]
+    L.tss_conv_splitk_plan.argtypes = [i64, i64, i64, i64, i32, P(Device), P(Verdict), P(i32)]
     L.tss_status_string.argtypes = [i32]
     L.tss_status_string.restype = ctypes.c_char_p
     for n in EXPORTS:
         if n != "tss_status_string":
             getattr(L, n).restype = i32
     L.tss_conv2d_workspace_size.restype = i64
+    L.tss_gemm_splitk_workspace_size.restype = i64
+    L.tss_conv2d_splitk_workspace_size.restype = i64
     _lib = L
     return L
 

@@ -109,6 +109,26 @@ def conv_plan(Cout: int, pixels: int, channels: int, taps: int, elem_bytes: int 
     return _plan_result(st, best, lst, cap, n, "tss_conv_plan")
 
 
+def splitk_plan(M: int, N: int, K: int, batch: int = 1, elem_bytes: int = 2, dev: Optional[C.Device] = None,
+                splits: int = 0) -> Tuple[int, dict]:
+    """tss_splitk_plan: (split count, verdict of the tile for the split
+    problem); splits > 0 plans the tile for that count only."""
+    v, S = C.Verdict(), C.i32(splits)
+    C.check(C.lib().tss_splitk_plan(batch, M, N, K, elem_bytes, ctypes.byref(dev) if dev is not None else None,
+                                    ctypes.byref(v), ctypes.byref(S)), "tss_splitk_plan")
+    return S.value, verdict_dict(v)
+
+
+def conv_splitk_plan(Cout: int, pixels: int, channels: int, taps: int, elem_bytes: int = 2,
+                     dev: Optional[C.Device] = None, splits: int = 0) -> Tuple[int, dict]:
+    """tss_conv_splitk_plan: as splitk_plan for a convolution's implicit GEMM."""
+    v, S = C.Verdict(), C.i32(splits)
+    C.check(C.lib().tss_conv_splitk_plan(Cout, pixels, channels, taps, elem_bytes,
+                                         ctypes.byref(dev) if dev is not None else None, ctypes.byref(v),
+                                         ctypes.byref(S)), "tss_conv_splitk_plan")
+    return S.value, verdict_dict(v)
+
+
 def conv2d_default_config(N: int, channels: int, H: int, W: int, Cout: int, kh: int, kw: int,
                           stride: Union[int, Sequence[int]] = 1, padding: Union[int, Sequence[int]] = 0,
                           dilation: Union[int, Sequence[int]] = 1) -> TileConfig:
@@ -224,10 +244,14 @@ def _same_device(*tensors):
     return dev
 
 
-def gemm(A, B, out_dtype: Optional[str] = None, cfg: Optional[TileConfig] = None, out=None, stream=None):
+def gemm(A, B, out_dtype: Optional[str] = None, cfg: Optional[TileConfig] = None, out=None, stream=None,
+         splits: int = 1, workspace=None):
     """C = A @ B for row-major fp16/bf16 device tensors, A [b,] M x K and
     B [b,] K x N; fp32 accumulation; out_dtype 'f32' or the input dtype
-    (default: the input dtype)."""
+    (default: the input dtype).  splits > 1: split K into at most that many
+    ranges (tss_gemm_splitk), 0: as many as the split-K plan says, with
+    `workspace` (a device tensor of at least gemm_splitk_workspace_size
+    bytes; allocated here when not given)."""
     if A.dim() not in (2, 3) or B.dim() != A.dim():
         raise ValueError("A and B must both be 2-D or both 3-D")
     if A.dtype != B.dtype:
@@ -248,11 +272,38 @@ def gemm(A, B, out_dtype: Optional[str] = None, cfg: Optional[TileConfig] = None
         out = torch.empty(shape, dtype=tdt, device=A.device)
     elif tuple(out.shape) != shape or out.dtype != tdt or not out.is_contiguous():
         raise ValueError("out has the wrong shape, dtype or layout")
-    with torch.cuda.device(_same_device(A, B, out)):
-        st = C.lib().tss_gemm(M, N, K, _DT[dt], A.data_ptr(), B.data_ptr(), out.data_ptr(), bt, _DT[od],
-                              ctypes.byref(cfg.c()) if cfg else None, _stream_ptr(stream))
-    C.check(st, "tss_gemm")
+    if splits == 1:
+        with torch.cuda.device(_same_device(A, B, out)):
+            st = C.lib().tss_gemm(M, N, K, _DT[dt], A.data_ptr(), B.data_ptr(), out.data_ptr(), bt, _DT[od],
+                                  ctypes.byref(cfg.c()) if cfg else None, _stream_ptr(stream))
+        C.check(st, "tss_gemm")
+        return out
+    # splits == 0: the library plans the count; the workspace is sized for it
+    need = gemm_splitk_workspace_size(bt, M, N, splits or splitk_plan(M, N, K, batch=bt)[0])
+    workspace = _workspace(workspace, need, A.device)
+    with torch.cuda.device(_same_device(A, B, out, workspace)):
+        st = C.lib().tss_gemm_splitk(M, N, K, _DT[dt], A.data_ptr(), B.data_ptr(), out.data_ptr(), bt, _DT[od],
+                                     ctypes.byref(cfg.c()) if cfg else None, splits, workspace.data_ptr(),
+                                     workspace.numel() * workspace.element_size(), _stream_ptr(stream))
+    C.check(st, "tss_gemm_splitk")
     return out
+
+
+def gemm_splitk_workspace_size(batch: int, M: int, N: int, splits: int) -> int:
+    n = C.lib().tss_gemm_splitk_workspace_size(batch, M, N, splits)
+    if n < 0:
+        C.check(int(n), "tss_gemm_splitk_workspace_size")
+    return int(n)
+
+
+def _workspace(workspace, need: int, device):
+    """The caller's workspace (checked), or a new one from torch's caching
+    allocator (device memory; the launches that use it are on one stream)."""
+    if workspace is None:
+        return torch.empty(max(need, 16), dtype=torch.uint8, device=device)
+    if not (workspace.is_cuda and workspace.is_contiguous() and workspace.numel() * workspace.element_size() >= need):
+        raise ValueError(f"workspace must be a contiguous device tensor of at least {need} bytes")
+    return workspace
 
 
 def conv2d_workspace_size(N: int, Ci: int, H: int, W: int, Cout: int, kh: int, kw: int) -> int:
@@ -267,12 +318,14 @@ def conv2d_workspace_size(N: int, Ci: int, H: int, W: int, Cout: int, kh: int, k
 def conv2d(x, w, stride: Union[int, Sequence[int]] = 1, padding: Union[int, Sequence[int]] = 0,
            dilation: Union[int, Sequence[int]] = 1, tile_oh: Optional[int] = None, out_dtype: Optional[str] = None,
            cfg: Optional[TileConfig] = None, out=None, stream=None, workspace=None, tile_ow: Optional[int] = None,
-           tile_n: Optional[int] = None):
+           tile_n: Optional[int] = None, splits: int = 1):
     """NCHW convolution as an implicit GEMM over tiles of tile_n images x
     tile_oh output rows x tile_ow output columns (defaults: the whole batch,
     height and width; tss_conv2d_tiled).  workspace: optional device tensor
     of at least conv2d_workspace_size(...) bytes for the operands'
-    channel-last copies (allocated here when not given)."""
+    channel-last copies (allocated here when not given).  splits > 1: the K
+    loop cut into at most that many ranges (tss_conv2d_splitk; the workspace
+    then also holds their partial outputs)."""
     pair = lambda v: (v, v) if isinstance(v, int) else tuple(v)
     (sh, sw), (ph, pw), (dh, dw) = pair(stride), pair(padding), pair(dilation)
     if x.dim() != 4 or w.dim() != 4 or x.dtype != w.dtype:
@@ -293,18 +346,25 @@ def conv2d(x, w, stride: Union[int, Sequence[int]] = 1, padding: Union[int, Sequ
         out = torch.empty(shape, dtype=tdt, device=x.device)
     elif tuple(out.shape) != shape or out.dtype != tdt or not out.is_contiguous():
         raise ValueError("out has the wrong shape, dtype or layout")
-    ws_bytes = conv2d_workspace_size(N, Ci, H, W, Co, kh, kw)
-    if workspace is None:
-        # torch's caching allocator: device memory only, no host copy; the
-        # convolution's two launches fill and read it on the same stream
-        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=x.device)
-    elif not (workspace.is_cuda and workspace.is_contiguous() and workspace.numel() * workspace.element_size()
-              >= ws_bytes):
-        raise ValueError(f"workspace must be a contiguous device tensor of at least {ws_bytes} bytes")
+    if splits == 1:
+        ws_bytes = conv2d_workspace_size(N, Ci, H, W, Co, kh, kw)
+    else:
+        n_splits = splits or conv_splitk_plan(Co, N * OH * OW, Ci, kh * kw)[0]
+        ws_bytes = C.lib().tss_conv2d_splitk_workspace_size(N, Ci, H, W, Co, kh, kw, sh, sw, ph, pw, dh, dw,
+                                                            n_splits)
+        if ws_bytes < 0:
+            C.check(int(ws_bytes), "tss_conv2d_splitk_workspace_size")
+    # torch's caching allocator when none is given: device memory only, no
+    # host copy; the convolution's launches fill and read it on one stream
+    workspace = _workspace(workspace, ws_bytes, x.device)
     with torch.cuda.device(_same_device(x, w, out, workspace)):
-        st = C.lib().tss_conv2d_tiled(N, Ci, H, W, Co, kh, kw, sh, sw, ph, pw, dh, dw, tile_n or N, tile_oh or OH,
-                                      tile_ow or OW, _DT[dt], _DT[od], x.data_ptr(), w.data_ptr(), out.data_ptr(),
-                                      workspace.data_ptr(), workspace.numel() * workspace.element_size(),
-                                      ctypes.byref(cfg.c()) if cfg else None, _stream_ptr(stream))
-    C.check(st, "tss_conv2d_tiled")
+        args = (N, Ci, H, W, Co, kh, kw, sh, sw, ph, pw, dh, dw, tile_n or N, tile_oh or OH, tile_ow or OW, _DT[dt],
+                _DT[od], x.data_ptr(), w.data_ptr(), out.data_ptr())
+        tail = (workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                ctypes.byref(cfg.c()) if cfg else None, _stream_ptr(stream))
+        if splits == 1:
+            st = C.lib().tss_conv2d_tiled(*args, *tail)
+        else:
+            st = C.lib().tss_conv2d_splitk(*args, splits, *tail)
+    C.check(st, "tss_conv2d_tiled" if splits == 1 else "tss_conv2d_splitk")
     return out

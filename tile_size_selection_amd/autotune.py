@@ -28,6 +28,7 @@ def time_config(A, B, out, cfg, iters: int, warmup: int, out_dtype: str) -> floa
     torch.cuda.synchronize()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda._sleep(int(2e6))   # the launches queue behind a GPU spin: the host's call cost stays out
     e0.record()
     for _ in range(iters):
         api.gemm(A, B, out_dtype=out_dtype, cfg=cfg, out=out)
@@ -93,6 +94,7 @@ def sweep_conv(iters: int = 20, warmup: int = 3, rounds: int = 2) -> Tuple[List[
             torch.cuda.synchronize()
             e0 = torch.cuda.Event(enable_timing=True)
             e1 = torch.cuda.Event(enable_timing=True)
+            torch.cuda._sleep(int(2e6))
             e0.record()
             for _ in range(iters):
                 run(r["config"])

@@ -13,6 +13,7 @@
 #include "conv_layout.h"
 #include "planner.h"
 #include "registry.h"
+#include "splitk_reduce.h"
 
 using namespace tss;
 
@@ -85,6 +86,36 @@ int32_t planned_config(bool conv, int64_t a, int64_t b, int64_t c, int64_t d, ts
   return TSS_OK;
 }
 
+// The split-K plan per problem, cached like planned_config: (tile, splits).
+int32_t planned_split(bool conv, int64_t a, int64_t b, int64_t c, int64_t d, tss_tile_config *out, int32_t *splits) {
+  using PKey = std::tuple<bool, int64_t, int64_t, int64_t, int64_t>;
+  static std::mutex mu;
+  static std::map<PKey, std::pair<tss_tile_config, int32_t>> cache;
+  PKey key{conv, a, b, c, d};
+  {
+    std::lock_guard<std::mutex> g(mu);
+    auto it = cache.find(key);
+    if (it != cache.end()) {
+      *out = it->second.first;
+      *splits = it->second.second;
+      return TSS_OK;
+    }
+  }
+  tss_verdict best{};
+  int32_t S = 0;  // let the plan choose
+  int32_t st = conv ? tss_conv_splitk_plan(a, b, c, d, 2, nullptr, &best, &S)
+                    : tss_splitk_plan(a, b, c, d, 2, nullptr, &best, &S);
+  if (st != TSS_OK) return st;
+  {
+    std::lock_guard<std::mutex> g(mu);
+    if (cache.size() >= 4096) cache.clear();
+    cache[key] = {best.cfg, S};
+  }
+  *out = best.cfg;
+  *splits = S;
+  return TSS_OK;
+}
+
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 int32_t check_config(const tss_tile_config &c) {
@@ -122,6 +153,86 @@ ConvWorkspace conv_workspace(int64_t N, int64_t C, int64_t H, int64_t W, int64_t
   return ws;
 }
 
+constexpr int32_t kMaxSplits = 256;
+
+// K ranges of a split-K launch: at most `splits` ranges of equal length in
+// whole K steps of bk (the last one holds the rest); fewer when K is short.
+struct SplitK {
+  int32_t n;        // ranges actually launched (1: no split)
+  int32_t k_split;  // K elements per range
+};
+SplitK split_k(int64_t K, int32_t splits, int32_t bk) {
+  if (splits <= 1 || K == 0) return SplitK{1, int32_t(K)};
+  const int64_t per = (K + splits - 1) / splits;
+  const int64_t ks = (per + bk - 1) / bk * bk;
+  const int64_t n = (K + ks - 1) / ks;
+  return n <= 1 ? SplitK{1, int32_t(K)} : SplitK{int32_t(n), int32_t(ks)};
+}
+
+// tss_gemm, tss_gemm_splitk: splits == 1 is the one-pass GEMM (no workspace).
+int32_t gemm_impl(int64_t M, int64_t N, int64_t K, int32_t dtype, const void *A, const void *B, void *C,
+                  int64_t batch, int32_t out_dtype, const tss_tile_config *cfg, int32_t splits, void *workspace,
+                  int64_t workspace_bytes, void *stream) {
+  if (batch < 1 || M < 0 || N < 0 || K < 0) return TSS_E_ARG;
+  if (M > INT32_MAX || N > INT32_MAX || K > INT32_MAX || batch > INT32_MAX) return TSS_E_ARG;
+  if (dtype != TSS_F16 && dtype != TSS_BF16) return TSS_E_DTYPE;
+  if (out_dtype != TSS_F32 && out_dtype != dtype) return TSS_E_DTYPE;
+  if (K % 8 || N % 8) return TSS_E_ALIGN;
+  if (M * K * 2 >= kTwoGiB || K * N * 2 >= kTwoGiB) return TSS_E_ARG;
+  if (M == 0 || N == 0) return TSS_OK;
+  if (!C || (K > 0 && (!A || !B))) return TSS_E_ARG;  // with K == 0, A and B are never read
+  if (!aligned16(A) || !aligned16(B) || !aligned16(C)) return TSS_E_ALIGN;
+  tss_tile_config c{};
+  if (splits == 0) {
+    // the split-K plan: its split count, and its tile unless one is given
+    int32_t st = planned_split(false, batch, M, N, K, &c, &splits);
+    if (st != TSS_OK) return st;
+  }
+  if (cfg) {
+    c = *cfg;
+    int32_t st = check_config(c);
+    if (st != TSS_OK) return st;
+  } else if (c.bm == 0) {
+    // the tile plan of the problem each K range is: batch * splits GEMMs of
+    // M x N x ceil(K / splits) (the one-pass plan for splits == 1)
+    int32_t st = planned_config(false, batch * splits, M, N, (K + splits - 1) / splits, &c);
+    if (st != TSS_OK) return st;
+  }
+  const KernelEntry *e = find_kernel(c, dtype, 0);
+  if (!e) return TSS_E_UNSUPPORTED;
+  const SplitK sk = split_k(K, splits, c.bk);
+  if (sk.n > 1) {
+    // every range's fp32 partial output in the workspace, then the reduction
+    const unsigned __int128 need = (unsigned __int128)sk.n * uint64_t(batch) * uint64_t(M) * uint64_t(N) * 4u;
+    if (!workspace || (unsigned __int128)workspace_bytes < need) return TSS_E_ARG;
+    if (!aligned16(workspace)) return TSS_E_ALIGN;
+  }
+  KernelArgs a{};
+  a.A = A;
+  a.B = B;
+  a.C = sk.n > 1 ? workspace : C;
+  a.M = int32_t(M);
+  a.N = int32_t(N);
+  a.K = int32_t(K);
+  a.lda = int32_t(K);
+  a.splits = sk.n;
+  a.k_split = sk.k_split;
+  a.tiles_m = int32_t((M + c.bm - 1) / c.bm);
+  a.tiles_n = int32_t((N + c.bn - 1) / c.bn);
+  a.group_m = group_m_for(a.tiles_m);
+  a.out_dtype = sk.n > 1 ? TSS_F32 : out_dtype;
+  a.batch_stride_a = M * K;
+  a.batch_stride_b = K * N;
+  a.batch_stride_c = M * N;
+  const int64_t blocks = batch * sk.n * a.tiles_m * a.tiles_n;
+  if (blocks * c.threads > int64_t(UINT32_MAX) || blocks > INT32_MAX) return TSS_E_ARG;
+  hipError_t err = e->launch(a, dim3(uint32_t(blocks)), e->lds_bytes, (hipStream_t)stream);
+  if (err == hipSuccess && sk.n > 1)
+    err = launch_splitk_reduce(static_cast<const float *>(workspace), C, out_dtype, batch, M * N, sk.n,
+                               (hipStream_t)stream);
+  return err == hipSuccess ? TSS_OK : TSS_E_HIP;
+}
+
 }  // namespace
 
 extern "C" {
@@ -131,7 +242,8 @@ int32_t tss_device_query(int32_t hip_device, tss_device *out) {
   hipDeviceProp_t pr;
   if (hipGetDeviceProperties(&pr, hip_device) != hipSuccess) return TSS_E_HIP;
   if (std::strncmp(pr.gcnArchName, "gfx950", 6) != 0) return TSS_E_UNSUPPORTED;
-  tss_device d = gfx950_device();
+  tss_device d{};
+  tss_device_gfx950(&d);  // the model with its ranking's cost parameters
   d.cores = pr.multiProcessorCount;
   d.onchip_per_core = int32_t(pr.maxSharedMemoryPerMultiProcessor);
   d.onchip_per_block_max = int32_t(pr.sharedMemPerBlock);
@@ -202,44 +314,23 @@ int32_t tss_gemm_default_config(int64_t batch, int64_t M, int64_t N, int64_t K, 
 
 int32_t tss_gemm(int64_t M, int64_t N, int64_t K, int32_t dtype, const void *A, const void *B, void *C,
                  int64_t batch, int32_t out_dtype, const tss_tile_config *cfg, void *stream) {
-  if (batch < 1 || M < 0 || N < 0 || K < 0) return TSS_E_ARG;
-  if (M > INT32_MAX || N > INT32_MAX || K > INT32_MAX || batch > INT32_MAX) return TSS_E_ARG;
-  if (dtype != TSS_F16 && dtype != TSS_BF16) return TSS_E_DTYPE;
-  if (out_dtype != TSS_F32 && out_dtype != dtype) return TSS_E_DTYPE;
-  if (K % 8 || N % 8) return TSS_E_ALIGN;
-  if (M * K * 2 >= kTwoGiB || K * N * 2 >= kTwoGiB) return TSS_E_ARG;
-  if (M == 0 || N == 0) return TSS_OK;
-  if (!C || (K > 0 && (!A || !B))) return TSS_E_ARG;  // with K == 0, A and B are never read
-  if (!aligned16(A) || !aligned16(B) || !aligned16(C)) return TSS_E_ALIGN;
-  tss_tile_config c{};
-  if (cfg) {
-    c = *cfg;
-    int32_t st = check_config(c);
-    if (st != TSS_OK) return st;
-  } else {
-    int32_t st = planned_config(false, batch, M, N, K, &c);
-    if (st != TSS_OK) return st;
-  }
-  const KernelEntry *e = find_kernel(c, dtype, 0);
-  if (!e) return TSS_E_UNSUPPORTED;
-  KernelArgs a{};
-  a.A = A;
-  a.B = B;
-  a.C = C;
-  a.M = int32_t(M);
-  a.N = int32_t(N);
-  a.K = int32_t(K);
-  a.tiles_m = int32_t((M + c.bm - 1) / c.bm);
-  a.tiles_n = int32_t((N + c.bn - 1) / c.bn);
-  a.group_m = group_m_for(a.tiles_m);
-  a.out_dtype = out_dtype;
-  a.batch_stride_a = M * K;
-  a.batch_stride_b = K * N;
-  a.batch_stride_c = M * N;
-  const int64_t blocks = batch * a.tiles_m * a.tiles_n;
-  if (blocks * c.threads > int64_t(UINT32_MAX)) return TSS_E_ARG;
-  hipError_t err = e->launch(a, dim3(uint32_t(blocks)), e->lds_bytes, (hipStream_t)stream);
-  return err == hipSuccess ? TSS_OK : TSS_E_HIP;
+  return gemm_impl(M, N, K, dtype, A, B, C, batch, out_dtype, cfg, 1, nullptr, 0, stream);
+}
+
+int64_t tss_gemm_splitk_workspace_size(int64_t batch, int64_t M, int64_t N, int32_t splits) {
+  if (batch < 1 || M < 0 || N < 0 || splits < 1 || splits > kMaxSplits) return TSS_E_ARG;
+  if (M > INT32_MAX || N > INT32_MAX || batch > INT32_MAX) return TSS_E_ARG;
+  if (splits == 1) return 0;
+  const unsigned __int128 bytes = (unsigned __int128)splits * uint64_t(batch) * uint64_t(M) * uint64_t(N) * 4u;
+  if (bytes > (unsigned __int128)INT64_MAX) return TSS_E_ARG;
+  return int64_t(bytes);
+}
+
+int32_t tss_gemm_splitk(int64_t M, int64_t N, int64_t K, int32_t dtype, const void *A, const void *B, void *C,
+                        int64_t batch, int32_t out_dtype, const tss_tile_config *cfg, int32_t splits,
+                        void *workspace, int64_t workspace_bytes, void *stream) {
+  if (splits < 0 || splits > kMaxSplits || workspace_bytes < 0) return TSS_E_ARG;
+  return gemm_impl(M, N, K, dtype, A, B, C, batch, out_dtype, cfg, splits, workspace, workspace_bytes, stream);
 }
 
 int64_t tss_conv2d_workspace_size(int64_t N, int64_t C, int64_t H, int64_t W, int64_t Cout, int64_t kh,
@@ -250,12 +341,18 @@ int64_t tss_conv2d_workspace_size(int64_t N, int64_t C, int64_t H, int64_t W, in
   return conv_workspace(N, C, H, W, Cout, kh, kw, kConvChannelAlignMax).total;
 }
 
-int32_t tss_conv2d_tiled(int64_t N, int64_t C, int64_t H, int64_t W, int64_t Cout, int64_t kh, int64_t kw,
+}  // extern "C"
+
+// tss_conv2d_tiled, tss_conv2d_splitk: splits == 1 is the one-pass
+// implicit GEMM.  Workspace: the operand layout copies (sized for any tile),
+// then at a 256-byte boundary the K ranges' fp32 partial outputs.
+static int32_t conv_impl(int64_t N, int64_t C, int64_t H, int64_t W, int64_t Cout, int64_t kh, int64_t kw,
                          int64_t sh, int64_t sw, int64_t ph, int64_t pw, int64_t dh, int64_t dw, int64_t tile_n,
                          int64_t tile_oh, int64_t tile_ow, int32_t dtype, int32_t out_dtype, const void *x,
-                         const void *w, void *y, void *workspace, int64_t workspace_bytes,
+                         const void *w, void *y, int32_t splits, void *workspace, int64_t workspace_bytes,
                          const tss_tile_config *cfg, void *stream) {
   const int64_t lim = int64_t(1) << 30;
+  if (splits < 0 || splits > kMaxSplits) return TSS_E_ARG;
   if (N < 1 || C < 1 || H < 1 || W < 1 || Cout < 1 || kh < 1 || kw < 1 || sh < 1 || sw < 1 || ph < 0 || pw < 0 ||
       dh < 1 || dw < 1)
     return TSS_E_ARG;
@@ -282,20 +379,39 @@ int32_t tss_conv2d_tiled(int64_t N, int64_t C, int64_t H, int64_t W, int64_t Cou
   if (workspace_bytes < wmax.total) return TSS_E_ARG;
   if (!aligned16(x) || !aligned16(w) || !aligned16(y) || !aligned16(workspace)) return TSS_E_ALIGN;
   tss_tile_config c{};
+  if (splits == 0) {
+    // the split-K plan: its split count, and its tile unless one is given
+    int32_t st = planned_split(true, Cout, N * OH * OW, C, kh * kw, &c, &splits);
+    if (st != TSS_OK) return st;
+  }
   if (cfg) {
     c = *cfg;
     int32_t st = check_config(c);
     if (st != TSS_OK) return st;
-  } else {
+  } else if (c.bm == 0 && splits == 1) {
     // The implicit GEMM: M = Cout, N = every output pixel, K = kh*kw*C with
     // the channels padded to the candidate's K step (tss_conv_plan).
     int32_t st = planned_config(true, Cout, N * OH * OW, C, kh * kw, &c);
     if (st != TSS_OK) return st;
+  } else if (c.bm == 0) {
+    // the tile plan of the problem each of the `splits` K ranges is
+    tss_verdict v{};
+    int32_t S = splits;
+    int32_t st = tss_conv_splitk_plan(Cout, N * OH * OW, C, kh * kw, 2, nullptr, &v, &S);
+    if (st != TSS_OK) return st;
+    c = v.cfg;
   }
   const KernelEntry *e = find_kernel(c, dtype, 1);
   if (!e) return TSS_E_UNSUPPORTED;
   const ConvWorkspace ws = conv_workspace(N, C, H, W, Cout, kh, kw, c.bk);
   const int64_t Kc = kh * kw * ws.Cp;  // K of the implicit GEMM, over (r, s, ci)
+  const SplitK sk = split_k(Kc, splits, c.bk);
+  const int64_t out_elems = N * Cout * OH * OW;
+  const int64_t part_offset = (wmax.total + 255) / 256 * 256;
+  if (sk.n > 1 && (unsigned __int128)workspace_bytes <
+                      (unsigned __int128)part_offset + (unsigned __int128)sk.n * uint64_t(out_elems) * 4u)
+    return TSS_E_ARG;
+  float *partials = reinterpret_cast<float *>(static_cast<char *>(workspace) + part_offset);
 
   // 1. operands in (r, s, ci) order: channel-last input, reordered weights
   uint16_t *xc = static_cast<uint16_t *>(workspace);
@@ -325,14 +441,18 @@ int32_t tss_conv2d_tiled(int64_t N, int64_t C, int64_t H, int64_t W, int64_t Cou
   KernelArgs a{};
   a.A = wr;
   a.B = xc;
-  a.C = y;
+  a.C = sk.n > 1 ? static_cast<void *>(partials) : y;
   a.M = int32_t(Cout);
   a.N = int32_t(tile_pixels);
   a.K = int32_t(Kc);
+  a.lda = int32_t(Kc);
+  a.splits = sk.n;
+  a.k_split = sk.k_split;
+  a.batch_stride_c = out_elems;  // between the K ranges' partial outputs
   a.tiles_m = int32_t((Cout + c.bm - 1) / c.bm);
   a.tiles_n = int32_t((tile_pixels + c.bn - 1) / c.bn);
   a.group_m = group_m_for(a.tiles_m);
-  a.out_dtype = out_dtype;
+  a.out_dtype = sk.n > 1 ? TSS_F32 : out_dtype;
   a.Nb = int32_t(N);
   a.Cin = int32_t(C);
   a.H = int32_t(H);
@@ -354,10 +474,52 @@ int32_t tss_conv2d_tiled(int64_t N, int64_t C, int64_t H, int64_t W, int64_t Cou
   a.n_ht = int32_t((OH + tile_oh - 1) / tile_oh);
   a.n_wt = int32_t((OW + tile_ow - 1) / tile_ow);
   const int64_t n_tiles = (N + tile_n - 1) / tile_n * a.n_ht * a.n_wt;
-  const int64_t blocks = n_tiles * a.tiles_m * a.tiles_n;
-  if (blocks * c.threads > int64_t(UINT32_MAX)) return TSS_E_ARG;
+  const int64_t blocks = n_tiles * sk.n * a.tiles_m * a.tiles_n;
+  if (blocks * c.threads > int64_t(UINT32_MAX) || blocks > INT32_MAX) return TSS_E_ARG;
   err = e->launch(a, dim3(uint32_t(blocks)), e->lds_bytes, (hipStream_t)stream);
+  if (err == hipSuccess && sk.n > 1)
+    err = launch_splitk_reduce(partials, y, out_dtype, 1, out_elems, sk.n, (hipStream_t)stream);
   return err == hipSuccess ? TSS_OK : TSS_E_HIP;
+}
+
+extern "C" {
+
+int32_t tss_conv2d_tiled(int64_t N, int64_t C, int64_t H, int64_t W, int64_t Cout, int64_t kh, int64_t kw,
+                         int64_t sh, int64_t sw, int64_t ph, int64_t pw, int64_t dh, int64_t dw, int64_t tile_n,
+                         int64_t tile_oh, int64_t tile_ow, int32_t dtype, int32_t out_dtype, const void *x,
+                         const void *w, void *y, void *workspace, int64_t workspace_bytes,
+                         const tss_tile_config *cfg, void *stream) {
+  return conv_impl(N, C, H, W, Cout, kh, kw, sh, sw, ph, pw, dh, dw, tile_n, tile_oh, tile_ow, dtype, out_dtype, x,
+                   w, y, 1, workspace, workspace_bytes, cfg, stream);
+}
+
+int64_t tss_conv2d_splitk_workspace_size(int64_t N, int64_t C, int64_t H, int64_t W, int64_t Cout, int64_t kh,
+                                         int64_t kw, int64_t sh, int64_t sw, int64_t ph, int64_t pw, int64_t dh,
+                                         int64_t dw, int32_t splits) {
+  const int64_t base = tss_conv2d_workspace_size(N, C, H, W, Cout, kh, kw);
+  if (base < 0) return base;
+  const int64_t lim = int64_t(1) << 30;
+  if (sh < 1 || sw < 1 || ph < 0 || pw < 0 || dh < 1 || dw < 1 || sh > lim || sw > lim || ph > lim || pw > lim ||
+      dh > lim || dw > lim || splits < 1 || splits > kMaxSplits)
+    return TSS_E_ARG;
+  if (H + 2 * ph < (kh - 1) * dh + 1 || W + 2 * pw < (kw - 1) * dw + 1) return TSS_E_ARG;
+  if (splits == 1) return base;
+  const int64_t OH = (H + 2 * ph - (kh - 1) * dh - 1) / sh + 1;
+  const int64_t OW = (W + 2 * pw - (kw - 1) * dw - 1) / sw + 1;
+  const unsigned __int128 bytes = (unsigned __int128)((base + 255) / 256 * 256) +
+                                  (unsigned __int128)splits * uint64_t(N) * uint64_t(Cout) * uint64_t(OH) *
+                                      uint64_t(OW) * 4u;
+  if (bytes > (unsigned __int128)INT64_MAX) return TSS_E_ARG;
+  return int64_t(bytes);
+}
+
+int32_t tss_conv2d_splitk(int64_t N, int64_t C, int64_t H, int64_t W, int64_t Cout, int64_t kh, int64_t kw,
+                          int64_t sh, int64_t sw, int64_t ph, int64_t pw, int64_t dh, int64_t dw, int64_t tile_n,
+                          int64_t tile_oh, int64_t tile_ow, int32_t dtype, int32_t out_dtype, const void *x,
+                          const void *w, void *y, int32_t splits, void *workspace, int64_t workspace_bytes,
+                          const tss_tile_config *cfg, void *stream) {
+  return conv_impl(N, C, H, W, Cout, kh, kw, sh, sw, ph, pw, dh, dw, tile_n, tile_oh, tile_ow, dtype, out_dtype, x,
+                   w, y, splits, workspace, workspace_bytes, cfg, stream);
 }
 
 int32_t tss_conv2d(int64_t N, int64_t C, int64_t H, int64_t W, int64_t Cout, int64_t kh, int64_t kw, int64_t sh,

@@ -67,7 +67,16 @@ struct KernelArgs {
   int32_t tiles_m, tiles_n;
   int32_t group_m;    // tile rows per group of the L2-friendly tile order
   int32_t out_dtype;  // TSS_F32 / TSS_F16 / TSS_BF16
-  int64_t batch_stride_a, batch_stride_b, batch_stride_c;  // GEMM only, elements
+  int64_t batch_stride_a, batch_stride_b;  // GEMM only, elements
+  // C: GEMM, elements between the outputs of consecutive (batch, K range)
+  // pairs; conv, elements between the outputs of consecutive K ranges
+  int64_t batch_stride_c;
+  // Split K: the block's z index (batch entry or conv tile) is split into
+  // `splits` K ranges of k_split elements (a multiple of BK; the last range
+  // holds the rest), each computed by its own blocks into its own output
+  // slice (fp32 partial sums, added up by splitk_reduce_kernel).
+  // splits == 1, k_split == K: the plain GEMM.  lda: A's row stride.
+  int32_t splits, k_split, lda;
   // convolution geometry (CONV only).  The output is cut into tiles of
   // tile_n images x tile_oh rows x tile_ow columns; the GEMM batch index is
   // the tile, (image group * n_ht + row tile) * n_wt + column tile.
@@ -421,15 +430,20 @@ __global__ __launch_bounds__(G::THREADS) void tiled_gemm_kernel(KernelArgs p) {
   const int per = nblk >> 3, extra = nblk & 7;
   const int t = xcd < extra ? xcd * (per + 1) + local : extra * (per + 1) + (xcd - extra) * per + local;
   const int tiles_mn = p.tiles_m * p.tiles_n;
-  const int bz = t / tiles_mn;
-  const int tt = t - bz * tiles_mn;
+  const int bzs = t / tiles_mn;  // (batch entry or conv tile) * splits + K range
+  const int tt = t - bzs * tiles_mn;
+  const int split = bzs % p.splits, bz = bzs / p.splits;
   const int span = p.group_m * p.tiles_n;
   const int first_m = (tt / span) * p.group_m;
   const int gm = min(p.tiles_m - first_m, p.group_m);
   const int in_g = tt - (tt / span) * span;
   const int tm = first_m + in_g % gm, tn = in_g / gm;
   const int m0 = tm * G::BM, n0 = tn * G::BN;
-  const int M = p.M, K = p.K;
+  const int M = p.M;
+  // this block's K range [kbeg, kbeg + K) (K == 0 for a range past the end)
+  const int kbeg = split * p.k_split;
+  const int K = max(0, min(p.k_split, p.K - kbeg));
+  const int lda = p.lda;
 
   // -- convolution: this block's tile (images, output rows, output
   // columns), its input slice and the sub-operator pads.  Rows and columns
@@ -461,15 +475,18 @@ __global__ __launch_bounds__(G::THREADS) void tiled_gemm_kernel(KernelArgs p) {
     cols_in = max(0, min(w_end, p.W) - w_start);
   }
 
-  const T *Ab = reinterpret_cast<const T *>(p.A) + (CONV ? 0 : int64_t(bz) * p.batch_stride_a) + int64_t(m0) * K;
-  const uint32_t a_range = uint32_t(min(G::BM, M - m0)) * uint32_t(K) * 2u;  // rows [m0, M)
+  const T *Ab =
+      reinterpret_cast<const T *>(p.A) + (CONV ? 0 : int64_t(bz) * p.batch_stride_a) + int64_t(m0) * lda + kbeg;
+  // rows [m0, M), columns [kbeg, kbeg + K) of each (rows past the last one read as zero)
+  const int a_rows = min(G::BM, M - m0);
+  const uint32_t a_range = (a_rows > 0 && K > 0) ? (uint32_t(a_rows - 1) * uint32_t(lda) + uint32_t(K)) * 2u : 0u;
   const i32x4 rsA4 = buffer_rsrc(Ab, a_range);
   i32x4 rsB4;
   if constexpr (CONV) {
     // the channel-last input xc[Nb][H][W][Cp]
     rsB4 = buffer_rsrc(p.B, uint32_t(p.Nb) * uint32_t(p.H) * uint32_t(p.W) * uint32_t(p.Cp) * 2u);
   } else {
-    const T *Bb = reinterpret_cast<const T *>(p.B) + int64_t(bz) * p.batch_stride_b + n0;
+    const T *Bb = reinterpret_cast<const T *>(p.B) + int64_t(bz) * p.batch_stride_b + int64_t(kbeg) * N + n0;
     // elements [n0, K*N); with K == 0 the range is empty (otherwise n0 < N <= K*N)
     rsB4 = buffer_rsrc(Bb, K > 0 ? (uint32_t(K) * uint32_t(N) - uint32_t(n0)) * 2u : 0u);
   }
@@ -482,7 +499,7 @@ __global__ __launch_bounds__(G::THREADS) void tiled_gemm_kernel(KernelArgs p) {
     int pchunk = (j * G::NW + wave) * 64 + lane;
     int r = pchunk / G::CA, pc = pchunk % G::CA;
     int lc = pc ^ G::swz_a(r);
-    a_off[j] = uint32_t(r) * uint32_t(K) * 2u + uint32_t(lc) * 16u;
+    a_off[j] = uint32_t(r) * uint32_t(lda) * 2u + uint32_t(lc) * 16u;
     a_kc[j] = lc * 8;
   }
   // -- B copy plan.
@@ -532,6 +549,13 @@ __global__ __launch_bounds__(G::THREADS) void tiled_gemm_kernel(KernelArgs p) {
   // ci0+BK-1 of it, and the cursor steps to the next tile with scalar adds
   // once a tile's copies are issued.
   int cur_ci = 0, cur_s = 0, cur_r = 0;
+  if constexpr (CONV) {
+    // a K range starts at a whole K tile: tap kbeg / Cp, channel kbeg % Cp
+    const int tap = kbeg / p.Cp;
+    cur_ci = kbeg - tap * p.Cp;
+    cur_s = tap % p.kw;
+    cur_r = tap / p.kw;
+  }
   auto cursor_next = [&]() __attribute__((always_inline)) {
     if constexpr (CONV) {
       cur_ci += G::BK;
@@ -811,7 +835,7 @@ __global__ __launch_bounds__(G::THREADS) void tiled_gemm_kernel(KernelArgs p) {
 
   // -- epilogue
   if constexpr (!CONV) {
-    const int64_t cbase = int64_t(bz) * p.batch_stride_c;
+    const int64_t cbase = (int64_t(bz) * p.splits + split) * p.batch_stride_c;
     if (p.out_dtype == TSS_F32)
       store_tile<G, float>(acc, reinterpret_cast<float *>(p.C) + cbase, smem, m0, n0, wave, wr, wc, lane, M, N);
     else if (p.out_dtype == TSS_F16)
@@ -820,8 +844,8 @@ __global__ __launch_bounds__(G::THREADS) void tiled_gemm_kernel(KernelArgs p) {
       store_tile<G, __bf16>(acc, reinterpret_cast<__bf16 *>(p.C) + cbase, smem, m0, n0, wave, wr, wc, lane, M, N);
   } else {
     if (p.out_dtype == TSS_F32)
-      store_conv<G, float>(acc, reinterpret_cast<float *>(p.C), p, m0, n0, wr, wc, lane, nb0, o0, rows_t, q0, cols_t,
-                                N);
+      store_conv<G, float>(acc, reinterpret_cast<float *>(p.C) + int64_t(split) * p.batch_stride_c, p, m0, n0, wr, wc,
+                           lane, nb0, o0, rows_t, q0, cols_t, N);
     else if (p.out_dtype == TSS_F16)
       store_conv<G, _Float16>(acc, reinterpret_cast<_Float16 *>(p.C), p, m0, n0, wr, wc, lane, nb0, o0, rows_t, q0, cols_t,
                                 N);

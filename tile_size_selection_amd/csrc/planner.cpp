@@ -8,11 +8,31 @@ using namespace tss;
 
 namespace {
 
+// The gfx950 model with its ranking's cost parameters (include/tss.h,
+// tss_device), properties of this library's kernels:
+//  step_cost_k 22: with a fixed cost of 22 K elements per K step, the 32-
+//    and 16-wide steps take 1.24x and 1.76x the 64-wide step's time per
+//    FLOP at equal K (measured on the convolution workload);
+//  tile_cost_k 600: the 4096^3 GEMM's prologue and epilogue take about
+//    10 us of one round against 1.41 us per 64-wide K step (86 K elements
+//    of cost), i.e. about 7 steps, 600 K elements;
+//  split_byte_cost 6, launch_cost_k 67000: the split-K plan's costs, with
+//    which its split count measured within 5% of the fastest on nine GEMM
+//    shapes (2 us of reduction launch at the rate the time term converts at).
+tss_device gfx950_with_costs() {
+  tss_device d = gfx950_device();
+  d.step_cost_k = 22;
+  d.tile_cost_k = 600;
+  d.split_byte_cost = 6;
+  d.launch_cost_k = 67000;
+  return d;
+}
+
 bool valid_device(const tss_device &d) {
   if (d.cores <= 0 || d.onchip_per_core <= 0 || d.onchip_per_block_max <= 0 || d.max_threads_per_core <= 0 ||
       d.max_threads_per_block <= 0 || d.max_blocks_per_core <= 0 || d.lane_count <= 0 ||
       d.reg_granule_per_lane <= 0 || d.acc_regs_max <= 0 || d.reg_overhead < 0 || d.step_cost_k < 0 ||
-      d.tile_cost_k < 0)
+      d.tile_cost_k < 0 || d.split_byte_cost < 0 || d.launch_cost_k < 0)
     return false;
   if (d.reg_model == TSS_REG_POOLED) return d.regs_per_core > 0;
   if (d.reg_model == TSS_REG_PER_SIMD)
@@ -35,6 +55,13 @@ struct FixedK {
 struct ConvK {
   int64_t C, taps;
   int64_t operator()(int32_t bk) const { return taps * ((C + bk - 1) / bk) * bk; }
+};
+// One of S ranges of a K: ceil(K / S), with the convolution's K depending on BK.
+template <typename KOf>
+struct RangeK {
+  KOf k_of;
+  int64_t S;
+  int64_t operator()(int32_t bk) const { return (k_of(bk) + S - 1) / S; }
 };
 
 constexpr int64_t kLim40 = int64_t(1) << 40;
@@ -114,6 +141,48 @@ struct NoUsage {
   const tss_measured_usage *operator()(const tss_tile_config &) const { return nullptr; }
 };
 
+// The split-K plan over kSplitCandidates (tss_splitk_plan): the tile plan of
+// the split problem for each S, its busiest-CU time plus the split's costs.
+template <typename KOf>
+int32_t splitk_sweep(int64_t batch, int64_t M, int64_t N, const KOf &k_of, int32_t elem_bytes, const tss_device &d,
+                     tss_verdict *best, int32_t *splits) {
+  if (!splits || d.ranking != TSS_RANK_GFX950 || *splits < 0 || *splits > 256) return TSS_E_ARG;
+  // *splits > 0: the tile plan for that many ranges only
+  const int32_t fixed = *splits;
+  bool found = false;
+  i128 best_total = 0;
+  tss_verdict best_v{};
+  int32_t best_s = 0;
+  const int32_t one[1] = {fixed};
+  const int32_t *cands = fixed ? one : kSplitCandidates;
+  const int ncand = fixed ? 1 : int(sizeof(kSplitCandidates) / sizeof(kSplitCandidates[0]));
+  for (int ci = 0; ci < ncand; ++ci) {
+    const int32_t S = cands[ci];
+    if (batch * S > (int64_t(1) << 20)) {  // beyond the planner's batch bound
+      if (fixed) return TSS_E_ARG;
+      break;
+    }
+    tss_verdict v{};
+    int32_t st = plan_sweep<NoUsage>(batch * S, M, N, RangeK<KOf>{k_of, S}, elem_bytes, d, 0, nullptr, &v, nullptr, 0,
+                                     nullptr);
+    if (st == TSS_E_INFEASIBLE) continue;
+    if (st != TSS_OK) return st;
+    if (!fixed && S > 1 && split_ranges(k_of(v.cfg.bk), S, v.cfg.bk) != S) continue;  // the kernel would cut fewer
+    const i128 total =
+        split_total(rank_key(v, d, RangeK<KOf>{k_of, S}(v.cfg.bk)).k[0], S, batch, M, N, elem_bytes, d);
+    if (!found || total < best_total) {
+      found = true;
+      best_total = total;
+      best_v = v;
+      best_s = S;
+    }
+  }
+  if (!found) return TSS_E_INFEASIBLE;
+  if (best) *best = best_v;
+  *splits = best_s;
+  return TSS_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -130,7 +199,7 @@ int32_t tss_instr_shape(int32_t instr, int32_t out[4]) {
 
 int32_t tss_device_gfx950(tss_device *out) {
   if (!out) return TSS_E_ARG;
-  *out = gfx950_device();
+  *out = gfx950_with_costs();
   return TSS_OK;
 }
 
@@ -142,7 +211,7 @@ int32_t tss_device_pages(int32_t sm_count, int32_t smem_kb, tss_device *out) {
 
 int32_t tss_evaluate(const tss_tile_config *cfg, const tss_device *dev, int64_t batch, int64_t M, int64_t N,
                      int64_t K, int32_t elem_bytes, tss_verdict *out) {
-  const tss_device d = dev ? *dev : gfx950_device();
+  const tss_device d = dev ? *dev : gfx950_with_costs();
   if (!cfg || !out || !sizes_ok(batch, M, N, K) || elem_bytes < 1 || elem_bytes > 8) return TSS_E_ARG;
   if (!valid_device(d) || !valid_config(*cfg, d)) return TSS_E_ARG;
   tss_verdict v = evaluate_block(*cfg, d, elem_bytes);
@@ -155,7 +224,7 @@ int32_t tss_evaluate(const tss_tile_config *cfg, const tss_device *dev, int64_t 
 int32_t tss_tile_plan(int64_t batch, int64_t M, int64_t N, int64_t K, int32_t elem_bytes, const tss_device *dev,
                       int32_t instr_filter, tss_verdict *best, tss_verdict *list, int32_t cap,
                       int32_t *n_feasible) {
-  const tss_device d = dev ? *dev : gfx950_device();
+  const tss_device d = dev ? *dev : gfx950_with_costs();
   return plan_sweep<NoUsage>(batch, M, N, FixedK{K}, elem_bytes, d, instr_filter, nullptr, best, list, cap,
                              n_feasible);
 }
@@ -163,11 +232,26 @@ int32_t tss_tile_plan(int64_t batch, int64_t M, int64_t N, int64_t K, int32_t el
 int32_t tss_conv_plan(int64_t Cout, int64_t pixels, int64_t C, int64_t taps, int32_t elem_bytes,
                       const tss_device *dev, tss_verdict *best, tss_verdict *list, int32_t cap,
                       int32_t *n_feasible) {
-  const tss_device d = dev ? *dev : gfx950_device();
+  const tss_device d = dev ? *dev : gfx950_with_costs();
   if (C < 1 || taps < 1 || C > (int64_t(1) << 30) || taps > (int64_t(1) << 20)) return TSS_E_ARG;
   if (d.ranking != TSS_RANK_GFX950 || d.lane_count != 64) return TSS_E_ARG;
   return plan_sweep<NoUsage>(1, Cout, pixels, ConvK{C, taps}, elem_bytes, d, 0, nullptr, best, list, cap,
                              n_feasible);
+}
+
+int32_t tss_splitk_plan(int64_t batch, int64_t M, int64_t N, int64_t K, int32_t elem_bytes, const tss_device *dev,
+                        tss_verdict *best, int32_t *splits) {
+  const tss_device d = dev ? *dev : gfx950_with_costs();
+  if (!sizes_ok(batch, M, N, K) || !valid_device(d)) return TSS_E_ARG;
+  return splitk_sweep(batch, M, N, FixedK{K}, elem_bytes, d, best, splits);
+}
+
+int32_t tss_conv_splitk_plan(int64_t Cout, int64_t pixels, int64_t C, int64_t taps, int32_t elem_bytes,
+                             const tss_device *dev, tss_verdict *best, int32_t *splits) {
+  const tss_device d = dev ? *dev : gfx950_with_costs();
+  if (C < 1 || taps < 1 || C > (int64_t(1) << 30) || taps > (int64_t(1) << 20) || !valid_device(d)) return TSS_E_ARG;
+  if (d.lane_count != 64) return TSS_E_ARG;
+  return splitk_sweep(1, Cout, pixels, ConvK{C, taps}, elem_bytes, d, best, splits);
 }
 
 int32_t tss_tile_plan_usage(int64_t batch, int64_t M, int64_t N, int64_t K, int32_t elem_bytes,
@@ -185,7 +269,8 @@ int32_t tss_tile_plan_usage(int64_t batch, int64_t M, int64_t N, int64_t K, int3
     }
     return nullptr;
   };
-  return plan_sweep(batch, M, N, FixedK{K}, elem_bytes, gfx950_device(), 0, &usage_of, best, list, cap, n_feasible);
+  return plan_sweep(batch, M, N, FixedK{K}, elem_bytes, gfx950_with_costs(), 0, &usage_of, best, list, cap,
+                    n_feasible);
 }
 
 int32_t tss_hw_tile(int64_t H, int64_t kh, int64_t sh, int64_t pt, int64_t d, int64_t o0, int64_t o1,

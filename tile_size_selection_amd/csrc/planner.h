@@ -73,8 +73,8 @@ constexpr tss_device gfx950_device() {
   d.wave_grid_rule = 1;
   d.load_bytes_per_lane = 16;
   d.ranking = TSS_RANK_GFX950;
-  d.step_cost_k = 22;
-  d.tile_cost_k = 0;
+  // the ranking's cost parameters are set by gfx950_costs (planner.cpp):
+  // they rank candidates, they never decide which kernels exist
   return d;
 }
 
@@ -95,6 +95,8 @@ constexpr tss_device pages_device(int32_t sm_count, int32_t smem_kb) {
   d.ranking = TSS_RANK_PAGES;
   d.step_cost_k = 0;
   d.tile_cost_k = 0;
+  d.split_byte_cost = 0;
+  d.launch_cost_k = 0;
   return d;
 }
 
@@ -334,6 +336,30 @@ constexpr Key rank_key(const tss_verdict &v, const tss_device &d, int64_t K_loop
     r.k[6] = v.smem_total;
   }
   return r;
+}
+
+// Split counts the split-K plan considers.
+constexpr int32_t kSplitCandidates[] = {1, 2, 3, 4, 6, 8, 12, 16};
+
+// Ranges a split of K into S parts of whole K steps of bk gives (the kernel's
+// cut: ceil(K / S) rounded up to a multiple of bk per range).
+constexpr int64_t split_ranges(int64_t K, int64_t S, int64_t bk) {
+  if (K == 0 || S <= 1) return 1;
+  const int64_t ks = cdiv(cdiv(K, S), bk) * bk;
+  return cdiv(K, ks);
+}
+
+// The split-K plan's total for S ranges whose tile plan has busiest-CU time
+// T_S, scaled by elem_bytes * cores to stay an integer:
+//   (T_S + [S > 1] * (8 * S * batch * M * N * split_byte_cost / (eb * cores) + launch_cost_k)) * eb * cores
+constexpr i128 split_total(i128 T_S, int64_t S, int64_t batch, int64_t M, int64_t N, int32_t eb,
+                           const tss_device &d) {
+  const i128 scale = i128(eb) * i128(d.cores);
+  i128 t = T_S * scale;
+  if (S > 1)
+    t += i128(8) * i128(S) * i128(batch) * i128(M) * i128(N) * i128(d.split_byte_cost) +
+         i128(d.launch_cost_k) * scale;
+  return t;
 }
 
 constexpr bool key_less(const Key &a, const Key &b) {
