@@ -45,7 +45,8 @@ enum {
   TSS_E_ALIGN = -3,        /* pointer or row stride not 16-byte aligned */
   TSS_E_INFEASIBLE = -4,   /* the tile config fails C1..C3 or fits no block on a CU */
   TSS_E_HIP = -5,          /* HIP runtime error (launch, device query) */
-  TSS_E_UNSUPPORTED = -6   /* feasible config with no compiled kernel */
+  TSS_E_UNSUPPORTED = -6,  /* feasible config with no compiled kernel */
+  TSS_E_SCRATCH = -7       /* needs more scratch than the library's static array holds */
 };
 
 /* ---- element types ------------------------------------------------------- */
@@ -398,6 +399,28 @@ int32_t tss_gemm_splitk(int64_t M, int64_t N, int64_t K, int32_t dtype, const vo
 /* splits * batch * M * N * 4 bytes (0 for splits == 1), or TSS_E_ARG (< 0)
    for sizes tss_gemm_splitk would reject. */
 int64_t tss_gemm_splitk_workspace_size(int64_t batch, int64_t M, int64_t N, int32_t splits);
+
+/*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc):
+ * tss_conv2d_splitk with its workspace (the operand layout copies and the
+ * K ranges' partial outputs) in a static device array of the library,
+ * TSS_SCRATCH_BYTES bytes per GPU, held from the first call on that GPU
+ * until the process ends.  Allocates nothing (no hipMalloc, no allocating
+ * library call); the array's address on the current device is looked up on
+ * the first call on that device.  Every call on one GPU uses the same array:
+ * calls that overlap on one GPU (other streams, other threads) race and must
+ * be ordered by the caller.  Arguments and results as tss_conv2d_splitk.
+ * Errors: as tss_conv2d_splitk; TSS_E_SCRATCH when the problem needs more
+ * than TSS_SCRATCH_BYTES (tss_conv2d_splitk_workspace_size for the split
+ * count used); TSS_E_HIP if the array's address cannot be read.
+ */
+#define TSS_SCRATCH_BYTES ((int64_t)64 << 20)
+int32_t tss_conv2d_splitk_noalloc(int64_t N, int64_t C, int64_t H, int64_t W, int64_t Cout, int64_t kh, int64_t kw,
+                                  int64_t sh, int64_t sw, int64_t ph, int64_t pw, int64_t dh, int64_t dw,
+                                  int64_t tile_n, int64_t tile_oh, int64_t tile_ow, int32_t dtype,
+                                  int32_t out_dtype, const void *x, const void *w, void *y, int32_t splits,
+                                  const tss_tile_config *cfg, void *stream);
 
 /* Bytes of workspace tss_conv2d needs for these sizes with any tile
    configuration (channels padded to 64), or TSS_E_ARG (< 0) for sizes

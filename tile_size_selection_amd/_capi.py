@@ -12,6 +12,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libtss.so")
 
 TSS_OK, TSS_E_ARG, TSS_E_DTYPE, TSS_E_ALIGN, TSS_E_INFEASIBLE, TSS_E_HIP, TSS_E_UNSUPPORTED = 0, -1, -2, -3, -4, -5, -6
+TSS_E_SCRATCH = -7
+TSS_SCRATCH_BYTES = 64 << 20
 TSS_F16, TSS_BF16, TSS_F32 = 1, 2, 3
 LDS_PATTERN = {"b32": 1, "b128": 2, "tr_b64": 3, "gemm_a": 4, "gemm_a_plain": 5, "gemm_b": 6, "gemm_b_plain": 7}
 INSTR = {"mfma32": 1, "mfma16": 2, "mma": 16, "wgmma": 17, "simt": 18}
@@ -62,7 +64,7 @@ EXPORTS = ["tss_device_gfx950", "tss_device_pages", "tss_device_query", "tss_eva
            "tss_conv2d_workspace_size", "tss_kernel_available", "tss_kernel_usage_query", "tss_tile_plan_measured",
            "tss_lds_probe", "tss_gemm_default_config", "tss_status_string", "tss_instr_shape", "tss_gemm_splitk",
            "tss_gemm_splitk_workspace_size", "tss_conv2d_splitk", "tss_conv2d_splitk_workspace_size",
-           "tss_splitk_plan", "tss_conv_splitk_plan"]
+           "tss_splitk_plan", "tss_conv_splitk_plan", "tss_conv2d_splitk_noalloc"]
 
 _lib = None
 
@@ -100,6 +102,7 @@ def lib():
     L.tss_gemm_splitk_workspace_size.argtypes = [i64, i64, i64, i32]
     L.tss_conv2d_splitk.argtypes = [i64] * 16 + [i32, i32, vp, vp, vp, i32, vp, i64, P(TileConfig), vp]
     L.tss_conv2d_splitk_workspace_size.argtypes = [i64] * 13 + [i32]
+    L.tss_conv2d_splitk_noalloc.argtypes = [i64] * 16 + [i32, i32, vp, vp, vp, i32, P(TileConfig), vp]
     L.tss_splitk_plan.argtypes = [i64, i64, i64, i64, i32, P(Device), P(Verdict), P(i32)]
     L.tss_conv_splitk_plan.argtypes = [i64, i64, i64, i64, i32, P(Device), P(Verdict), P(i32)]
     L.tss_status_string.argtypes = [i32]

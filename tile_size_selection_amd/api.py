@@ -306,6 +306,39 @@ def _workspace(workspace, need: int, device):
     return workspace
 
 
+def conv2d_noalloc(x, w, stride: Union[int, Sequence[int]] = 1, padding: Union[int, Sequence[int]] = 0,
+                   dilation: Union[int, Sequence[int]] = 1, tile_oh: Optional[int] = None,
+                   out_dtype: Optional[str] = None, cfg: Optional[TileConfig] = None, out=None, stream=None,
+                   tile_ow: Optional[int] = None, tile_n: Optional[int] = None, splits: int = 1):
+    """conv2d through tss_conv2d_splitk_noalloc: the workspace is the
+    library's static device array (no allocation by the library; `out` must
+    be given, so nothing is allocated here either).  Calls on one GPU share
+    the array and must not overlap."""
+    pair = lambda v: (v, v) if isinstance(v, int) else tuple(v)
+    (sh, sw), (ph, pw), (dh, dw) = pair(stride), pair(padding), pair(dilation)
+    if x.dim() != 4 or w.dim() != 4 or x.dtype != w.dtype:
+        raise ValueError("x must be NCHW and w OIHW, same dtype")
+    if out is None:
+        raise ValueError("out must be given")
+    N, Ci, H, W = x.shape
+    Co, _, kh, kw = w.shape
+    OH = (H + 2 * ph - (kh - 1) * dh - 1) // sh + 1
+    OW = (W + 2 * pw - (kw - 1) * dw - 1) // sw + 1
+    dt = _dt_of(x)
+    od = _dt_of(out)
+    if out_dtype is not None and out_dtype != od:
+        raise ValueError("out_dtype and out disagree")
+    if tuple(out.shape) != (N, Co, OH, OW) or not (x.is_contiguous() and w.is_contiguous() and out.is_contiguous()):
+        raise ValueError("x, w, out must be contiguous, out of shape (N, Cout, OH, OW)")
+    with torch.cuda.device(_same_device(x, w, out)):
+        st = C.lib().tss_conv2d_splitk_noalloc(N, Ci, H, W, Co, kh, kw, sh, sw, ph, pw, dh, dw, tile_n or N,
+                                               tile_oh or OH, tile_ow or OW, _DT[dt], _DT[od], x.data_ptr(),
+                                               w.data_ptr(), out.data_ptr(), splits,
+                                               ctypes.byref(cfg.c()) if cfg else None, _stream_ptr(stream))
+    C.check(st, "tss_conv2d_splitk_noalloc")
+    return out
+
+
 def conv2d_workspace_size(N: int, Ci: int, H: int, W: int, Cout: int, kh: int, kw: int) -> int:
     """Bytes of device workspace tss_conv2d needs for these sizes (Ci input
     channels)."""

@@ -42,7 +42,8 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++20", "-fPIC", "-Wall", "-Wno-u
 
 
 def sources():
-    return ([os.path.join(CSRC, "planner.cpp"), os.path.join(CSRC, "api.cpp"), os.path.join(CSRC, "lds_probe.hip")]
+    return ([os.path.join(CSRC, "planner.cpp"), os.path.join(CSRC, "api.cpp"), os.path.join(CSRC, "lds_probe.hip"),
+             os.path.join(CSRC, "noalloc.cpp")]
             + sorted(glob.glob(os.path.join(CSRC, "inst", "*.hip"))))
 
 

@@ -302,6 +302,7 @@ const char *tss_status_string(int32_t status) {
     case TSS_E_INFEASIBLE: return "tile configuration infeasible";
     case TSS_E_HIP: return "HIP runtime error";
     case TSS_E_UNSUPPORTED: return "no compiled kernel for this configuration";
+    case TSS_E_SCRATCH: return "the problem needs more scratch than the library's static array holds";
     default: return "unknown status";
   }
 }
