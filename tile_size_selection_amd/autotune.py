@@ -4,6 +4,7 @@ a hardware constraint, time every survivor on the device, keep the fastest).
 
     python -m tile_size_selection_amd.autotune --m 4096 --n 4096 --k 4096 [--out report.md]
     python -m tile_size_selection_amd.autotune --conv [--out report.md]     (the conv workload)
+    python -m tile_size_selection_amd.autotune summarize report1.md report2.md ...   (one row per report)
 
 Prints, for every feasible configuration, its measured time and TFLOP/s, its
 rank in the planner's order, and how the planner's first choice compares with
@@ -128,7 +129,28 @@ def report(M, N, K, batch, rows, summary) -> str:
     return "\n".join(lines) + "\n"
 
 
+def summarize(paths: List[str]) -> str:
+    """One table row per sweep report written by this module (--out): the
+    planner's choice, the fastest configuration and their time ratio."""
+    import re
+    rows = ["| M x N x K | planner's choice | us | fastest measured (planner rank) | us | planner / fastest |",
+            "|---|---|---|---|---|---|"]
+    for p in paths:
+        txt = open(p, encoding="utf-8").read()
+        shape = re.search(r"GEMM (\d+)x(\d+)x(\d+)x(\d+)", txt).groups()
+        plan = re.search(r"planner's choice: (.+?): ([\d.]+) us", txt).groups()
+        fast = re.search(r"fastest measured: (.+?) \(planner rank (\d+)\): ([\d.]+) us", txt).groups()
+        ratio = re.search(r"planner time / fastest time: ([\d.]+)", txt).group(1)
+        b, M, N, K = shape
+        rows.append(f"| {M} x {N} x {K}{'' if b == '1' else f' (batch {b})'} | {plan[0]} | {plan[1]} | "
+                    f"{fast[0]} ({fast[1]}) | {fast[2]} | {ratio} |")
+    return "\n".join(rows) + "\n"
+
+
 def main():
+    if len(sys.argv) > 1 and sys.argv[1] == "summarize":
+        sys.stdout.write(summarize(sys.argv[2:]))
+        return 0
     ap = argparse.ArgumentParser()
     ap.add_argument("--m", type=int, default=4096)
     ap.add_argument("--n", type=int, default=4096)
