@@ -161,3 +161,60 @@ def test_conv_padding_on_wrong_side_is_caught():
             for ow in range(y.shape[3]):
                 wrong[0, co, oh, ow] = np.sum(xp[0, :, oh:oh + 3, ow:ow + 3] * w[co])
     assert not np.array_equal(wrong, y)
+
+
+def _fails(fn) -> bool:
+    try:
+        fn()
+    except AssertionError:
+        return True
+    return False
+
+
+@pytest.mark.parametrize("mistake", ["rounds_as_tiles", "no_step_cost", "k_not_in_whole_steps", "panel_one_side"])
+def test_time_term_mistakes_are_caught(monkeypatch, mistake):
+    """The hand-worked closed forms of the gfx950 time term catch a round cost
+    charged per tile instead of per round, a dropped step cost, a K loop not
+    cut into whole steps, and a panel counting one operand only."""
+    import test_oracle_planner as T
+
+    def wrong(v, dev, k_loop=None):
+        c = v.config
+        k = v.k_loop if k_loop is None else k_loop
+        w = -(-v.grid // dev.cores)
+        if w == 0:
+            return 0
+        u = min(v.blocks_per_core, w)
+        rounds = -(-w // u)
+        steps = -(-k // c.block_k)
+        panel = c.block_m + c.block_n
+        step_cost = dev.step_cost_k
+        if mistake == "rounds_as_tiles":
+            rounds = w
+        elif mistake == "no_step_cost":
+            step_cost = 0
+        elif mistake == "k_not_in_whole_steps":
+            return w * panel * k + rounds * panel * dev.tile_cost_k
+        elif mistake == "panel_one_side":
+            panel = c.block_m
+        return w * panel * steps * (c.block_k + step_cost) + rounds * panel * dev.tile_cost_k
+    monkeypatch.setattr(P, "busiest_core_time", wrong)
+    assert _fails(T.test_gfx950_busiest_core_time_closed_forms)
+
+
+@pytest.mark.parametrize("mistake", ["partials_counted_for_two_ranges", "total_without_launch", "ranges_floor"])
+def test_split_mistakes_are_caught(monkeypatch, mistake):
+    """The split pins catch partial-sum traffic that stops growing past two
+    ranges, a dropped reduction launch, and ranges cut by floor instead of by
+    whole K steps."""
+    import test_oracle_planner as T
+    real_total, real_ranges = P.splitk_total, P.split_ranges
+    if mistake == "partials_counted_for_two_ranges":
+        monkeypatch.setattr(P, "splitk_total", lambda t, s, b, m, n, eb, dev: real_total(t, min(s, 2), b, m, n, eb, dev)
+                            if s > 1 else real_total(t, s, b, m, n, eb, dev))
+    elif mistake == "total_without_launch":
+        monkeypatch.setattr(P, "splitk_total", lambda t, s, b, m, n, eb, dev:
+                            real_total(t, s, b, m, n, eb, P.replace(dev, launch_cost_k=0)))
+    else:
+        monkeypatch.setattr(P, "split_ranges", lambda k, s, bk: max(1, k // (-(-k // s)) if s > 1 and k else 1))
+    assert _fails(T.test_split_ranges_and_total_closed_forms)
