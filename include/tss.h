@@ -372,6 +372,40 @@ int32_t tss_conv2d_tiled(int64_t N, int64_t C, int64_t H, int64_t W, int64_t Cou
                          int64_t workspace_bytes, const tss_tile_config *cfg, void *stream);
 
 /*
+ * The same convolution on channel-last tensors, read in place: input
+ * x[N][H][W][C] (NHWC), weights w[Cout][kh][kw][C] (OHWI), output
+ * y[N][OH][OW][Cout] (NHWC).  The implicit GEMM's K runs over (r, s, ci), so
+ * a channel-last pixel is a contiguous run of K: the kernel of
+ * tss_conv2d_tiled copies its B rows (8 channels of one input pixel per
+ * 16-byte chunk) and its A rows straight from x and w, one launch and no
+ * operand copies.  Each tap's channels are padded to the tile's K step as in
+ * tss_conv2d (the same K, the same plan, the same sum order); the padding is
+ * not in memory and reads as zero.  Same tiles, H/W tiling formulas and
+ * halo as tss_conv2d_tiled.
+ * Requirements: C a multiple of 8 (16-byte pixels); x, w, y 16-byte aligned.
+ * splits in [0, 256] as tss_conv2d_splitk: 1 = one pass (workspace unused,
+ * may be NULL); 0 = the split-K plan's count; > 1 = K cut into ranges whose
+ * fp32 partial outputs go to workspace (at least
+ * tss_conv2d_nhwc_workspace_size(..., S) bytes for the count S used,
+ * 16-byte aligned, owned by the caller).
+ * Everything else, and the errors, as tss_conv2d_splitk; TSS_E_ARG also for
+ * C not a multiple of 8.
+ */
+int32_t tss_conv2d_nhwc(int64_t N, int64_t C, int64_t H, int64_t W, int64_t Cout, int64_t kh,
+                        int64_t kw, int64_t sh, int64_t sw, int64_t ph, int64_t pw, int64_t dh,
+                        int64_t dw, int64_t tile_n, int64_t tile_oh, int64_t tile_ow, int32_t dtype,
+                        int32_t out_dtype, const void *x, const void *w, void *y, int32_t splits,
+                        void *workspace, int64_t workspace_bytes, const tss_tile_config *cfg,
+                        void *stream);
+
+/* splits * N * Cout * OH * OW * 4 bytes (0 for splits == 1), or TSS_E_ARG
+   (< 0) for splits outside [1, 256] or arguments tss_conv2d_nhwc would
+   reject on size alone. */
+int64_t tss_conv2d_nhwc_workspace_size(int64_t N, int64_t C, int64_t H, int64_t W, int64_t Cout,
+                                       int64_t kh, int64_t kw, int64_t sh, int64_t sw, int64_t ph,
+                                       int64_t pw, int64_t dh, int64_t dw, int32_t splits);
+
+/*
  * Split K: the same GEMM with its K loop cut into ranges computed by
  * separate blocks, for problems whose output tiles alone leave CUs idle (the
  * C4 "idle" warning of the tile_decision.py page: fewer tiles than CUs).

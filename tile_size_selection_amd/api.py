@@ -351,20 +351,36 @@ def conv2d_workspace_size(N: int, Ci: int, H: int, W: int, Cout: int, kh: int, k
 def conv2d(x, w, stride: Union[int, Sequence[int]] = 1, padding: Union[int, Sequence[int]] = 0,
            dilation: Union[int, Sequence[int]] = 1, tile_oh: Optional[int] = None, out_dtype: Optional[str] = None,
            cfg: Optional[TileConfig] = None, out=None, stream=None, workspace=None, tile_ow: Optional[int] = None,
-           tile_n: Optional[int] = None, splits: int = 1):
-    """NCHW convolution as an implicit GEMM over tiles of tile_n images x
-    tile_oh output rows x tile_ow output columns (defaults: the whole batch,
-    height and width; tss_conv2d_tiled).  workspace: optional device tensor
-    of at least conv2d_workspace_size(...) bytes for the operands'
-    channel-last copies (allocated here when not given).  splits > 1: the K
-    loop cut into at most that many ranges (tss_conv2d_splitk; the workspace
-    then also holds their partial outputs)."""
+           tile_n: Optional[int] = None, splits: int = 1, layout: Optional[str] = None):
+    """Convolution as an implicit GEMM over tiles of tile_n images x tile_oh
+    output rows x tile_ow output columns (defaults: the whole batch, height
+    and width).  x is (N, C, H, W), w (Cout, C, kh, kw), the result
+    (N, Cout, OH, OW), in one of two memory layouts:
+      layout "nchw": contiguous x, w and result (tss_conv2d_tiled; the
+        operands are first rewritten into channel-last copies in
+        `workspace`, an optional device tensor of at least
+        conv2d_workspace_size(...) bytes, allocated here when not given);
+      layout "nhwc": x, w and the result in torch's channels_last format
+        (stored [N][H][W][C], [Cout][kh][kw][C], [N][OH][OW][Cout]), read and
+        written in place (tss_conv2d_nhwc; C a multiple of 8; the workspace
+        holds only split-K partial outputs).
+    layout None: "nhwc" when x is channels_last and not also plain contiguous.
+    splits > 1: the K loop cut into at most that many ranges (the workspace
+    then also holds their partial outputs); 0: the split-K plan's count."""
     pair = lambda v: (v, v) if isinstance(v, int) else tuple(v)
     (sh, sw), (ph, pw), (dh, dw) = pair(stride), pair(padding), pair(dilation)
     if x.dim() != 4 or w.dim() != 4 or x.dtype != w.dtype:
-        raise ValueError("x must be NCHW and w OIHW, same dtype")
-    if not (x.is_cuda and w.is_cuda and x.is_contiguous() and w.is_contiguous()):
-        raise ValueError("x and w must be contiguous device tensors")
+        raise ValueError("x must be (N, C, H, W) and w (Cout, C, kh, kw), same dtype")
+    cl = torch.channels_last
+    if layout is None:
+        layout = "nhwc" if x.is_contiguous(memory_format=cl) and not x.is_contiguous() else "nchw"
+    if layout not in ("nchw", "nhwc"):
+        raise ValueError("layout must be 'nchw' or 'nhwc'")
+    nhwc = layout == "nhwc"
+    fmt = cl if nhwc else torch.contiguous_format
+    if not (x.is_cuda and w.is_cuda and x.is_contiguous(memory_format=fmt) and w.is_contiguous(memory_format=fmt)):
+        raise ValueError("x and w must be device tensors, contiguous in the " +
+                         ("channels_last" if nhwc else "NCHW") + " memory format")
     N, Ci, H, W = x.shape
     Co, Ci2, kh, kw = w.shape
     if Ci != Ci2:
@@ -376,9 +392,24 @@ def conv2d(x, w, stride: Union[int, Sequence[int]] = 1, padding: Union[int, Sequ
     tdt = {"f16": torch.float16, "bf16": torch.bfloat16, "f32": torch.float32}[od]
     shape = (N, Co, OH, OW)
     if out is None:
-        out = torch.empty(shape, dtype=tdt, device=x.device)
-    elif tuple(out.shape) != shape or out.dtype != tdt or not out.is_contiguous():
+        out = torch.empty(shape, dtype=tdt, device=x.device, memory_format=fmt)
+    elif tuple(out.shape) != shape or out.dtype != tdt or not out.is_contiguous(memory_format=fmt):
         raise ValueError("out has the wrong shape, dtype or layout")
+    if nhwc:
+        n_splits = splits or conv_splitk_plan(Co, N * OH * OW, Ci, kh * kw)[0]
+        ws_bytes = C.lib().tss_conv2d_nhwc_workspace_size(N, Ci, H, W, Co, kh, kw, sh, sw, ph, pw, dh, dw, n_splits)
+        if ws_bytes < 0:
+            C.check(int(ws_bytes), "tss_conv2d_nhwc_workspace_size")
+        workspace = _workspace(workspace, ws_bytes, x.device) if ws_bytes else workspace
+        with torch.cuda.device(_same_device(x, w, out, *(() if workspace is None else (workspace,)))):
+            st = C.lib().tss_conv2d_nhwc(
+                N, Ci, H, W, Co, kh, kw, sh, sw, ph, pw, dh, dw, tile_n or N, tile_oh or OH, tile_ow or OW, _DT[dt],
+                _DT[od], x.data_ptr(), w.data_ptr(), out.data_ptr(), splits,
+                workspace.data_ptr() if workspace is not None else None,
+                workspace.numel() * workspace.element_size() if workspace is not None else 0,
+                ctypes.byref(cfg.c()) if cfg else None, _stream_ptr(stream))
+        C.check(st, "tss_conv2d_nhwc")
+        return out
     if splits == 1:
         ws_bytes = conv2d_workspace_size(N, Ci, H, W, Co, kh, kw)
     else:

@@ -343,14 +343,18 @@ int64_t tss_conv2d_workspace_size(int64_t N, int64_t C, int64_t H, int64_t W, in
 
 }  // extern "C"
 
-// tss_conv2d_tiled, tss_conv2d_splitk: splits == 1 is the one-pass
-// implicit GEMM.  Workspace: the operand layout copies (sized for any tile),
-// then at a 256-byte boundary the K ranges' fp32 partial outputs.
+// tss_conv2d_tiled, tss_conv2d_splitk, tss_conv2d_nhwc: splits == 1 is the
+// one-pass implicit GEMM.  NCHW (nhwc false): the workspace holds the operand
+// layout copies (sized for any tile), then at a 256-byte boundary the K
+// ranges' fp32 partial outputs.  NHWC (nhwc true): x is [N][H][W][C], w is
+// [Cout][kh][kw][C] and y is [N][OH][OW][Cout]; the implicit GEMM reads x and
+// w in place (C a multiple of 8; the channels past C up to the K step's
+// multiple read as zero) and the workspace holds only the partial outputs.
 static int32_t conv_impl(int64_t N, int64_t C, int64_t H, int64_t W, int64_t Cout, int64_t kh, int64_t kw,
                          int64_t sh, int64_t sw, int64_t ph, int64_t pw, int64_t dh, int64_t dw, int64_t tile_n,
                          int64_t tile_oh, int64_t tile_ow, int32_t dtype, int32_t out_dtype, const void *x,
                          const void *w, void *y, int32_t splits, void *workspace, int64_t workspace_bytes,
-                         const tss_tile_config *cfg, void *stream) {
+                         const tss_tile_config *cfg, void *stream, bool nhwc = false) {
   const int64_t lim = int64_t(1) << 30;
   if (splits < 0 || splits > kMaxSplits) return TSS_E_ARG;
   if (N < 1 || C < 1 || H < 1 || W < 1 || Cout < 1 || kh < 1 || kw < 1 || sh < 1 || sw < 1 || ph < 0 || pw < 0 ||
@@ -365,8 +369,9 @@ static int32_t conv_impl(int64_t N, int64_t C, int64_t H, int64_t W, int64_t Cou
   const int64_t OW = (W + 2 * pw - (kw - 1) * dw - 1) / sw + 1;
   if (H + 2 * ph < (kh - 1) * dh + 1 || W + 2 * pw < (kw - 1) * dw + 1) return TSS_E_ARG;
   if (tile_oh < 1 || tile_oh > OH || tile_ow < 1 || tile_ow > OW || tile_n < 1 || tile_n > N) return TSS_E_ARG;
-  // sizes with the largest channel padding any tile can ask for
-  const ConvWorkspace wmax = conv_workspace(N, C, H, W, Cout, kh, kw, kConvChannelAlignMax);
+  if (nhwc && C % 8 != 0) return TSS_E_ARG;  // 16-byte pixels in place
+  // sizes with the largest channel padding any tile can ask for (NHWC: none)
+  const ConvWorkspace wmax = conv_workspace(N, C, H, W, Cout, kh, kw, nhwc ? 1 : kConvChannelAlignMax);
   // every operand, and both layout copies, addressable with 32-bit byte offsets
   if (N * C * H * W * 2 >= kTwoGiB || Cout * C * kh * kw * 2 >= kTwoGiB || wmax.xc_bytes >= kTwoGiB ||
       wmax.wr_bytes >= kTwoGiB || kh * kw * wmax.Cp > INT32_MAX)
@@ -375,9 +380,10 @@ static int32_t conv_impl(int64_t N, int64_t C, int64_t H, int64_t W, int64_t Cou
   if (N * Cout * OH * OW * out_bytes >= (int64_t(1) << 40)) return TSS_E_ARG;
   const int64_t tile_pixels = tile_n * tile_oh * tile_ow;
   if (tile_pixels > INT32_MAX) return TSS_E_ARG;
-  if (!x || !w || !y || !workspace) return TSS_E_ARG;
-  if (workspace_bytes < wmax.total) return TSS_E_ARG;
-  if (!aligned16(x) || !aligned16(w) || !aligned16(y) || !aligned16(workspace)) return TSS_E_ALIGN;
+  const int64_t layout_bytes = nhwc ? 0 : wmax.total;  // the operand copies in the workspace
+  if (!x || !w || !y) return TSS_E_ARG;
+  if (layout_bytes > 0 && (!workspace || workspace_bytes < layout_bytes)) return TSS_E_ARG;
+  if (!aligned16(x) || !aligned16(w) || !aligned16(y) || (workspace && !aligned16(workspace))) return TSS_E_ALIGN;
   tss_tile_config c{};
   if (splits == 0) {
     // the split-K plan: its split count, and its tile unless one is given
@@ -404,48 +410,57 @@ static int32_t conv_impl(int64_t N, int64_t C, int64_t H, int64_t W, int64_t Cou
   const KernelEntry *e = find_kernel(c, dtype, 1);
   if (!e) return TSS_E_UNSUPPORTED;
   const ConvWorkspace ws = conv_workspace(N, C, H, W, Cout, kh, kw, c.bk);
-  const int64_t Kc = kh * kw * ws.Cp;  // K of the implicit GEMM, over (r, s, ci)
+  const int64_t Kc = kh * kw * ws.Cp;       // K of the implicit GEMM, over (r, s, ci), ci padded to Cp
+  const int64_t Cs = nhwc ? C : ws.Cp;      // channels per pixel (and per tap of a weight row) in memory
   const SplitK sk = split_k(Kc, splits, c.bk);
   const int64_t out_elems = N * Cout * OH * OW;
-  const int64_t part_offset = (wmax.total + 255) / 256 * 256;
-  if (sk.n > 1 && (unsigned __int128)workspace_bytes <
-                      (unsigned __int128)part_offset + (unsigned __int128)sk.n * uint64_t(out_elems) * 4u)
+  const int64_t part_offset = (layout_bytes + 255) / 256 * 256;
+  if (sk.n > 1 && (!workspace || (unsigned __int128)workspace_bytes <
+                                     (unsigned __int128)part_offset +
+                                         (unsigned __int128)sk.n * uint64_t(out_elems) * 4u))
     return TSS_E_ARG;
-  float *partials = reinterpret_cast<float *>(static_cast<char *>(workspace) + part_offset);
+  float *partials = sk.n > 1 ? reinterpret_cast<float *>(static_cast<char *>(workspace) + part_offset) : nullptr;
 
-  // 1. operands in (r, s, ci) order: channel-last input, reordered weights
-  uint16_t *xc = static_cast<uint16_t *>(workspace);
-  uint16_t *wr = reinterpret_cast<uint16_t *>(static_cast<char *>(workspace) + ws.wr_offset);
-  LayoutArgs la{};
-  la.x = static_cast<const uint16_t *>(x);
-  la.xc = xc;
-  la.w = static_cast<const uint16_t *>(w);
-  la.wr = wr;
-  la.N = int32_t(N);
-  la.C = int32_t(C);
-  la.HW = int32_t(H * W);
-  la.Cp = int32_t(ws.Cp);
-  la.Cout = int32_t(Cout);
-  la.KHW = int32_t(kh * kw);
-  la.c_tiles = int32_t((ws.Cp + 63) / 64);
-  la.p_tiles = int32_t((H * W + 63) / 64);
-  const int64_t x_blocks = N * la.c_tiles * la.p_tiles;
-  const int64_t w_blocks = Cout;  // one block per output channel
-  if (x_blocks + w_blocks > int64_t(INT32_MAX)) return TSS_E_ARG;
-  hipLaunchKernelGGL(conv_layout_kernel, dim3(uint32_t(w_blocks + x_blocks)), dim3(kLayoutThreads), 0,
-                     (hipStream_t)stream, la);
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return TSS_E_HIP;
+  hipError_t err = hipSuccess;
+  const void *opA = w, *opB = x;
+  if (!nhwc) {
+    // 1. operands in (r, s, ci) order: channel-last input, reordered weights
+    uint16_t *xc = static_cast<uint16_t *>(workspace);
+    uint16_t *wr = reinterpret_cast<uint16_t *>(static_cast<char *>(workspace) + ws.wr_offset);
+    LayoutArgs la{};
+    la.x = static_cast<const uint16_t *>(x);
+    la.xc = xc;
+    la.w = static_cast<const uint16_t *>(w);
+    la.wr = wr;
+    la.N = int32_t(N);
+    la.C = int32_t(C);
+    la.HW = int32_t(H * W);
+    la.Cp = int32_t(ws.Cp);
+    la.Cout = int32_t(Cout);
+    la.KHW = int32_t(kh * kw);
+    la.c_tiles = int32_t((ws.Cp + 63) / 64);
+    la.p_tiles = int32_t((H * W + 63) / 64);
+    const int64_t x_blocks = N * la.c_tiles * la.p_tiles;
+    const int64_t w_blocks = Cout;  // one block per output channel
+    if (x_blocks + w_blocks > int64_t(INT32_MAX)) return TSS_E_ARG;
+    hipLaunchKernelGGL(conv_layout_kernel, dim3(uint32_t(w_blocks + x_blocks)), dim3(kLayoutThreads), 0,
+                       (hipStream_t)stream, la);
+    err = hipGetLastError();
+    if (err != hipSuccess) return TSS_E_HIP;
+    opA = wr;
+    opB = xc;
+  }
 
   // 2. the implicit GEMM over the tiles
   KernelArgs a{};
-  a.A = wr;
-  a.B = xc;
+  a.A = opA;
+  a.B = opB;
+  a.y_nhwc = nhwc ? 1 : 0;
   a.C = sk.n > 1 ? static_cast<void *>(partials) : y;
   a.M = int32_t(Cout);
   a.N = int32_t(tile_pixels);
   a.K = int32_t(Kc);
-  a.lda = int32_t(Kc);
+  a.lda = int32_t(kh * kw * Cs);  // a weight row in memory
   a.splits = sk.n;
   a.k_split = sk.k_split;
   a.batch_stride_c = out_elems;  // between the K ranges' partial outputs
@@ -469,6 +484,7 @@ static int32_t conv_impl(int64_t N, int64_t C, int64_t H, int64_t W, int64_t Cou
   a.OW = int32_t(OW);
   a.tile_oh = int32_t(tile_oh);
   a.Cp = int32_t(ws.Cp);
+  a.Cs = int32_t(Cs);
   a.tile_ow = int32_t(tile_ow);
   a.tile_n = int32_t(tile_n);
   a.n_ht = int32_t((OH + tile_oh - 1) / tile_oh);
@@ -520,6 +536,35 @@ int32_t tss_conv2d_splitk(int64_t N, int64_t C, int64_t H, int64_t W, int64_t Co
                           const tss_tile_config *cfg, void *stream) {
   return conv_impl(N, C, H, W, Cout, kh, kw, sh, sw, ph, pw, dh, dw, tile_n, tile_oh, tile_ow, dtype, out_dtype, x,
                    w, y, splits, workspace, workspace_bytes, cfg, stream);
+}
+
+int32_t tss_conv2d_nhwc(int64_t N, int64_t C, int64_t H, int64_t W, int64_t Cout, int64_t kh, int64_t kw, int64_t sh,
+                        int64_t sw, int64_t ph, int64_t pw, int64_t dh, int64_t dw, int64_t tile_n, int64_t tile_oh,
+                        int64_t tile_ow, int32_t dtype, int32_t out_dtype, const void *x, const void *w, void *y,
+                        int32_t splits, void *workspace, int64_t workspace_bytes, const tss_tile_config *cfg,
+                        void *stream) {
+  return conv_impl(N, C, H, W, Cout, kh, kw, sh, sw, ph, pw, dh, dw, tile_n, tile_oh, tile_ow, dtype, out_dtype, x,
+                   w, y, splits, workspace, workspace_bytes, cfg, stream, true);
+}
+
+int64_t tss_conv2d_nhwc_workspace_size(int64_t N, int64_t C, int64_t H, int64_t W, int64_t Cout, int64_t kh,
+                                       int64_t kw, int64_t sh, int64_t sw, int64_t ph, int64_t pw, int64_t dh,
+                                       int64_t dw, int32_t splits) {
+  const int64_t lim = int64_t(1) << 30;
+  if (N < 1 || C < 1 || H < 1 || W < 1 || Cout < 1 || kh < 1 || kw < 1 || sh < 1 || sw < 1 || ph < 0 || pw < 0 ||
+      dh < 1 || dw < 1 || splits < 1 || splits > kMaxSplits)
+    return TSS_E_ARG;
+  if (N > lim || C > lim || H > lim || W > lim || Cout > lim || kh > lim || kw > lim || sh > lim || sw > lim ||
+      ph > lim || pw > lim || dh > lim || dw > lim)
+    return TSS_E_ARG;
+  if (H + 2 * ph < (kh - 1) * dh + 1 || W + 2 * pw < (kw - 1) * dw + 1) return TSS_E_ARG;
+  if (splits == 1) return 0;
+  const int64_t OH = (H + 2 * ph - (kh - 1) * dh - 1) / sh + 1;
+  const int64_t OW = (W + 2 * pw - (kw - 1) * dw - 1) / sw + 1;
+  const unsigned __int128 bytes =
+      (unsigned __int128)splits * uint64_t(N) * uint64_t(Cout) * uint64_t(OH) * uint64_t(OW) * 4u;
+  if (bytes > (unsigned __int128)INT64_MAX) return TSS_E_ARG;
+  return int64_t(bytes);
 }
 
 int32_t tss_conv2d(int64_t N, int64_t C, int64_t H, int64_t W, int64_t Cout, int64_t kh, int64_t kw, int64_t sh,

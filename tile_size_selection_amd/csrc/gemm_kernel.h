@@ -32,9 +32,10 @@
 // A is the weight matrix Cout x (kh*kw*Cp) with K ordered (r, s, ci), loaded
 // exactly as the GEMM's A; B is the im2col matrix of one output tile (images
 // x output rows x output columns), stored in LDS transposed (pixels x K, laid
-// out like A) and copied HBM -> LDS from a channel-last copy of the input, 16
-// bytes (8 channels of one input pixel) per lane.  Both operand copies come
-// from conv_layout.h.  The batch index of the GEMM is the tile.  Each block
+// out like A) and copied HBM -> LDS from a channel-last input, 16 bytes (8
+// channels of one input pixel) per lane.  The operands are either the
+// caller's channel-last tensors (NHWC input, OHWI weights) or copies of NCHW /
+// OIHW ones made by conv_layout.h.  The batch index of the GEMM is the tile.  Each block
 // derives its input rows and columns and the sub-operator pads from the
 // Tiling page's H/W tiling formulas; chunks that fall in a pad or outside the
 // slice read as zero.
@@ -81,8 +82,10 @@ struct KernelArgs {
   // tile_n images x tile_oh rows x tile_ow columns; the GEMM batch index is
   // the tile, (image group * n_ht + row tile) * n_wt + column tile.
   int32_t Nb, Cin, H, W, kh, kw, sh, sw, ph, pw, dh, dw, OH, OW, tile_oh;
-  int32_t Cp;  // channels of the channel-last input copy: Cin rounded up to a multiple of BK
+  int32_t Cp;  // K per tap: Cin rounded up to a multiple of BK (a K tile is one tap)
+  int32_t Cs;  // channels per pixel in memory: B's pixel stride and A's stride per tap (Cp or Cin)
   int32_t tile_ow, tile_n, n_ht, n_wt;
+  int32_t y_nhwc;  // output y[Nb][OH][OW][Cout] (channel-last) instead of y[Nb][Cout][OH][OW]
 };
 
 // ---- small device helpers --------------------------------------------------
@@ -343,11 +346,14 @@ __device__ __forceinline__ void store_tile(const Acc (&acc)[G::TM][G::TN], O *C,
 
 // Convolution epilogue: row = output channel, column = pixel of the tile
 // (image nb0 + n_l, output row o0 + oh_l, output column q0 + ow_l); y is
-// NCHW.  The pixels a lane holds do not depend on the MFMA row, so each is
-// decoded once: the first of every group of 4 consecutive columns by
-// division, the next three by stepping (ow_l, oh_l, n) forward.  A lane's 4 consecutive columns are 4
-// consecutive y elements unless they straddle two images; where they are
-// (and the channel plane keeps them aligned) they go out as one vector store.
+// NCHW, or NHWC with p.y_nhwc.  The pixels a lane holds do not depend on the
+// MFMA row, so each is decoded once: the first of every group of 4
+// consecutive columns by division, the next three by stepping (ow_l, oh_l,
+// n) forward.  NCHW: a lane's 4 consecutive columns are 4 consecutive y
+// elements unless they straddle two images; where they are (and the channel
+// plane keeps them aligned) they go out as one vector store.  NHWC: the 16
+// (or 32) lanes of an MFMA column hold consecutive channels of one pixel, so
+// each store instruction writes runs of consecutive channels.
 template <typename G, typename O, typename Acc>
 __device__ __forceinline__ void store_conv(const Acc (&acc)[G::TM][G::TN], O *y, const KernelArgs &p, int m0, int n0,
                                            int wr, int wc, int lane, int nb0, int o0, int rows_t, int q0, int cols_t,
@@ -357,6 +363,8 @@ __device__ __forceinline__ void store_conv(const Acc (&acc)[G::TM][G::TN], O *y,
   using V4 = typename Vec4<O>::type;
   const int plane = rows_t * cols_t;
   const int64_t chan = int64_t(p.OH) * p.OW;
+  const bool nhwc = p.y_nhwc != 0;
+  const int64_t pix_mul = nhwc ? p.M : 1, co_mul = nhwc ? 1 : chan;  // y strides of a pixel and a channel
   int64_t off[G::TN][NACC];  // y offset of the pixel at channel 0, or -1 past the last pixel
   bool run[G::TN][NACC / 4];  // the group of 4 is one aligned vector in every channel
 #pragma unroll
@@ -372,7 +380,7 @@ __device__ __forceinline__ void store_conv(const Acc (&acc)[G::TM][G::TN], O *y,
 #pragma unroll
       for (int d = 0; d < 4; ++d) {
         off[j][e4 * 4 + d] =
-            pix < npix ? (int64_t(n) * p.M * chan + int64_t(o0 + oh) * p.OW + q0 + ow) : int64_t(-1);
+            pix < npix ? (int64_t(n) * p.M * chan + (int64_t(o0 + oh) * p.OW + q0 + ow) * pix_mul) : int64_t(-1);
         ++pix;
         if (++ow == cols_t) {
           ow = 0;
@@ -383,7 +391,7 @@ __device__ __forceinline__ void store_conv(const Acc (&acc)[G::TM][G::TN], O *y,
         }
       }
       const int64_t o = off[j][e4 * 4];
-      run[j][e4] = chan % 4 == 0 && o >= 0 && o % 4 == 0 && off[j][e4 * 4 + 3] == o + 3;
+      run[j][e4] = !nhwc && chan % 4 == 0 && o >= 0 && o % 4 == 0 && off[j][e4 * 4 + 3] == o + 3;
     }
 #pragma unroll
   for (int i = 0; i < G::TM; ++i) {
@@ -402,7 +410,7 @@ __device__ __forceinline__ void store_conv(const Acc (&acc)[G::TM][G::TN], O *y,
 #pragma unroll
           for (int d = 0; d < 4; ++d) {
             const int e = e4 * 4 + d;
-            if (off[j][e] >= 0) y[off[j][e] + int64_t(co) * chan] = convert_out<O>(acc[i][j][e]);
+            if (off[j][e] >= 0) y[off[j][e] + int64_t(co) * co_mul] = convert_out<O>(acc[i][j][e]);
           }
         }
       }
@@ -475,16 +483,21 @@ __global__ __launch_bounds__(G::THREADS) void tiled_gemm_kernel(KernelArgs p) {
     cols_in = max(0, min(w_end, p.W) - w_start);
   }
 
-  const T *Ab =
-      reinterpret_cast<const T *>(p.A) + (CONV ? 0 : int64_t(bz) * p.batch_stride_a) + int64_t(m0) * lda + kbeg;
-  // rows [m0, M), columns [kbeg, kbeg + K) of each (rows past the last one read as zero)
+  // GEMM: rows [m0, M), columns [kbeg, kbeg + K) of each (rows past the last
+  // one read as zero).  conv: rows [m0, M) whole; a K tile's columns come
+  // from the tap cursor (below)
+  const T *Ab = reinterpret_cast<const T *>(p.A) + (CONV ? 0 : int64_t(bz) * p.batch_stride_a) + int64_t(m0) * lda +
+                (CONV ? 0 : kbeg);
   const int a_rows = min(G::BM, M - m0);
-  const uint32_t a_range = (a_rows > 0 && K > 0) ? (uint32_t(a_rows - 1) * uint32_t(lda) + uint32_t(K)) * 2u : 0u;
+  const uint32_t a_range =
+      (a_rows > 0 && K > 0) ? (CONV ? uint32_t(a_rows) * uint32_t(lda) * 2u
+                                    : (uint32_t(a_rows - 1) * uint32_t(lda) + uint32_t(K)) * 2u)
+                            : 0u;
   const i32x4 rsA4 = buffer_rsrc(Ab, a_range);
   i32x4 rsB4;
   if constexpr (CONV) {
-    // the channel-last input xc[Nb][H][W][Cp]
-    rsB4 = buffer_rsrc(p.B, uint32_t(p.Nb) * uint32_t(p.H) * uint32_t(p.W) * uint32_t(p.Cp) * 2u);
+    // the channel-last input x[Nb][H][W][Cs]
+    rsB4 = buffer_rsrc(p.B, uint32_t(p.Nb) * uint32_t(p.H) * uint32_t(p.W) * uint32_t(p.Cs) * 2u);
   } else {
     const T *Bb = reinterpret_cast<const T *>(p.B) + int64_t(bz) * p.batch_stride_b + int64_t(kbeg) * N + n0;
     // elements [n0, K*N); with K == 0 the range is empty (otherwise n0 < N <= K*N)
@@ -534,7 +547,7 @@ __global__ __launch_bounds__(G::THREADS) void tiled_gemm_kernel(KernelArgs p) {
       const int ih = in_start - pt_sub + sr;      // its input row (= (o0 + oh_l)*sh - ph)
       const int iw = w_start - pl_sub + sc;       // its input column (= (q0 + ow_l)*sw - pw)
       // may wrap below zero for a pad corner; used only where the chunk is valid
-      b_off[j] = uint32_t((((nb0 + n) * p.H + ih) * p.W + iw) * p.Cp + lc * 8) * 2u;
+      b_off[j] = uint32_t((((nb0 + n) * p.H + ih) * p.W + iw) * p.Cs + lc * 8) * 2u;
       b_k[j] = lc * 8;
       b_row[j] = pix < N ? sr - pt_sub : (1 << 30);  // slice rows [pt', pt' + rows_in) hold data
       b_col[j] = sc - pl_sub;                        // slice columns [pl', pl' + cols_in) likewise
@@ -547,7 +560,8 @@ __global__ __launch_bounds__(G::THREADS) void tiled_gemm_kernel(KernelArgs p) {
   // conv: the refill cursor.  K tiles are copied in order 0, 1, 2, ...; Cp is
   // a multiple of BK, so each tile is one tap (r, s) and channels ci0 ..
   // ci0+BK-1 of it, and the cursor steps to the next tile with scalar adds
-  // once a tile's copies are issued.
+  // once a tile's copies are issued.  Channels at or past Cin (Cp > Cs = Cin:
+  // operands read in place) are not in memory and read as zero.
   int cur_ci = 0, cur_s = 0, cur_r = 0;
   if constexpr (CONV) {
     // a K range starts at a whole K tile: tap kbeg / Cp, channel kbeg % Cp
@@ -570,12 +584,21 @@ __global__ __launch_bounds__(G::THREADS) void tiled_gemm_kernel(KernelArgs p) {
   };
   // conv, the K tile at the cursor (starting at k0): byte offset of the copy
   // of B chunk j, or kOOB where the chunk lies in a pad, outside the tile's
-  // slice, past the last pixel or past K
+  // slice, past the last pixel, past the channels or past K
   auto conv_b_off = [&](int k0, int j) __attribute__((always_inline)) -> uint32_t {
     const int dr = cur_r * p.dh, ds = cur_s * p.dw;
-    const bool ok = k0 + b_k[j] < K && uint32_t(b_row[j] + dr) < uint32_t(rows_in) &&
+    const bool ok = k0 + b_k[j] < K && cur_ci + b_k[j] < p.Cin && uint32_t(b_row[j] + dr) < uint32_t(rows_in) &&
                     uint32_t(b_col[j] + ds) < uint32_t(cols_in);
-    return ok ? b_off[j] + uint32_t(((dr * p.W + ds) * p.Cp + cur_ci) * 2) : kOOB;
+    return ok ? b_off[j] + uint32_t(((dr * p.W + ds) * p.Cs + cur_ci) * 2) : kOOB;
+  };
+  // conv, the K tile at the cursor: the A row offset of its first column
+  // (tap (cur_r, cur_s), channel cur_ci; rows hold kh*kw*Cs elements), and
+  // whether A chunk j holds channels (and lies before K)
+  auto conv_a_soff = [&]() __attribute__((always_inline)) -> uint32_t {
+    return uint32_t(((cur_r * p.kw + cur_s) * p.Cs + cur_ci) * 2);
+  };
+  auto conv_a_ok = [&](int k0, int j) __attribute__((always_inline)) -> bool {
+    return k0 + a_kc[j] < K && cur_ci + a_kc[j] < p.Cin;
   };
   // LDS slots.  The plain ring: stage s holds A at s*STAGE_BYTES and B right
   // after it.  The A3 ring (GEMM, 2 stages): three A slots, then two B slots.
@@ -592,7 +615,9 @@ __global__ __launch_bounds__(G::THREADS) void tiled_gemm_kernel(KernelArgs p) {
   auto issue_one = [&](int kt, int sa, int sb, int j) __attribute__((always_inline)) {
     const int k0 = kt * G::BK;
     if (j < G::A_LOADS) {
-      copy_to_lds16(rsA4, a_off[j], uint32_t(k0) * 2u, (lds_void *)(a_slot(sa) + (j * G::NW + wave) * 1024));
+      lds_void *dst = (lds_void *)(a_slot(sa) + (j * G::NW + wave) * 1024);
+      if constexpr (CONV) copy_to_lds16(rsA4, conv_a_ok(k0, j) ? a_off[j] : kOOB, conv_a_soff(), dst);
+      else copy_to_lds16(rsA4, a_off[j], uint32_t(k0) * 2u, dst);
     } else {
       const int jb = j - G::A_LOADS;
       lds_void *dst = (lds_void *)(b_slot(sb) + (jb * G::NW + wave) * 1024);
@@ -608,8 +633,13 @@ __global__ __launch_bounds__(G::THREADS) void tiled_gemm_kernel(KernelArgs p) {
     } else {
       const int k0 = ckt * G::BK;
       if (j < G::A_LOADS) {
-        const uint32_t off = (k0 + a_kc[j] < K) ? a_off[j] + uint32_t(k0) * 2u : kOOB;
-        copy_to_lds16(rsA4, off, 0u, (lds_void *)(a_slot(sa) + (j * G::NW + wave) * 1024));
+        lds_void *dst = (lds_void *)(a_slot(sa) + (j * G::NW + wave) * 1024);
+        if constexpr (CONV) {
+          copy_to_lds16(rsA4, conv_a_ok(k0, j) ? a_off[j] : kOOB, conv_a_soff(), dst);
+        } else {
+          const uint32_t off = (k0 + a_kc[j] < K) ? a_off[j] + uint32_t(k0) * 2u : kOOB;
+          copy_to_lds16(rsA4, off, 0u, dst);
+        }
       } else {
         const int jb = j - G::A_LOADS;
         lds_void *dst = (lds_void *)(b_slot(sb) + (jb * G::NW + wave) * 1024);
