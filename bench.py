@@ -185,6 +185,21 @@ def main():
     _, conv_host_us = warm_up(launch_conv, 10, min_s=0.2)
     conv_ms, _, _ = timed(launch_conv, 200, conv_host_us, stream)
     conv_us = conv_ms * 1e3
+
+    # the same convolution on channel-last tensors (torch's channels_last
+    # format), read and written in place: one launch, no operand copies
+    cx = dx.contiguous(memory_format=torch.channels_last)
+    cwt = dwt.contiguous(memory_format=torch.channels_last)
+    yc = tss.conv2d(cx, cwt, cw.stride, cw.pad, cw.dil, tile_oh=cw.tile_oh, out_dtype=cw.out_dtype)
+    torch.cuda.synchronize()
+    nhwc_same = bool(torch.equal(yc.contiguous(), y))  # the same bits as the NCHW path
+
+    def launch_conv_nhwc():
+        tss.conv2d(cx, cwt, cw.stride, cw.pad, cw.dil, tile_oh=cw.tile_oh, out_dtype=cw.out_dtype, out=yc)
+
+    _, nhwc_host_us = warm_up(launch_conv_nhwc, 10, min_s=0.2)
+    nhwc_ms, _, _ = timed(launch_conv_nhwc, 200, nhwc_host_us, stream)
+    nhwc_us = nhwc_ms * 1e3
     OH = OW = 28
     conv_flops = 2 * cw.N * cw.Co * OH * OW * cw.C * cw.kh * cw.kw
     conv_cfg = tss.conv2d_default_config(cw.N, cw.C, cw.H, cw.W, cw.Co, cw.kh, cw.kw, cw.stride, cw.pad, cw.dil)
@@ -216,10 +231,15 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_F16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_F16_TFLOPS, 4),
                      "traffic": profiled_traffic(cfg_str)},
-        "conv": {"workload": "conv_f16_n8c256h56_k3s2p1 (tileOh 8, fp32 out)", "us": round(conv_us, 2),
+        "conv": {"workload": "conv_f16_n8c256h56_k3s2p1 (tileOh 8, fp32 out), NCHW x / OIHW w / NCHW y: "
+                             "layout pass + implicit GEMM", "us": round(conv_us, 2),
                  "tflops": round(conv_flops / (conv_us * 1e-6) / 1e12, 2),
                  "tile": f"{conv_cfg.bm}x{conv_cfg.bn}x{conv_cfg.bk}/s{conv_cfg.stages}/t{conv_cfg.threads}/"
                          f"{conv_cfg.instr}"},
+        "conv_nhwc": {"workload": "the same convolution, NHWC x / OHWI w / NHWC y (channels_last tensors) read "
+                                  "and written in place: the implicit GEMM alone", "us": round(nhwc_us, 2),
+                      "tflops": round(conv_flops / (nhwc_us * 1e-6) / 1e12, 2),
+                      "same_bits_as_nchw": nhwc_same},
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(A, B)

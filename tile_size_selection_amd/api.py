@@ -4,6 +4,7 @@ the stream."""
 from __future__ import annotations
 
 import ctypes
+import functools
 from dataclasses import dataclass
 from fractions import Fraction
 from typing import List, Optional, Sequence, Tuple, Union
@@ -127,6 +128,17 @@ def conv_splitk_plan(Cout: int, pixels: int, channels: int, taps: int, elem_byte
                                          ctypes.byref(dev) if dev is not None else None, ctypes.byref(v),
                                          ctypes.byref(S)), "tss_conv_splitk_plan")
     return S.value, verdict_dict(v)
+
+
+@functools.lru_cache(maxsize=4096)
+def _planned_splits(conv: bool, a: int, b: int, c: int, d: int) -> int:
+    """The split-K plan's count for sizing a workspace, cached per problem as
+    the library caches its own plan (planning evaluates every candidate at
+    every count, far longer than a launch).  conv: (Cout, pixels, C, taps);
+    else (batch, M, N, K)."""
+    if conv:
+        return conv_splitk_plan(a, b, c, d)[0]
+    return splitk_plan(b, c, d, batch=a)[0]
 
 
 def conv2d_default_config(N: int, channels: int, H: int, W: int, Cout: int, kh: int, kw: int,
@@ -279,7 +291,7 @@ def gemm(A, B, out_dtype: Optional[str] = None, cfg: Optional[TileConfig] = None
         C.check(st, "tss_gemm")
         return out
     # splits == 0: the library plans the count; the workspace is sized for it
-    need = gemm_splitk_workspace_size(bt, M, N, splits or splitk_plan(M, N, K, batch=bt)[0])
+    need = gemm_splitk_workspace_size(bt, M, N, splits or _planned_splits(False, bt, M, N, K))
     workspace = _workspace(workspace, need, A.device)
     with torch.cuda.device(_same_device(A, B, out, workspace)):
         st = C.lib().tss_gemm_splitk(M, N, K, _DT[dt], A.data_ptr(), B.data_ptr(), out.data_ptr(), bt, _DT[od],
@@ -396,7 +408,7 @@ def conv2d(x, w, stride: Union[int, Sequence[int]] = 1, padding: Union[int, Sequ
     elif tuple(out.shape) != shape or out.dtype != tdt or not out.is_contiguous(memory_format=fmt):
         raise ValueError("out has the wrong shape, dtype or layout")
     if nhwc:
-        n_splits = splits or conv_splitk_plan(Co, N * OH * OW, Ci, kh * kw)[0]
+        n_splits = splits or _planned_splits(True, Co, N * OH * OW, Ci, kh * kw)
         ws_bytes = C.lib().tss_conv2d_nhwc_workspace_size(N, Ci, H, W, Co, kh, kw, sh, sw, ph, pw, dh, dw, n_splits)
         if ws_bytes < 0:
             C.check(int(ws_bytes), "tss_conv2d_nhwc_workspace_size")
@@ -413,7 +425,7 @@ def conv2d(x, w, stride: Union[int, Sequence[int]] = 1, padding: Union[int, Sequ
     if splits == 1:
         ws_bytes = conv2d_workspace_size(N, Ci, H, W, Co, kh, kw)
     else:
-        n_splits = splits or conv_splitk_plan(Co, N * OH * OW, Ci, kh * kw)[0]
+        n_splits = splits or _planned_splits(True, Co, N * OH * OW, Ci, kh * kw)
         ws_bytes = C.lib().tss_conv2d_splitk_workspace_size(N, Ci, H, W, Co, kh, kw, sh, sw, ph, pw, dh, dw,
                                                             n_splits)
         if ws_bytes < 0:

@@ -212,12 +212,14 @@ def summarize(d: str, trace: str = None) -> str:
     return "\n".join(lines) + "\n"
 
 
-def trace_summary(path: str, last: int = 0) -> str:
+def trace_summary(path: str, last: int = 0, until: str = "", after: str = "") -> str:
     """Per-kernel durations of a rocprofv3 kernel trace: the run's results
     database (<dir>/<name>_results.db, the default output) or its
     kernel_trace.csv.  last > 0 adds, per kernel, the mean of its last `last`
     launches (the timed region of a benchmark run) and the mean gap between
-    them."""
+    them.  until / after (a kernel-name substring K): only the dispatches up
+    to the one right after K's last dispatch / only those starting after K's
+    last dispatch has ended (to split a run into phases)."""
     rows = []   # (name, start_ns, end_ns)
     if path.endswith(".db"):
         import sqlite3
@@ -228,6 +230,15 @@ def trace_summary(path: str, last: int = 0) -> str:
             for r in csv.DictReader(f):
                 rows.append((r["Kernel_Name"], int(r["Start_Timestamp"]), int(r["End_Timestamp"])))
         rows.sort(key=lambda r: r[1])
+    rows.sort(key=lambda r: r[1])
+    for key, keep_until in ((until, True), (after, False)):
+        if not key:
+            continue
+        idx = [i for i, r in enumerate(rows) if key in r[0]]
+        if not idx:
+            raise SystemExit(f"no kernel named like {key!r} in {path}")
+        i = idx[-1]
+        rows = rows[:i + 2] if keep_until else [r for r in rows if r[1] >= rows[i][2]]
     by = defaultdict(list)
     for name, st, en in rows:
         by[name].append((st, en))
@@ -258,9 +269,11 @@ def main():
     t = sub.add_parser("trace-summary")
     t.add_argument("path")
     t.add_argument("--last", type=int, default=0)
+    t.add_argument("--until", default="")
+    t.add_argument("--after", default="")
     a = ap.parse_args()
     if a.cmd == "trace-summary":
-        sys.stdout.write(trace_summary(a.path, a.last))
+        sys.stdout.write(trace_summary(a.path, a.last, a.until, a.after))
         return 0
     if a.cmd == "run":
         run(a.launches)
