@@ -153,3 +153,38 @@ def test_conv_nhwc_split_plan_and_errors():
         tss.conv2d(_cl(x), w.to(CUDA), 1, 1, 1, layout="nhwc")  # OIHW weights
     with pytest.raises(ValueError):
         tss.conv2d(x.to(CUDA), _cl(w), 1, 1, 1, layout="nhwc")  # NCHW input
+
+
+def test_random_conv_geometries_nhwc_exact():
+    """Random geometries (C a multiple of 8 up to 264, windows up to 7x7,
+    strides up to 4, dilations up to 3, pads up to 4, random tiles), each
+    with a random feasible tile configuration and dtype, channel-last
+    tensors: exact for integer inputs."""
+    rng = np.random.default_rng(2027)
+    cfgs = _configs()
+    bad = []
+    n = 0
+    while n < 40:
+        N, C, Co = int(rng.integers(1, 3)), 8 * int(rng.integers(1, 34)), int(rng.integers(1, 140))
+        H, W = int(rng.integers(1, 20)), int(rng.integers(1, 20))
+        kh, kw = int(rng.integers(1, 8)), int(rng.integers(1, 8))
+        st = (int(rng.integers(1, 5)), int(rng.integers(1, 5)))
+        pd = (int(rng.integers(0, 5)), int(rng.integers(0, 5)))
+        dl = (int(rng.integers(1, 4)), int(rng.integers(1, 4)))
+        if H + 2 * pd[0] < (kh - 1) * dl[0] + 1 or W + 2 * pd[1] < (kw - 1) * dl[1] + 1:
+            continue
+        OH = (H + 2 * pd[0] - (kh - 1) * dl[0] - 1) // st[0] + 1
+        OW = (W + 2 * pd[1] - (kw - 1) * dl[1] - 1) // st[1] + 1
+        toh, tow, tn = int(rng.integers(1, OH + 1)), int(rng.integers(1, OW + 1)), int(rng.integers(1, N + 1))
+        cfg = cfgs[int(rng.integers(0, len(cfgs)))]
+        dtype = ["f16", "bf16"][int(rng.integers(0, 2))]
+        x = draw((N, C, H, W), "int", -2, 2, dtype, 700 + n)
+        w = draw((Co, C, kh, kw), "int", -2, 2, dtype, 800 + n)
+        ref, _ = G.conv2d(x.double().numpy(), w.double().numpy(), st, pd, dl)
+        y = tss.conv2d(_cl(x), _cl(w), st, pd, dl, tile_oh=toh, tile_ow=tow, tile_n=tn, out_dtype="f32", cfg=cfg,
+                       layout="nhwc")
+        torch.cuda.synchronize()
+        if not (y.is_contiguous(memory_format=CL) and np.array_equal(to_f64(y), ref)):
+            bad.append((N, C, H, W, Co, kh, kw, st, pd, dl, toh, tow, tn, cfg, dtype))
+        n += 1
+    assert not bad, bad[:3]

@@ -376,7 +376,8 @@ def conv2d(x, w, stride: Union[int, Sequence[int]] = 1, padding: Union[int, Sequ
         (stored [N][H][W][C], [Cout][kh][kw][C], [N][OH][OW][Cout]), read and
         written in place (tss_conv2d_nhwc; C a multiple of 8; the workspace
         holds only split-K partial outputs).
-    layout None: "nhwc" when x is channels_last and not also plain contiguous.
+    layout None: "nhwc" when x and w are channels_last and not both also
+    plain contiguous (a tensor with H = W = 1 or C = 1 is both).
     splits > 1: the K loop cut into at most that many ranges (the workspace
     then also holds their partial outputs); 0: the split-K plan's count."""
     pair = lambda v: (v, v) if isinstance(v, int) else tuple(v)
@@ -385,7 +386,8 @@ def conv2d(x, w, stride: Union[int, Sequence[int]] = 1, padding: Union[int, Sequ
         raise ValueError("x must be (N, C, H, W) and w (Cout, C, kh, kw), same dtype")
     cl = torch.channels_last
     if layout is None:
-        layout = "nhwc" if x.is_contiguous(memory_format=cl) and not x.is_contiguous() else "nchw"
+        both_cl = x.is_contiguous(memory_format=cl) and w.is_contiguous(memory_format=cl)
+        layout = "nhwc" if both_cl and not (x.is_contiguous() and w.is_contiguous()) else "nchw"
     if layout not in ("nchw", "nhwc"):
         raise ValueError("layout must be 'nchw' or 'nhwc'")
     nhwc = layout == "nhwc"

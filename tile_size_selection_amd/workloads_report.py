@@ -8,8 +8,9 @@ device.  The launches of n back-to-back calls are captured in one HIP graph
 (so a small workload's time is the GPU's, not the Python call's), and HIP
 events on the stream time its replay: the median of 5 replays, divided by n.
 The graph's output is checked against the eager call's, bit for bit.  The
-convolution is the whole tss_conv2d call (operand layout pass + implicit
-GEMM).  The 4096^3 GEMM is also timed cold: a 512 MB device write before
+convolution is timed twice: the whole tss_conv2d call on NCHW tensors
+(operand layout pass + implicit GEMM) and the tss_conv2d_nhwc call on the
+same values as channel-last tensors (the implicit GEMM alone).  The 4096^3 GEMM is also timed cold: a 512 MB device write before
 every launch evicts its operands from the caches (L2 and the 256 MB cache in
 front of HBM), and HIP events bracket each launch alone (median of 30).
 """
@@ -111,8 +112,22 @@ def run_one(w, rounds: int = 5):
     n = max(20, min(2000, int(20000 / max(t1, 1.0))))
     us = _time_graph(fn, out, n, rounds)
     tf = flops / (us * 1e-6) / 1e12
-    return {"name": w.name, "us": us, "tflops": tf, "frac": tf / PEAK_TFLOPS, "launches": n,
-            "tile": f"{cfg.bm}x{cfg.bn}x{cfg.bk}/s{cfg.stages}/t{cfg.threads}/{cfg.instr}"}
+    r = {"name": w.name, "us": us, "tflops": tf, "frac": tf / PEAK_TFLOPS, "launches": n,
+         "tile": f"{cfg.bm}x{cfg.bn}x{cfg.bk}/s{cfg.stages}/t{cfg.threads}/{cfg.instr}"}
+    if not isinstance(w, ConvWorkload):
+        return [r]
+    # the same convolution on channel-last tensors: one launch, x and w read in place
+    cl = torch.channels_last
+    cx, cw = dx.contiguous(memory_format=cl), dw.contiguous(memory_format=cl)
+    yc = api.conv2d(cx, cw, w.stride, w.pad, w.dil, tile_oh=w.tile_oh, out_dtype=w.out_dtype)
+    fnc = lambda: api.conv2d(cx, cw, w.stride, w.pad, w.dil, tile_oh=w.tile_oh, out_dtype=w.out_dtype, out=yc)
+    torch.cuda.synchronize()
+    t1 = _time(fnc, 5)
+    n = max(20, min(2000, int(20000 / max(t1, 1.0))))
+    usc = _time_graph(fnc, yc, n, rounds)
+    tfc = flops / (usc * 1e-6) / 1e12
+    return [r, {"name": w.name + " (channel-last)", "us": usc, "tflops": tfc, "frac": tfc / PEAK_TFLOPS,
+                "launches": n, "tile": r["tile"]}]
 
 
 def main(argv=None):
@@ -121,10 +136,10 @@ def main(argv=None):
     a = ap.parse_args(argv)
     rows = []
     for i in sorted(WORKLOADS):
-        r = run_one(WORKLOADS[i])
-        rows.append(r)
-        print(f"{r['name']}: {r['us']:.2f} us, {r['tflops']:.1f} TFLOP/s ({100 * r['frac']:.1f}% of peak),"
-              f" tile {r['tile']}", flush=True)
+        for r in run_one(WORKLOADS[i]):
+            rows.append(r)
+            print(f"{r['name']}: {r['us']:.2f} us, {r['tflops']:.1f} TFLOP/s ({100 * r['frac']:.1f}% of peak),"
+                  f" tile {r['tile']}", flush=True)
     cold = cold_gemm_us(WORKLOADS[2])
     warm = next(r for r in rows if r["name"] == WORKLOADS[2].name)
     print(f"{WORKLOADS[2].name} cold (512 MB written before each launch): {cold:.2f} us "
