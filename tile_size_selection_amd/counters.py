@@ -71,6 +71,93 @@ def run(launches: int = 5):
     print(f"config {cfg.bm}x{cfg.bn}x{cfg.bk}/s{cfg.stages}/t{cfg.threads}/{cfg.instr}", flush=True)
 
 
+def run_conv(launches: int = 5):
+    """The convolution workload: `launches` NCHW calls (layout pass + implicit
+    GEMM), then `launches` calls on the same values as channel-last tensors
+    (the implicit GEMM alone), then `launches` 4096^3 GEMMs for comparison."""
+    import torch
+    from . import api
+    from .inputs import WORKLOADS
+    cw = WORKLOADS[5]
+    x, w = cw.make()
+    dx, dw = x.cuda(), w.cuda()
+    cl = torch.channels_last
+    cx, cwt = dx.contiguous(memory_format=cl), dw.contiguous(memory_format=cl)
+    y = api.conv2d(dx, dw, cw.stride, cw.pad, cw.dil, tile_oh=cw.tile_oh, out_dtype=cw.out_dtype)
+    yc = api.conv2d(cx, cwt, cw.stride, cw.pad, cw.dil, tile_oh=cw.tile_oh, out_dtype=cw.out_dtype)
+    ws = torch.empty(api.conv2d_workspace_size(cw.N, cw.C, cw.H, cw.W, cw.Co, cw.kh, cw.kw), dtype=torch.uint8,
+                     device="cuda")
+    for _ in range(launches):
+        api.conv2d(dx, dw, cw.stride, cw.pad, cw.dil, tile_oh=cw.tile_oh, out_dtype=cw.out_dtype, out=y,
+                   workspace=ws)
+    for _ in range(launches):
+        api.conv2d(cx, cwt, cw.stride, cw.pad, cw.dil, tile_oh=cw.tile_oh, out_dtype=cw.out_dtype, out=yc)
+    g = WORKLOADS[2]
+    A, B = g.make()
+    dA, dB = A.cuda(), B.cuda()
+    out = torch.empty((g.M, g.N), dtype=torch.float16, device="cuda")
+    for _ in range(launches):
+        api.gemm(dA, dB, out=out)
+    torch.cuda.synchronize()
+    print("conv and GEMM launches done", flush=True)
+
+
+# hardware counter passes of `run-conv` (each within one pass's counter limits)
+CONV_PASSES = [
+    "MfmaUtil LdsUtil",
+    "LdsLatency",
+    "VmemLatency",
+    "SQ_WAIT_INST_LDS SQ_WAIT_INST_ANY SQ_WAVE_CYCLES SQ_BUSY_CYCLES SQ_ACTIVE_INST_VMEM SQ_ACTIVE_INST_LDS "
+    "SQ_LDS_BANK_CONFLICT SQ_INSTS_MFMA",
+    "SQ_INSTS_LDS SQ_INSTS_VMEM SQ_INSTS_VALU SQ_INSTS_SALU SQ_WAVES SQ_LDS_DATA_FIFO_FULL SQ_LDS_CMD_FIFO_FULL "
+    "SQ_VMEM_TA_CMD_FIFO_FULL",
+]
+
+
+def summarize_conv(d: str) -> str:
+    """Per kernel of a `run-conv` run, the mean of every counter over its
+    dispatches (pass directories <d>/p1 ... <d>/pN, one per CONV_PASSES
+    entry).  A conv GEMM dispatch that follows a layout pass is the NCHW
+    call's; the others are the channel-last call's."""
+    vals = defaultdict(lambda: defaultdict(list))
+    for i in range(1, len(CONV_PASSES) + 1):
+        files = glob.glob(os.path.join(d, f"p{i}", "**", "*counter_collection.csv"), recursive=True)
+        if not files:
+            raise SystemExit(f"counter pass p{i} missing under {d}")
+        prev = ""
+        for _, name, c in per_dispatch_all(files[0]):
+            if "conv_layout" in name:
+                kind = "layout pass (NCHW call)"
+            elif "tiled_gemm_kernel" in name and "Lb1E" in name:
+                kind = "conv implicit GEMM, NCHW call" if "conv_layout" in prev else \
+                    "conv implicit GEMM, channel-last call"
+            elif "tiled_gemm_kernel" in name:
+                kind = "GEMM 4096^3"
+            else:
+                prev = name
+                continue
+            prev = name
+            for k, v in c.items():
+                vals[kind][k].append(v)
+    kinds = ["conv implicit GEMM, channel-last call", "conv implicit GEMM, NCHW call", "layout pass (NCHW call)",
+             "GEMM 4096^3"]
+    counters = sorted({k for kind in kinds for k in vals[kind]})
+    lines = ["| counter | " + " | ".join(kinds) + " |", "|---|" + "---|" * len(kinds)]
+    for k in counters:
+        lines.append(f"| {k} | " + " | ".join(f"{_mean(vals[kind][k]):.4g}" if vals[kind][k] else "—"
+                                               for kind in kinds) + " |")
+    per_mfma = []
+    for kind in kinds[:2] + kinds[3:]:
+        v = vals[kind]
+        if v["SQ_INSTS_MFMA"] and v["SQ_INSTS_LDS"]:
+            m = _mean(v["SQ_INSTS_MFMA"])
+            per_mfma.append(f"| {kind} | {_mean(v['SQ_INSTS_LDS']) / m:.3f} | {_mean(v['SQ_INSTS_VMEM']) / m:.3f} | "
+                            f"{_mean(v['SQ_WAIT_INST_ANY']) / _mean(v['SQ_WAVE_CYCLES']):.3f} |")
+    lines += ["", "| kernel | LDS instructions per MFMA | VMEM instructions per MFMA | "
+              "SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES |", "|---|---|---|---|"] + per_mfma
+    return "\n".join(lines) + "\n"
+
+
 def run_lds():
     """Every pattern of the LDS bank table, one launch each, in table order."""
     from . import api
@@ -261,6 +348,10 @@ def main():
     r = sub.add_parser("run")
     r.add_argument("--launches", type=int, default=5)
     sub.add_parser("run-lds")
+    rc = sub.add_parser("run-conv")
+    rc.add_argument("--launches", type=int, default=5)
+    sc = sub.add_parser("summarize-conv")
+    sc.add_argument("dir")
     s = sub.add_parser("summarize")
     s.add_argument("dir")
     s.add_argument("--trace", default=None)
@@ -279,6 +370,10 @@ def main():
         run(a.launches)
     elif a.cmd == "run-lds":
         run_lds()
+    elif a.cmd == "run-conv":
+        run_conv(a.launches)
+    elif a.cmd == "summarize-conv":
+        sys.stdout.write(summarize_conv(a.dir))
     elif a.cmd == "summarize-util":
         sys.stdout.write(summarize_util(a.dir))
     else:
