@@ -406,6 +406,31 @@ int64_t tss_conv2d_nhwc_workspace_size(int64_t N, int64_t C, int64_t H, int64_t 
                                        int64_t pw, int64_t dh, int64_t dw, int32_t splits);
 
 /*
+ * Measured choice of the tile (the Tiling page's autotuning: enumerate the
+ * candidates, time each on the device, keep the fastest), for shapes where
+ * the model's ranking alone falls short (short K loops, where one tile's
+ * 256- and 512-thread versions rank equal but do not run equal).  Takes the
+ * first `topk` candidates of tss_tile_plan's gfx950 ranking for this
+ * problem, times `iters` back-to-back launches of each on `stream` with HIP
+ * events, in two interleaved rounds over all candidates (after running the
+ * first candidate for at least 20 ms to bring the engine clock up; one
+ * untimed launch before each timing), and returns the candidate with the
+ * least time of its better round in *best (the better-ranked one of equal
+ * times) and that time per launch in *best_us (may be NULL).
+ * Arguments as tss_gemm; C receives the products of every candidate in
+ * turn (every candidate computes the same product; C holds the last one).
+ * Blocking: it synchronizes with the stream after each candidate.  The
+ * choice depends on the measurement (run-to-run noise can pick either of
+ * two tiles within a few percent of each other); pass it to tss_gemm as cfg.
+ * topk in [1, 1024], iters in [1, 100000].
+ * Errors: as tss_gemm, and TSS_E_ARG for topk or iters out of range or a
+ * NULL best.
+ */
+int32_t tss_gemm_autotune(int64_t M, int64_t N, int64_t K, int32_t dtype, const void *A,
+                          const void *B, void *C, int64_t batch, int32_t out_dtype, int32_t topk,
+                          int32_t iters, void *stream, tss_tile_config *best, float *best_us);
+
+/*
  * Split K: the same GEMM with its K loop cut into ranges computed by
  * separate blocks, for problems whose output tiles alone leave CUs idle (the
  * C4 "idle" warning of the tile_decision.py page: fewer tiles than CUs).

@@ -64,7 +64,7 @@ EXPORTS = ["tss_device_gfx950", "tss_device_pages", "tss_device_query", "tss_eva
            "tss_conv2d_workspace_size", "tss_kernel_available", "tss_kernel_usage_query", "tss_tile_plan_measured",
            "tss_lds_probe", "tss_gemm_default_config", "tss_status_string", "tss_instr_shape", "tss_gemm_splitk",
            "tss_gemm_splitk_workspace_size", "tss_conv2d_splitk", "tss_conv2d_splitk_workspace_size",
-           "tss_conv2d_nhwc", "tss_conv2d_nhwc_workspace_size",
+           "tss_conv2d_nhwc", "tss_conv2d_nhwc_workspace_size", "tss_gemm_autotune",
            "tss_splitk_plan", "tss_conv_splitk_plan", "tss_conv2d_splitk_noalloc"]
 
 _lib = None
@@ -105,6 +105,8 @@ def lib():
     L.tss_conv2d_splitk_workspace_size.argtypes = [i64] * 13 + [i32]
     L.tss_conv2d_nhwc.argtypes = [i64] * 16 + [i32, i32, vp, vp, vp, i32, vp, i64, P(TileConfig), vp]
     L.tss_conv2d_nhwc_workspace_size.argtypes = [i64] * 13 + [i32]
+    L.tss_gemm_autotune.argtypes = [i64, i64, i64, i32, vp, vp, vp, i64, i32, i32, i32, vp, P(TileConfig),
+                                     P(ctypes.c_float)]
     L.tss_conv2d_splitk_noalloc.argtypes = [i64] * 16 + [i32, i32, vp, vp, vp, i32, P(TileConfig), vp]
     L.tss_splitk_plan.argtypes = [i64, i64, i64, i64, i32, P(Device), P(Verdict), P(i32)]
     L.tss_conv_splitk_plan.argtypes = [i64, i64, i64, i64, i32, P(Device), P(Verdict), P(i32)]

@@ -256,14 +256,9 @@ def _same_device(*tensors):
     return dev
 
 
-def gemm(A, B, out_dtype: Optional[str] = None, cfg: Optional[TileConfig] = None, out=None, stream=None,
-         splits: int = 1, workspace=None):
-    """C = A @ B for row-major fp16/bf16 device tensors, A [b,] M x K and
-    B [b,] K x N; fp32 accumulation; out_dtype 'f32' or the input dtype
-    (default: the input dtype).  splits > 1: split K into at most that many
-    ranges (tss_gemm_splitk), 0: as many as the split-K plan says, with
-    `workspace` (a device tensor of at least gemm_splitk_workspace_size
-    bytes; allocated here when not given)."""
+def _check_gemm_operands(A, B):
+    """(batch, M, N, K, dtype) of row-major device operands A [b,] M x K and
+    B [b,] K x N, or ValueError."""
     if A.dim() not in (2, 3) or B.dim() != A.dim():
         raise ValueError("A and B must both be 2-D or both 3-D")
     if A.dtype != B.dtype:
@@ -276,14 +271,31 @@ def gemm(A, B, out_dtype: Optional[str] = None, cfg: Optional[TileConfig] = None
     K2, N = B.shape[-2], B.shape[-1]
     if K != K2 or (batched and B.shape[0] != bt):
         raise ValueError(f"shape mismatch {tuple(A.shape)} x {tuple(B.shape)}")
-    dt = _dt_of(A)
-    od = out_dtype or dt
-    shape = (bt, M, N) if batched else (M, N)
+    return bt, M, N, K, _dt_of(A)
+
+
+def _gemm_out(out, bt: int, M: int, N: int, od: str, A):
+    """The caller's output tensor (checked) or a new one, [b,] M x N of od."""
+    shape = (bt, M, N) if A.dim() == 3 else (M, N)
     tdt = {"f16": torch.float16, "bf16": torch.bfloat16, "f32": torch.float32}[od]
     if out is None:
-        out = torch.empty(shape, dtype=tdt, device=A.device)
-    elif tuple(out.shape) != shape or out.dtype != tdt or not out.is_contiguous():
+        return torch.empty(shape, dtype=tdt, device=A.device)
+    if tuple(out.shape) != shape or out.dtype != tdt or not out.is_contiguous():
         raise ValueError("out has the wrong shape, dtype or layout")
+    return out
+
+
+def gemm(A, B, out_dtype: Optional[str] = None, cfg: Optional[TileConfig] = None, out=None, stream=None,
+         splits: int = 1, workspace=None):
+    """C = A @ B for row-major fp16/bf16 device tensors, A [b,] M x K and
+    B [b,] K x N; fp32 accumulation; out_dtype 'f32' or the input dtype
+    (default: the input dtype).  splits > 1: split K into at most that many
+    ranges (tss_gemm_splitk), 0: as many as the split-K plan says, with
+    `workspace` (a device tensor of at least gemm_splitk_workspace_size
+    bytes; allocated here when not given)."""
+    bt, M, N, K, dt = _check_gemm_operands(A, B)
+    od = out_dtype or dt
+    out = _gemm_out(out, bt, M, N, od, A)
     if splits == 1:
         with torch.cuda.device(_same_device(A, B, out)):
             st = C.lib().tss_gemm(M, N, K, _DT[dt], A.data_ptr(), B.data_ptr(), out.data_ptr(), bt, _DT[od],
@@ -306,6 +318,23 @@ def gemm_splitk_workspace_size(batch: int, M: int, N: int, splits: int) -> int:
     if n < 0:
         C.check(int(n), "tss_gemm_splitk_workspace_size")
     return int(n)
+
+
+def autotune_gemm(A, B, out_dtype: Optional[str] = None, topk: int = 64, iters: int = 10, out=None,
+                  stream=None) -> Tuple[TileConfig, float]:
+    """tss_gemm_autotune: time the planner's first `topk` candidates on these
+    operands (blocking) and return (the fastest tile, its microseconds per
+    launch); pass the tile to gemm(..., cfg=...)."""
+    bt, M, N, K, dt = _check_gemm_operands(A, B)
+    od = out_dtype or dt
+    out = _gemm_out(out, bt, M, N, od, A)
+    best = C.TileConfig()
+    us = ctypes.c_float(0.0)
+    with torch.cuda.device(_same_device(A, B, out)):
+        st = C.lib().tss_gemm_autotune(M, N, K, _DT[dt], A.data_ptr(), B.data_ptr(), out.data_ptr(), bt, _DT[od],
+                                       topk, iters, _stream_ptr(stream), ctypes.byref(best), ctypes.byref(us))
+    C.check(st, "tss_gemm_autotune")
+    return TileConfig.from_c(best), float(us.value)
 
 
 def _workspace(workspace, need: int, device):

@@ -5,6 +5,8 @@ a hardware constraint, time every survivor on the device, keep the fastest).
     python -m tile_size_selection_amd.autotune --m 4096 --n 4096 --k 4096 [--out report.md]
     python -m tile_size_selection_amd.autotune --conv [--out report.md]     (the conv workload)
     python -m tile_size_selection_amd.autotune summarize report1.md report2.md ...   (one row per report)
+    python -m tile_size_selection_amd.autotune library [--topk 64] [--out report.md]   (tss_gemm_autotune's choice
+        against the full sweep on nine GEMM shapes)
 
 Prints, for every feasible configuration, its measured time and TFLOP/s, its
 rank in the planner's order, and how the planner's first choice compares with
@@ -147,9 +149,61 @@ def summarize(paths: List[str]) -> str:
     return "\n".join(rows) + "\n"
 
 
+LIBRARY_SHAPES = [(2048, 2048, 2048), (1024, 4096, 4096), (8192, 1024, 8192), (3000, 3000, 3000),
+                  (512, 512, 8192), (4096, 4096, 72), (2048, 8192, 136), (4096, 4096, 200), (4096, 4096, 4096)]
+
+
+def library_check(shapes, topk: int = 64, iters: int = 20) -> str:
+    """For each shape: the full measured sweep (every feasible tile, as
+    `sweep`), then the library's own measured choice (tss_gemm_autotune over
+    the planner's first `topk` candidates), re-timed the way the sweep times
+    every tile, against the sweep's fastest and against the model's plan.
+    Writes a markdown report."""
+    rows = []
+    for (M, N, K) in shapes:
+        srows, summ = sweep(M, N, K, iters=iters, warmup=3, rounds=2)
+        A = draw((M, K), "uniform", -1, 1, "f16", 2000).cuda()
+        B = draw((K, N), "uniform", -1, 1, "f16", 2001).cuda()
+        out = torch.empty((M, N), dtype=torch.float16, device="cuda")
+        torch.cuda.synchronize()
+        t0 = time.time()
+        cfg, us_lib = api.autotune_gemm(A, B, topk=topk, iters=iters, out=out)
+        wall = time.time() - t0
+        t_pick = min(time_config(A, B, out, cfg, iters, 3, "f16") for _ in range(2))
+        fastest = summ["fastest"]
+        key = lambda c: f"{c.bm}x{c.bn}x{c.bk} s{c.stages} t{c.threads} {c.instr}"
+        rank = next(r["rank"] for r in srows if r["config"] == cfg)
+        rows.append(f"| {M} x {N} x {K} | {key(cfg)} (planner rank {rank}) | {t_pick:.1f} | "
+                    f"{key(fastest['config'])} | {fastest['us']:.1f} | {t_pick / fastest['us']:.4f} | "
+                    f"{summ['planner_over_fastest']:.4f} | {wall * 1e3:.0f} |")
+        print(rows[-1], flush=True)
+    head = ("| M x N x K | library's measured choice | us | fastest of the full sweep | us | choice / fastest |"
+            " model plan / fastest | autotune wall ms |\n|---|---|---|---|---|---|---|---|\n")
+    return head + "\n".join(rows) + "\n"
+
+
 def main():
     if len(sys.argv) > 1 and sys.argv[1] == "summarize":
         sys.stdout.write(summarize(sys.argv[2:]))
+        return 0
+    if len(sys.argv) > 1 and sys.argv[1] == "library":
+        lp = argparse.ArgumentParser()
+        lp.add_argument("cmd")
+        lp.add_argument("--topk", type=int, default=64)
+        lp.add_argument("--iters", type=int, default=20)
+        lp.add_argument("--out", default=None)
+        la = lp.parse_args()
+        txt = ("# The library's measured tile choice (tss_gemm_autotune) against the full sweep\n\n"
+               "Command (repository root, MI355X): `python3 -m tile_size_selection_amd.autotune library"
+               + (f" --out {la.out}" if la.out else "") + "`\n\n"
+               f"Per shape (fp16, fp16 out): every feasible tile timed as `sweep` does ({la.iters} launches behind a"
+               " GPU spin, best of 2 rounds), then tss_gemm_autotune over the planner's first"
+               f" {la.topk} candidates ({la.iters} launches each, best of 2 interleaved rounds), its choice re-timed like"
+               " the sweep; model plan = the planner's first candidate.\n\n"
+               + library_check(LIBRARY_SHAPES, la.topk, la.iters))
+        if la.out:
+            with open(la.out, "w") as f:
+                f.write(txt)
         return 0
     ap = argparse.ArgumentParser()
     ap.add_argument("--m", type=int, default=4096)

@@ -326,6 +326,80 @@ int64_t tss_gemm_splitk_workspace_size(int64_t batch, int64_t M, int64_t N, int3
   return int64_t(bytes);
 }
 
+int32_t tss_gemm_autotune(int64_t M, int64_t N, int64_t K, int32_t dtype, const void *A, const void *B, void *C,
+                          int64_t batch, int32_t out_dtype, int32_t topk, int32_t iters, void *stream,
+                          tss_tile_config *best, float *best_us) {
+  if (!best || topk < 1 || topk > 1024 || iters < 1 || iters > 100000) return TSS_E_ARG;
+  std::vector<tss_verdict> list(static_cast<size_t>(topk));
+  int32_t n = 0;
+  int32_t st = tss_tile_plan(batch, M, N, K, 2, nullptr, 0, nullptr, list.data(), topk, &n);
+  if (st != TSS_OK) return st;
+  const int32_t cand = n < topk ? n : topk;
+  hipStream_t s = (hipStream_t)stream;
+  auto launch = [&](const tss_tile_config &c) {
+    return gemm_impl(M, N, K, dtype, A, B, C, batch, out_dtype, &c, 1, nullptr, 0, stream);
+  };
+  st = launch(list[0].cfg);  // also every argument check, before any event exists
+  if (st != TSS_OK) return st;
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  if (hipEventCreate(&e0) != hipSuccess) return TSS_E_HIP;
+  if (hipEventCreate(&e1) != hipSuccess) {
+    (void)hipEventDestroy(e0);
+    return TSS_E_HIP;
+  }
+  // time `reps` launches of c on the stream: microseconds per launch, or < 0 on an error
+  auto time_cfg = [&](const tss_tile_config &c, int32_t reps) -> float {
+    if (hipEventRecord(e0, s) != hipSuccess) return -1.f;
+    for (int32_t r = 0; r < reps; ++r)
+      if (launch(c) != TSS_OK) return -1.f;
+    float ms = 0.f;
+    if (hipEventRecord(e1, s) != hipSuccess || hipEventSynchronize(e1) != hipSuccess ||
+        hipEventElapsedTime(&ms, e0, e1) != hipSuccess)
+      return -1.f;
+    return ms * 1000.f / float(reps);
+  };
+  // bring the engine clock up first: the plan's first tile for at least 20 ms (at most 50 rounds)
+  float spent = 0.f;
+  for (int round = 0; round < 50 && spent < 20000.f; ++round) {
+    const float us = time_cfg(list[0].cfg, 20);
+    if (us < 0.f) {
+      st = TSS_E_HIP;
+      break;
+    }
+    spent += 20.f * us;
+    if (us == 0.f) break;  // nothing launched (M or N is 0)
+  }
+  // two interleaved rounds over the candidates, each candidate's best round
+  // (a drift of the clock or a slow round then favours no candidate)
+  std::vector<float> t(size_t(cand), -1.f);
+  for (int round = 0; round < 2 && st == TSS_OK; ++round)
+    for (int32_t i = 0; i < cand; ++i) {
+      if (launch(list[i].cfg) != TSS_OK) {  // one warm-up launch of this kernel
+        st = TSS_E_HIP;
+        break;
+      }
+      const float us = time_cfg(list[i].cfg, iters);
+      if (us < 0.f) {
+        st = TSS_E_HIP;
+        break;
+      }
+      if (t[i] < 0.f || us < t[i]) t[i] = us;
+    }
+  float best_t = 0.f;
+  int32_t best_i = -1;
+  for (int32_t i = 0; st == TSS_OK && i < cand; ++i)
+    if (best_i < 0 || t[i] < best_t) {  // the first of equal times: the better-ranked candidate
+      best_t = t[i];
+      best_i = i;
+    }
+  (void)hipEventDestroy(e0);
+  (void)hipEventDestroy(e1);
+  if (st != TSS_OK) return st;
+  *best = list[best_i].cfg;
+  if (best_us) *best_us = best_t;
+  return TSS_OK;
+}
+
 int32_t tss_gemm_splitk(int64_t M, int64_t N, int64_t K, int32_t dtype, const void *A, const void *B, void *C,
                         int64_t batch, int32_t out_dtype, const tss_tile_config *cfg, int32_t splits,
                         void *workspace, int64_t workspace_bytes, void *stream) {
