@@ -203,61 +203,90 @@ def _ceil_div(a: int, b: int) -> int:
 # ---------------------------------------------------------------------------
 
 
+def _c3_checks(cfg: TileConfig, dev: DeviceModel, elem_bytes: int) -> List[Tuple[str, str]]:
+    """C3, instruction-shape multiples: (failure code, message) for every
+    way the block fails to be a whole number of the intrinsic's tiles, of
+    its issuing group of threads, of the device's thread limit, and on gfx950
+    of a wave grid of whole MFMA tiles and of whole wave-wide copies."""
+    out = []
+    im, inn, ik, it = dev.shape(cfg.instr)
+    dims = (("C3_M", cfg.block_m, "block_M", im), ("C3_N", cfg.block_n, "block_N", inn),
+            ("C3_K", cfg.block_k, "block_K", ik))
+    out += [(code, f"C3 {name}={dim} is not a multiple of {mult} ({cfg.instr})")
+            for code, dim, name, mult in dims if dim % mult]
+    if cfg.threads % it:
+        out.append(("C3_THREADS", f"C3 threads={cfg.threads} is not a multiple of {it} ({cfg.instr})"))
+    if cfg.threads > dev.max_threads_per_block:
+        out.append(("C3_MAXTHREADS", f"C3 threads={cfg.threads} exceeds {dev.max_threads_per_block} per block"))
+    if dev.wave_grid_rule:
+        waves = cfg.threads // dev.lane_count if cfg.threads % dev.lane_count == 0 else 0
+        grid = WAVE_GRIDS.get(waves)
+        if grid is None or cfg.block_m % (grid[0] * im) or cfg.block_n % (grid[1] * inn):
+            out.append(("C3_WAVEGRID", f"C3 block ({cfg.block_m},{cfg.block_n}) does not split into whole"
+                                       f" {im}x{inn} tiles per wave for {cfg.threads // dev.lane_count} waves"))
+    if dev.load_bytes_per_lane:
+        # each wave copies the same whole number of wave-wide loads of each operand tile per stage
+        unit = dev.load_bytes_per_lane * dev.lane_count * max(cfg.threads // dev.lane_count, 1)
+        if (cfg.block_m * cfg.block_k * elem_bytes) % unit or (cfg.block_k * cfg.block_n * elem_bytes) % unit:
+            out.append(("C3_LOAD", f"C3 operand tiles are not whole {unit}-byte block loads"))
+    return out
+
+
+def _c1_bytes(cfg: TileConfig, elem_bytes: int) -> Tuple[int, int]:
+    """C1's on-chip footprint: one A tile (block_M x block_K) and one B tile
+    (block_K x block_N) per pipeline stage -> (bytes per stage, total)."""
+    per_stage = (cfg.block_m * cfg.block_k + cfg.block_k * cfg.block_n) * elem_bytes
+    return per_stage, per_stage * cfg.stages
+
+
+def _c2_registers(cfg: TileConfig, dev: DeviceModel, accum_bytes: int) -> Tuple[int, int]:
+    """C2's register model: the C tile's accumulators spread over the
+    block's threads, in 4-byte registers rounded up to the allocation
+    granule -> (accumulators per thread, accumulator registers per lane)."""
+    acc = _ceil_div(cfg.block_m * cfg.block_n, cfg.threads)
+    regs = _ceil_div(acc * accum_bytes // 4, dev.reg_granule_per_lane) * dev.reg_granule_per_lane
+    return acc, regs
+
+
+def _residency(v: Verdict, cfg: TileConfig, dev: DeviceModel) -> None:
+    """Resident blocks per SM/CU allowed by registers, on-chip memory and
+    threads, under the hardware block cap; the binding resource is the first
+    of (regs, smem, threads) attaining the least.  Fills v."""
+    if dev.reg_model == REG_POOLED:
+        v.blocks_by_regs = dev.regs_per_core // max(v.regs_per_block, 1)
+    else:
+        waves_per_simd = min(dev.max_waves_per_simd, dev.regs_per_lane_per_simd // v.regs_per_thread)
+        v.blocks_by_regs = (dev.simds_per_core * waves_per_simd) // max(_ceil_div(cfg.threads, dev.lane_count), 1)
+    v.blocks_by_smem = dev.onchip_per_core // max(v.smem_total, 1)
+    v.blocks_by_threads = dev.max_threads_per_core // max(cfg.threads, 1)
+    limits = (("regs", v.blocks_by_regs), ("smem", v.blocks_by_smem), ("threads", v.blocks_by_threads))
+    least = min(n for _, n in limits)
+    v.blocks_per_core = max(min(least, dev.max_blocks_per_core), 0)
+    if v.blocks_per_core > 0:
+        v.binding = next(name for name, n in limits if n == least)
+
+
 def evaluate(cfg: TileConfig, dev: DeviceModel, elem_bytes: int = 2, accum_bytes: int = 4,
              regs_measured: Optional[int] = None, spill_bytes: int = 0) -> Verdict:
-    """C3, C1, C2 and occupancy of one configuration.  regs_measured: the
-    registers per lane a compiled kernel of this configuration uses; given,
-    they replace the register estimate in the occupancy (rounded up to the
-    allocation granule).  spill_bytes > 0: that kernel spills to scratch,
-    which fails C2 -- the README page names the accumulator-only register
-    model a limitation, and C2's own message is the spill."""
+    """C3, C1, C2 and occupancy of one configuration, failures listed in
+    that order.  regs_measured: the registers per lane a compiled kernel of
+    this configuration uses; given, they replace the register estimate in
+    the occupancy (rounded up to the allocation granule).  spill_bytes > 0:
+    that kernel spills to scratch, which fails C2 -- the README page names
+    the accumulator-only register model a limitation, and C2's own message
+    is the spill."""
     v = Verdict(config=cfg)
-    bm, bn, bk, st, thr = cfg.block_m, cfg.block_n, cfg.block_k, cfg.stages, cfg.threads
+    for code, msg in _c3_checks(cfg, dev, elem_bytes):
+        v.failures.append(code)
+        v.messages.append(msg)
 
-    # C3 -- every block dimension is a whole number of intrinsic tiles, and the
-    # thread count a whole number of the intrinsic's issuing group.
-    im, inn, ik, it = dev.shape(cfg.instr)
-    for code, dim, name, mult in (("C3_M", bm, "block_M", im), ("C3_N", bn, "block_N", inn),
-                                  ("C3_K", bk, "block_K", ik)):
-        if dim % mult:
-            v.failures.append(code)
-            v.messages.append(f"C3 {name}={dim} is not a multiple of {mult} ({cfg.instr})")
-    if thr % it:
-        v.failures.append("C3_THREADS")
-        v.messages.append(f"C3 threads={thr} is not a multiple of {it} ({cfg.instr})")
-    if thr > dev.max_threads_per_block:
-        v.failures.append("C3_MAXTHREADS")
-        v.messages.append(f"C3 threads={thr} exceeds {dev.max_threads_per_block} per block")
-    if dev.wave_grid_rule:
-        waves = thr // dev.lane_count if thr % dev.lane_count == 0 else 0
-        grid = WAVE_GRIDS.get(waves)
-        if grid is None or bm % (grid[0] * im) or bn % (grid[1] * inn):
-            v.failures.append("C3_WAVEGRID")
-            v.messages.append(f"C3 block ({bm},{bn}) does not split into whole {im}x{inn} tiles"
-                              f" per wave for {thr // dev.lane_count} waves")
-    if dev.load_bytes_per_lane:
-        # every wave of the block copies the same whole number of wave-wide
-        # loads (load_bytes_per_lane per lane) of each operand tile per stage
-        waves = max(thr // dev.lane_count, 1)
-        unit = dev.load_bytes_per_lane * dev.lane_count * waves
-        if (bm * bk * elem_bytes) % unit or (bk * bn * elem_bytes) % unit:
-            v.failures.append("C3_LOAD")
-            v.messages.append(f"C3 operand tiles are not whole {unit}-byte block loads")
-
-    # C1 -- on-chip capacity: every pipeline stage holds one A tile (block_M x
-    # block_K) and one B tile (block_K x block_N).
-    v.smem_per_stage = (bm * bk + bk * bn) * elem_bytes
-    v.smem_total = v.smem_per_stage * st
+    v.smem_per_stage, v.smem_total = _c1_bytes(cfg, elem_bytes)
     if v.smem_total > dev.onchip_per_block_max:
         v.failures.append("C1")
         v.messages.append(f"C1 shared {v.smem_total} B > {dev.onchip_per_block_max} B per block"
-                          f" at stages={st}")
+                          f" at stages={cfg.stages}")
 
-    # C2 -- register pressure: the C tile's fp32 accumulators spread over the
-    # block's threads, rounded up to the allocation granule.
-    v.accum_per_thread = _ceil_div(bm * bn, thr)
-    raw = v.accum_per_thread * accum_bytes // 4
-    acc_regs = _ceil_div(raw, dev.reg_granule_per_lane) * dev.reg_granule_per_lane
+    v.accum_per_thread, acc_regs = _c2_registers(cfg, dev, accum_bytes)
     v.regs_per_thread = acc_regs + dev.reg_overhead
     if regs_measured:
         v.regs_per_thread = _ceil_div(regs_measured, dev.reg_granule_per_lane) * dev.reg_granule_per_lane
@@ -268,27 +297,12 @@ def evaluate(cfg: TileConfig, dev: DeviceModel, elem_bytes: int = 2, accum_bytes
     elif spill_bytes > 0:
         v.failures.append("C2")
         v.messages.append(f"C2 the compiled kernel spills {spill_bytes} bytes/thread to local memory")
-    v.regs_per_block = v.regs_per_thread * thr
+    v.regs_per_block = v.regs_per_thread * cfg.threads
 
-    # Occupancy: resident blocks per SM/CU allowed by registers, by on-chip
-    # memory and by threads, under the hardware block cap.
-    if dev.reg_model == REG_POOLED:
-        v.blocks_by_regs = dev.regs_per_core // max(v.regs_per_block, 1)
-    else:
-        waves_per_simd = min(dev.max_waves_per_simd, dev.regs_per_lane_per_simd // v.regs_per_thread)
-        v.blocks_by_regs = (dev.simds_per_core * waves_per_simd) // max(_ceil_div(thr, dev.lane_count), 1)
-    v.blocks_by_smem = dev.onchip_per_core // max(v.smem_total, 1)
-    v.blocks_by_threads = dev.max_threads_per_core // max(thr, 1)
-    v.blocks_per_core = max(min(v.blocks_by_regs, v.blocks_by_smem, v.blocks_by_threads,
-                                dev.max_blocks_per_core), 0)
+    _residency(v, cfg, dev)
     if v.blocks_per_core == 0:
         v.failures.append("OCC0")
         v.messages.append("C1/C2 no resident block fits: blocks_per_SM = 0")
-    else:
-        # the first of (regs, smem, threads) attaining the minimum
-        pairs = (("regs", v.blocks_by_regs), ("smem", v.blocks_by_smem), ("threads", v.blocks_by_threads))
-        least = min(p[1] for p in pairs)
-        v.binding = next(name for name, val in pairs if val == least)
     return v
 
 
