@@ -28,17 +28,19 @@
 // the buffer's range, so the hardware range check writes zeros into LDS; the
 // epilogue masks rows >= M and columns >= N.
 //
-// The same kernel computes a convolution as an implicit GEMM (CONV = true):
-// A is the weight matrix Cout x (kh*kw*Cp) with K ordered (r, s, ci), loaded
-// exactly as the GEMM's A; B is the im2col matrix of one output tile (images
-// x output rows x output columns), stored in LDS transposed (pixels x K, laid
-// out like A) and copied HBM -> LDS from a channel-last input, 16 bytes (8
-// channels of one input pixel) per lane.  The operands are either the
-// caller's channel-last tensors (NHWC input, OHWI weights) or copies of NCHW /
-// OIHW ones made by conv_layout.h.  The batch index of the GEMM is the tile.  Each block
+// The same kernel computes a convolution as an implicit GEMM (CONV = true).
+// A is the weight matrix Cout x (kh*kw*Cp) with K ordered (r, s, ci), each
+// tap's channels padded to Cp (a multiple of BK); it is loaded like the
+// GEMM's A, the columns of a K tile taken from the tap cursor.  B is the
+// im2col matrix of one output tile (images x output rows x output columns),
+// stored in LDS transposed (pixels x K, laid out like A) and copied
+// HBM -> LDS from a channel-last input, 16 bytes (8 channels of one input
+// pixel) per lane.  The operands are either the caller's channel-last
+// tensors (NHWC input, OHWI weights) or copies of NCHW / OIHW ones made by
+// conv_layout.h.  The batch index of the GEMM is the tile.  Each block
 // derives its input rows and columns and the sub-operator pads from the
-// Tiling page's H/W tiling formulas; chunks that fall in a pad or outside the
-// slice read as zero.
+// Tiling page's H/W tiling formulas; chunks that fall in a pad, outside the
+// slice or past the channels read as zero.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -61,10 +63,10 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 typedef __attribute__((address_space(3))) i16x8 lds_i16x8;
 
 struct KernelArgs {
-  const void *A;  // GEMM: A[batch][M][K].       conv: weights wr[Cout][kh][kw][Cp]
-  const void *B;  // GEMM: B[batch][K][N].       conv: input xc[Nb][H][W][Cp]
+  const void *A;  // GEMM: A[batch][M][K].       conv: weights w[Cout][kh][kw][Cs]
+  const void *B;  // GEMM: B[batch][K][N].       conv: input x[Nb][H][W][Cs] (channel-last)
   void *C;        // GEMM: C[batch][M][N].       conv: output y[Nb][Cout][OH][OW]
-  int32_t M, N, K;  // conv: M = Cout, K = kh*kw*Cp, N = pixels of a full tile
+  int32_t M, N, K;  // conv: M = Cout, K = kh*kw*Cp, N = pixels of a full tile; lda = kh*kw*Cs
   int32_t tiles_m, tiles_n;
   int32_t group_m;    // tile rows per group of the L2-friendly tile order
   int32_t out_dtype;  // TSS_F32 / TSS_F16 / TSS_BF16
