@@ -106,18 +106,27 @@ typedef struct {
        term off: the loop then costs its padded K alone.
      tile_cost_k: the fixed cost of one round of co-resident tiles on a CU
        (prologue, epilogue, output write), as a K-loop length of the same
-       tile.  0 turns it off.
+       tile.  gfx950 model: 900 (a round of a 256x256 tile weighs about 10
+       K steps of 64; at 4096^3 its prologue and epilogue take about 10 us
+       against 1.4 us per step, and the value is set above 824, where the
+       K = 200 sweep's 128x128 tiles, measured faster, overtake the 256x256
+       tile).  0 turns it off.
      Cost parameters of the split-K plan (tss_splitk_plan), in the same
      units (one streamed panel element):
      split_byte_cost: what one byte of the partial sums' extra traffic (each
        range's fp32 output written once and read once by the reduction)
        costs, as bytes of streamed panel; the partial sums of S ranges add
        8 * S * batch * M * N * split_byte_cost / (elem_bytes * cores).
-     launch_cost_k: the fixed cost of the reduction launch. */
+     launch_cost_k: the fixed cost of the reduction launch.
+     target_waves_per_simd: the occupancy the gfx950 ranking's tie-break
+       prefers among candidates of equal time, traffic, K step and resident
+       blocks: resident waves per SIMD closest to this first, then the most
+       (0: the most resident waves first).  gfx950 model: 4. */
   int32_t step_cost_k;
   int32_t tile_cost_k;
   int32_t split_byte_cost;
   int32_t launch_cost_k;
+  int32_t target_waves_per_simd;
 } tss_device;
 
 /* One tile configuration (block tile BM x BN, K step BK, pipeline stages,

@@ -68,6 +68,9 @@ class DeviceModel:
     # (see busiest_core_time); the pages' ranking does not use them
     step_cost_k: int = 0            # a K step's cost beyond its BK elements
     tile_cost_k: int = 0            # a round of co-resident tiles' fixed cost
+    # the gfx950 ranking's occupancy tie-break: resident waves per SIMD closest
+    # to this first (0: none, the most resident waves first)
+    target_waves_per_simd: int = 0
     # cost parameters of the split-K plan (see splitk_total)
     split_byte_cost: int = 0        # one byte of partial-sum traffic, in streamed panel bytes
     launch_cost_k: int = 0          # the reduction launch, in streamed panel elements
@@ -113,13 +116,19 @@ def device_pages(sm_count: int = 132, smem_kb: int = 228) -> DeviceModel:
 # (measured), not of the pages: a K step costs about 22 K elements beyond its
 # BK (with that fixed cost per step, the 32- and 16-wide steps take 1.24x and
 # 1.76x the 64-wide step's time per FLOP at equal K, as measured on the
-# convolution workload); a round of co-resident tiles costs about 600 K
+# convolution workload); a round of co-resident tiles costs about 900 K
 # elements more (the 4096^3 GEMM's prologue and epilogue, about 10 us, against
-# 1.41 us per 64-wide K step of 86 K elements' cost).  The functions below
-# take them from the device record, so any other values can be given through
-# dataclasses.replace.
+# 1.41 us per 64-wide K step of 86 K elements' cost, put the figure near 600;
+# 900 is the value above 824, the point past which the K = 200 GEMM's 128x128
+# tiles, measured faster there, rank ahead of the 256x256 tile).  Among
+# candidates the time, traffic, K step and residency rank equal, 4 resident
+# waves per SIMD is preferred (the 256-thread blocks that ran 8-16% faster
+# than their 512-thread twins on K loops of 2 to 4 steps).  The functions
+# below take these from the device record, so any other values can be given
+# through dataclasses.replace.
 GFX950_STEP_COST_K = 22
-GFX950_TILE_COST_K = 600
+GFX950_TILE_COST_K = 900
+GFX950_TARGET_WAVES_PER_SIMD = 4
 # Split K: each byte of the partial sums' extra traffic costs as much as 6
 # bytes of streamed panel, and the reduction launch as much as 67000 panel
 # elements; with these, the split count of the split-K plan measured within
@@ -144,6 +153,7 @@ def device_gfx950() -> DeviceModel:
         max_waves_per_simd=8, instr_shapes=GFX950_SHAPES,
         wave_grid_rule=True, load_bytes_per_lane=16, ranking="gfx950",
         step_cost_k=GFX950_STEP_COST_K, tile_cost_k=GFX950_TILE_COST_K,
+        target_waves_per_simd=GFX950_TARGET_WAVES_PER_SIMD,
         split_byte_cost=GFX950_SPLIT_BYTE_COST, launch_cost_k=GFX950_LAUNCH_COST_K, core_name="CU")
 
 
@@ -402,10 +412,11 @@ def rank_key(v: Verdict, dev: DeviceModel, k_loop: Optional[int] = None):
     gfx950: least time on the busiest CU (busiest_core_time: C0 per tile
     under C4's dealing of the grid over the cores), then least total traffic
     (C0); then, as the Tiling page's rules of thumb advise when on-chip memory
-    has room, the larger block_K; then most resident blocks and most resident
-    waves per CU (occupancy, that page's third constraint), counting only the
-    blocks the grid can supply (a CU never holds more than ceil(grid / cores)
-    blocks at once); then the deeper pipeline; then less LDS.
+    has room, the larger block_K; then most resident blocks per CU (occupancy,
+    that page's third constraint), counting only the blocks the grid can
+    supply (a CU never holds more than ceil(grid / cores) blocks at once);
+    then resident waves per SIMD nearest target_waves_per_simd, then the most
+    resident waves; then the deeper pipeline; then less LDS.
     """
     t = round_half_even(v.traffic)
     if dev.ranking == "pages":
@@ -413,7 +424,11 @@ def rank_key(v: Verdict, dev: DeviceModel, k_loop: Optional[int] = None):
     c = v.config
     usable = min(v.blocks_per_core, _ceil_div(v.grid, dev.cores))
     resident_waves = usable * (c.threads // dev.lane_count)
-    return (busiest_core_time(v, dev, k_loop), t, -c.block_k, -usable, -resident_waves, -c.stages, v.smem_total)
+    # distance from the target, kept in whole waves per CU:
+    # |waves / simds - target| * simds
+    off = abs(resident_waves - dev.simds_per_core * dev.target_waves_per_simd) if dev.target_waves_per_simd else 0
+    return (busiest_core_time(v, dev, k_loop), t, -c.block_k, -usable, off, -resident_waves, -c.stages,
+            v.smem_total)
 
 
 def candidates(dev: DeviceModel, k: int, instrs: Sequence[str]):

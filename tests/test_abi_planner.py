@@ -337,18 +337,18 @@ def test_conv_default_config_is_the_conv_plan():
         tss.conv_plan(64, 100, 0, 9)
 
 
-def _with_costs(step, tile):
+def _with_costs(step, tile, target=4):
     d = tss.device_gfx950()
-    d.step_cost_k, d.tile_cost_k = step, tile
-    return d, OP.replace(OP.device_gfx950(), step_cost_k=step, tile_cost_k=tile)
+    d.step_cost_k, d.tile_cost_k, d.target_waves_per_simd = step, tile, target
+    return d, OP.replace(OP.device_gfx950(), step_cost_k=step, tile_cost_k=tile, target_waves_per_simd=target)
 
 
-@pytest.mark.parametrize("step,tile", [(0, 0), (22, 0), (10, 300), (40, 2000)])
-def test_ranking_cost_parameters_bit_exact(step, tile):
-    """The gfx950 ranking's cost parameters come from the device record on
-    both sides: with any values, the C++ plans equal the oracle's, GEMM and
-    convolution, every verdict in rank order."""
-    cd, od = _with_costs(step, tile)
+@pytest.mark.parametrize("step,tile,target", [(0, 0, 0), (22, 0, 4), (10, 300, 2), (40, 2000, 8), (22, 900, 0)])
+def test_ranking_cost_parameters_bit_exact(step, tile, target):
+    """The gfx950 ranking's cost parameters and waves target come from the
+    device record on both sides: with any values, the C++ plans equal the
+    oracle's, GEMM and convolution, every verdict in rank order."""
+    cd, od = _with_costs(step, tile, target)
     ins = [s for s, _ in od.instr_shapes]
     for (b, M, N, K) in [(1, 4096, 4096, 4096), (1, 4096, 4096, 72), (1, 2048, 8192, 136), (4, 3000, 5000, 2048),
                          (1, 256, 256, 256), (1, 8192, 1024, 8192)]:
@@ -398,6 +398,9 @@ def test_planner_at_the_edge_of_its_size_bounds():
     assert L.tss_conv_plan(1 << 31, (1 << 31) + 1, 64, 9, 2, None, ctypes.byref(v), None, 0, None) == C.TSS_E_ARG
     d = tss.device_gfx950()
     d.step_cost_k = -1
+    assert L.tss_tile_plan(1, 64, 64, 64, 2, ctypes.byref(d), 0, ctypes.byref(v), None, 0, None) == C.TSS_E_ARG
+    d = tss.device_gfx950()
+    d.target_waves_per_simd = -1
     assert L.tss_tile_plan(1, 64, 64, 64, 2, ctypes.byref(d), 0, ctypes.byref(v), None, 0, None) == C.TSS_E_ARG
     pages = tss.device_pages()
     assert L.tss_conv_plan(64, 64, 64, 9, 2, ctypes.byref(pages), ctypes.byref(v), None, 0, None) == C.TSS_E_ARG

@@ -208,12 +208,45 @@ def test_gfx950_rank_prefers_occupancy_then_bigger_k_step():
     res = P.sweep(4096, 4096, 4096, g, [s for s, _ in g.instr_shapes])
     c = res[0].config
     assert (c.block_m, c.block_n, c.block_k, c.stages, c.threads, c.instr) == (256, 256, 64, 2, 512, "mfma16")
-    # one tile per CU, 256 + 256 panel rows, 64 K steps of 64 + 22, one round of 600
-    assert (g.step_cost_k, g.tile_cost_k) == (22, 600)
-    assert P.rank_key(res[0], g)[:1] == (1 * 512 * 64 * (64 + 22) + 1 * 512 * 600,) == (3125248,)
-    assert P.rank_key(res[0], g)[4] == -8
+    # one tile per CU, 256 + 256 panel rows, 64 K steps of 64 + 22, one round of 900
+    assert (g.step_cost_k, g.tile_cost_k, g.target_waves_per_simd) == (22, 900, 4)
+    assert P.rank_key(res[0], g)[:1] == (1 * 512 * 64 * (64 + 22) + 1 * 512 * 900,) == (3278848,)
+    # 8 resident waves on 4 SIMDs: 2 per SIMD, 2 below the target of 4 -> 8 waves off
+    assert P.rank_key(res[0], g)[4:6] == (8, -8)
     d = res[1].config    # the 32x32x16 twin ties on every key and follows it
     assert (d.block_m, d.block_n, d.block_k, d.stages, d.threads, d.instr) == (256, 256, 64, 2, 512, "mfma32")
+
+
+def test_gfx950_round_cost_crossover_and_waves_target():
+    """K = 200 on 4096 x 4096, worked by hand.  256x256x64 (512 threads):
+    256 tiles, one per CU, 4 steps of 64 + 22 over 512 panel rows, one round:
+    T = 512 * 4 * 86 + 512 * f.  128x128x32 (256 threads): 1024 tiles, W = 4,
+    all resident (LDS 32 KiB -> 5 blocks), 7 steps of 32 + 22 over 256 rows,
+    one round: T = 4 * 256 * 7 * 54 + 256 * f.  They cross at
+    256 * f = 387072 - 176128, f = 824.  Its 512-thread twin has the same T
+    and residency (4 blocks of 8 waves: 8 per SIMD) and is 16 waves off a
+    target of 4 per SIMD against 0: the target decides; without it the twin's
+    32 waves win."""
+    g = P.device_gfx950()
+    ins = [s for s, _ in g.instr_shapes]
+
+    def time_of(dev, bm, bn, bk, thr):
+        res = {v.config: v for v in P.sweep(4096, 4096, 200, dev, ins)}
+        return P.rank_key(res[P.TileConfig(bm, bn, bk, 2, thr, "mfma16")], dev)
+
+    for f in (823, 824, 825, 900):
+        d = P.replace(g, tile_cost_k=f)
+        big, small = time_of(d, 256, 256, 64, 512)[0], time_of(d, 128, 128, 32, 256)[0]
+        assert (big, small) == (176128 + 512 * f, 387072 + 256 * f)
+        assert (big < small, big == small) == (f < 824, f == 824)
+    first = P.sweep(4096, 4096, 200, g, ins)[0].config
+    assert (first.block_m, first.block_n, first.block_k, first.threads) == (128, 128, 32, 256)
+    k256, k512 = time_of(g, 128, 128, 32, 256), time_of(g, 128, 128, 32, 512)
+    assert k256[:4] == k512[:4] == (617472, k256[1], -32, -4)
+    assert (k256[4:6], k512[4:6]) == ((0, -16), (16, -32))
+    g0 = P.replace(g, target_waves_per_simd=0)
+    first0 = P.sweep(4096, 4096, 200, g0, ins)[0].config
+    assert (first0.block_m, first0.block_n, first0.block_k, first0.threads) == (128, 128, 32, 512)
 
 
 def test_gfx950_busiest_core_time_closed_forms():
@@ -262,9 +295,9 @@ def test_gfx950_conv_and_small_shape_choices():
     # one block at most, so the LDS room for 3 blocks of a 2-stage ring buys nothing and the 4-stage ring wins
     assert (c.block_m, c.block_n, c.block_k, c.stages, c.threads, c.instr) == (128, 64, 64, 4, 512, "mfma16")
     v = P.sweep(256, 6272, 2304, g, ins)[0]
-    assert v.blocks_per_core == 1 and P.rank_key(v, g)[3:6] == (-1, -8, -4)
+    assert v.blocks_per_core == 1 and P.rank_key(v, g)[3:7] == (-1, 8, -8, -4)
     two = P.finish_parallelism(P.evaluate(P.TileConfig(128, 64, 64, 2, 512, "mfma16"), g), 256, 6272, g)
-    assert two.blocks_per_core == 3 and P.rank_key(two, g)[3:6] == (-1, -8, -2)   # 3 resident, 1 usable
+    assert two.blocks_per_core == 3 and P.rank_key(two, g)[3:7] == (-1, 8, -8, -2)   # 3 resident, 1 usable
     c = P.sweep(256, 256, 256, g, ins)[0].config
     assert (c.block_m, c.block_n) == (64, 64)     # 16 tiles over 16 CUs beat one 256x256 tile
     c = P.sweep(3000, 5000, 2048, g, ins, batch=4)[0].config

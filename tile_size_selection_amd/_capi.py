@@ -30,7 +30,8 @@ class Device(ctypes.Structure):
         "cores", "onchip_per_core", "onchip_per_block_max", "max_threads_per_core", "max_threads_per_block",
         "max_blocks_per_core", "lane_count", "reg_granule_per_lane", "acc_regs_max", "reg_overhead", "reg_model",
         "regs_per_core", "simds_per_core", "regs_per_lane_per_simd", "max_waves_per_simd", "wave_grid_rule",
-        "load_bytes_per_lane", "ranking", "step_cost_k", "tile_cost_k", "split_byte_cost", "launch_cost_k")]
+        "load_bytes_per_lane", "ranking", "step_cost_k", "tile_cost_k", "split_byte_cost", "launch_cost_k",
+        "target_waves_per_simd")]
 
 
 class TileConfig(ctypes.Structure):

@@ -13,18 +13,24 @@ namespace {
 //  step_cost_k 22: with a fixed cost of 22 K elements per K step, the 32-
 //    and 16-wide steps take 1.24x and 1.76x the 64-wide step's time per
 //    FLOP at equal K (measured on the convolution workload);
-//  tile_cost_k 600: the 4096^3 GEMM's prologue and epilogue take about
+//  tile_cost_k 900: the 4096^3 GEMM's prologue and epilogue take about
 //    10 us of one round against 1.41 us per 64-wide K step (86 K elements
-//    of cost), i.e. about 7 steps, 600 K elements;
+//    of cost), about 7 steps or 600 K elements; 900 is past 824, where the
+//    K = 200 GEMM's 128x128 tiles (measured faster there) overtake the
+//    256x256 tile;
+//  target_waves_per_simd 4: among tiles equal in time, traffic, K step and
+//    resident blocks, 256-thread blocks at 4 waves per SIMD ran 8-16%
+//    faster than their 512-thread twins on K loops of 2 to 4 steps;
 //  split_byte_cost 6, launch_cost_k 67000: the split-K plan's costs, with
 //    which its split count measured within 5% of the fastest on nine GEMM
 //    shapes (2 us of reduction launch at the rate the time term converts at).
 tss_device gfx950_with_costs() {
   tss_device d = gfx950_device();
   d.step_cost_k = 22;
-  d.tile_cost_k = 600;
+  d.tile_cost_k = 900;
   d.split_byte_cost = 6;
   d.launch_cost_k = 67000;
+  d.target_waves_per_simd = 4;
   return d;
 }
 
@@ -32,7 +38,7 @@ bool valid_device(const tss_device &d) {
   if (d.cores <= 0 || d.onchip_per_core <= 0 || d.onchip_per_block_max <= 0 || d.max_threads_per_core <= 0 ||
       d.max_threads_per_block <= 0 || d.max_blocks_per_core <= 0 || d.lane_count <= 0 ||
       d.reg_granule_per_lane <= 0 || d.acc_regs_max <= 0 || d.reg_overhead < 0 || d.step_cost_k < 0 ||
-      d.tile_cost_k < 0 || d.split_byte_cost < 0 || d.launch_cost_k < 0)
+      d.tile_cost_k < 0 || d.split_byte_cost < 0 || d.launch_cost_k < 0 || d.target_waves_per_simd < 0)
     return false;
   if (d.reg_model == TSS_REG_POOLED) return d.regs_per_core > 0;
   if (d.reg_model == TSS_REG_PER_SIMD)

@@ -97,6 +97,7 @@ constexpr tss_device pages_device(int32_t sm_count, int32_t smem_kb) {
   d.tile_cost_k = 0;
   d.split_byte_cost = 0;
   d.launch_cost_k = 0;
+  d.target_waves_per_simd = 0;
   return d;
 }
 
@@ -284,7 +285,7 @@ constexpr Space space_for(const tss_device &d, int32_t instr_filter) {
 // traffic and time terms of problems near the accepted bounds exceed 64 bits.
 using i128 = __int128;
 struct Key {
-  i128 k[7];
+  i128 k[8];
 };
 
 // The gfx950 time term of a candidate whose K loop runs over K elements
@@ -321,19 +322,23 @@ constexpr Key rank_key(const tss_verdict &v, const tss_device &d, int64_t K_loop
     r.k[2] = v.smem_total;
   } else {
     // the busiest CU's time (above); then total C0, larger BK, most resident
-    // blocks, most resident waves, deeper pipeline, less LDS.  Residency
-    // counts only the blocks the grid can supply: with ceil(grid / CUs) waves
-    // of tiles no CU ever holds more than that many blocks at once, whatever
-    // its capacity.
+    // blocks; resident waves per SIMD closest to target_waves_per_simd (in
+    // whole waves per CU: |u * waves - SIMDs * target|), then the most
+    // resident waves; deeper pipeline, less LDS.  Residency counts only the
+    // blocks the grid can supply: with ceil(grid / CUs) waves of tiles no CU
+    // ever holds more than that many blocks at once, whatever its capacity.
     const int64_t W = cdiv(v.grid, d.cores);
     const int64_t usable = v.blocks_per_core < W ? v.blocks_per_core : W;
+    const int64_t waves = usable * (v.cfg.threads / d.lane_count);
+    const int64_t off = waves - int64_t(d.simds_per_core) * d.target_waves_per_simd;
     r.k[0] = busiest_core_time(v, d, K_loop);
     r.k[1] = t;
     r.k[2] = -v.cfg.bk;
     r.k[3] = -usable;
-    r.k[4] = -usable * (v.cfg.threads / d.lane_count);
-    r.k[5] = -v.cfg.stages;
-    r.k[6] = v.smem_total;
+    r.k[4] = d.target_waves_per_simd > 0 ? (off < 0 ? -off : off) : 0;
+    r.k[5] = -waves;
+    r.k[6] = -v.cfg.stages;
+    r.k[7] = v.smem_total;
   }
   return r;
 }
@@ -363,7 +368,7 @@ constexpr i128 split_total(i128 T_S, int64_t S, int64_t batch, int64_t M, int64_
 }
 
 constexpr bool key_less(const Key &a, const Key &b) {
-  for (int i = 0; i < 7; ++i) {
+  for (int i = 0; i < 8; ++i) {
     if (a.k[i] != b.k[i]) return a.k[i] < b.k[i];
   }
   return false;
