@@ -90,18 +90,20 @@ def test_split_count_within_10pct_of_the_fastest(shape):
 
 # GEMMs with a K loop of 2 to 4 steps of 64: the tile's prologue, epilogue and
 # output write weigh most, and the round cost and the waves target decide.
-SHORT_K = [(4096, 4096, 72), (2048, 8192, 136), (4096, 4096, 200)]
+# (M, N, K, bound on planner / fastest).  Full sweeps measured the plan at
+# 1.03, 1.00 and 1.09 of the fastest tile on these shapes (128x256 tiles lead
+# at K = 200, where the time term ranks them behind 128x128); the bounds leave
+# room for timing noise.
+SHORT_K = [(4096, 4096, 72, 1.10), (2048, 8192, 136, 1.10), (4096, 4096, 200, 1.20)]
 
 
-@pytest.mark.parametrize("shape", SHORT_K, ids=[f"{m}x{n}x{k}" for m, n, k in SHORT_K])
-def test_short_k_tile_choice_within_15pct_of_the_fastest(shape):
+@pytest.mark.parametrize("shape", SHORT_K, ids=[f"{m}x{n}x{k}" for m, n, k, _ in SHORT_K])
+def test_short_k_tile_choice_near_the_fastest(shape):
     """The GEMM plan's tile against every feasible tile of the candidate
     space (fp16, fp16 out), on K loops of a few steps: each tile's better
     of two interleaved rounds, after 200 ms of launches that bring the clocks
-    up.  Full sweeps measured the plan at 1.03, 1.00 and 1.09 of the fastest
-    tile on these shapes (128x256 tiles lead at K = 200, where the time term
-    ranks them behind 128x128); the bound leaves room for timing noise."""
-    M, N, K = shape
+    up."""
+    M, N, K, bound = shape
     A = draw((M, K), "uniform", -1, 1, "f16", 91).to(CUDA)
     B = draw((K, N), "uniform", -1, 1, "f16", 92).to(CUDA)
     out = torch.empty((M, N), dtype=torch.float16, device=CUDA)
@@ -126,4 +128,4 @@ def test_short_k_tile_choice_within_15pct_of_the_fastest(shape):
     fastest = min(times, key=times.get)
     print(f"{M}x{N}x{K}: chosen {chosen} {times[chosen]:.2f} us; fastest {fastest} {times[fastest]:.2f} us "
           f"(ratio {times[chosen] / times[fastest]:.3f})", flush=True)
-    assert times[chosen] <= 1.15 * times[fastest]
+    assert times[chosen] <= bound * times[fastest]
