@@ -204,8 +204,10 @@ int32_t tss_evaluate(const tss_tile_config *cfg, const tss_device *dev, int64_t 
  *   gfx950 model: BM, BN in {256, 128, 64} (largest first), BK in
  *                 {16, 32, 64}, stages 2..4, threads {128, 256, 512}, both
  *                 MFMA shapes, 16x16x32 first (or the one in instr_filter);
- *                 key (T, round(traffic), -BK, -u, -u * waves/block,
- *                 -stages, LDS bytes).  T is the busiest CU's time in units
+ *                 key (T, round(traffic), -BK, -u,
+ *                 |u * waves/block - SIMDs * dev->target_waves_per_simd|
+ *                 (0 when the target is 0), -u * waves/block, -stages, LDS
+ *                 bytes).  T is the busiest CU's time in units
  *                 of streamed panel elements: with W = ceil(grid / CUs)
  *                 tiles on that CU, u = min(blocks/CU, W) of them resident
  *                 at once (R = ceil(W / u) rounds) and n = ceil(K / BK) K
