@@ -175,8 +175,9 @@ def main():
     x, wt = cw.make()
     dx, dwt = x.to("cuda:0"), wt.to("cuda:0")
     y = tss.conv2d(dx, dwt, cw.stride, cw.pad, cw.dil, tile_oh=cw.tile_oh, out_dtype=cw.out_dtype)
-    ws = torch.empty(tss.conv2d_workspace_size(cw.N, cw.C, cw.H, cw.W, cw.Co, cw.kh, cw.kw), dtype=torch.uint8,
-                     device="cuda:0")
+    # room for two sets of the operand copies: consecutive calls alternate between them
+    ws_set = (tss.conv2d_workspace_size(cw.N, cw.C, cw.H, cw.W, cw.Co, cw.kh, cw.kw) + 255) // 256 * 256
+    ws = torch.empty(2 * ws_set, dtype=torch.uint8, device="cuda:0")
 
     def launch_conv():
         tss.conv2d(dx, dwt, cw.stride, cw.pad, cw.dil, tile_oh=cw.tile_oh, out_dtype=cw.out_dtype, out=y,

@@ -135,6 +135,28 @@ def test_conv_low_precision_output():
     check_bound(to_f64(y), ref, S, "conv f16 out")
 
 
+def test_conv_two_operand_sets_alternate_exact():
+    """A workspace with room for two sets of the operand copies: consecutive
+    calls alternate between the sets (one call writes the set the previous
+    call's GEMM did not read).  Five calls in a row on two problems, one pass
+    and split K (two sets, then the partial outputs after both): every
+    output exact, whichever set a call took."""
+    shapes = ((2, 16, 13, 11, 24, 3, 3), (1, 8, 9, 9, 16, 3, 3))
+    set_bytes = max((tss.conv2d_workspace_size(*sh) + 255) // 256 * 256 for sh in shapes)
+    part = 4 * 2 * 24 * 7 * 11 * 4                       # 4 ranges of the first problem's fp32 output
+    ws = torch.empty(2 * set_bytes + part, dtype=torch.uint8, device=CUDA)
+    for call in range(5):
+        N, Ci, H, W, Co, kh, kw = shapes[call % 2]
+        x = draw((N, Ci, H, W), "int", -2, 2, "f16", 90 + call)
+        w = draw((Co, Ci, kh, kw), "int", -2, 2, "f16", 95 + call)
+        ref, _ = G.conv2d(x.double().numpy(), w.double().numpy(), (2, 1), (1, 1), (1, 1))
+        for splits in (1, 4):
+            y = tss.conv2d(x.to(CUDA), w.to(CUDA), (2, 1), (1, 1), 1, tile_oh=2, out_dtype="f32", workspace=ws,
+                           splits=splits)
+            torch.cuda.synchronize()
+            assert np.array_equal(to_f64(y), ref), (call, splits)
+
+
 def test_conv_workspace_reuse_and_errors():
     """A caller-owned workspace serves calls of different sizes in a row on
     one stream; a workspace below tss_conv2d_workspace_size is rejected

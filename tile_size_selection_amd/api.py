@@ -400,7 +400,9 @@ def conv2d(x, w, stride: Union[int, Sequence[int]] = 1, padding: Union[int, Sequ
       layout "nchw": contiguous x, w and result (tss_conv2d_tiled; the
         operands are first rewritten into channel-last copies in
         `workspace`, an optional device tensor of at least
-        conv2d_workspace_size(...) bytes, allocated here when not given);
+        conv2d_workspace_size(...) bytes, allocated here when not given;
+        with twice that, consecutive calls alternate between two sets of the
+        operand copies, which runs the layout pass faster);
       layout "nhwc": x, w and the result in torch's channels_last format
         (stored [N][H][W][C], [Cout][kh][kw][C], [N][OH][OW][Cout]), read and
         written in place (tss_conv2d_nhwc; C a multiple of 8; the workspace
@@ -462,7 +464,11 @@ def conv2d(x, w, stride: Union[int, Sequence[int]] = 1, padding: Union[int, Sequ
         if ws_bytes < 0:
             C.check(int(ws_bytes), "tss_conv2d_splitk_workspace_size")
     # torch's caching allocator when none is given: device memory only, no
-    # host copy; the convolution's launches fill and read it on one stream
+    # host copy; the convolution's launches fill and read it on one stream.
+    # Allocated here, it has room for a second set of the operand copies, so
+    # that consecutive calls alternate between the two (tss_conv2d).
+    if workspace is None:
+        ws_bytes += (conv2d_workspace_size(N, Ci, H, W, Co, kh, kw) + 255) // 256 * 256
     workspace = _workspace(workspace, ws_bytes, x.device)
     with torch.cuda.device(_same_device(x, w, out, workspace)):
         args = (N, Ci, H, W, Co, kh, kw, sh, sw, ph, pw, dh, dw, tile_n or N, tile_oh or OH, tile_ow or OW, _DT[dt],

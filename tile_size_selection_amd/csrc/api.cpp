@@ -3,6 +3,7 @@
 // memory.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstring>
 #include <map>
 #include <mutex>
@@ -417,10 +418,18 @@ int64_t tss_conv2d_workspace_size(int64_t N, int64_t C, int64_t H, int64_t W, in
 
 }  // extern "C"
 
+// Consecutive NCHW calls whose workspace holds two sets of operand copies
+// alternate between them: the layout pass then writes the set the previous
+// call's GEMM did not read (rewriting lines a kernel has just read made the
+// pass ~40% slower on MI355X).  Any order of calls is correct; the counter only
+// picks the set.
+static std::atomic<uint32_t> g_layout_flip{0};
+
 // tss_conv2d_tiled, tss_conv2d_splitk, tss_conv2d_nhwc: splits == 1 is the
 // one-pass implicit GEMM.  NCHW (nhwc false): the workspace holds the operand
-// layout copies (sized for any tile), then at a 256-byte boundary the K
-// ranges' fp32 partial outputs.  NHWC (nhwc true): x is [N][H][W][C], w is
+// layout copies (sized for any tile; a second set at the next 256-byte
+// boundary when the workspace has room for both and the partial outputs),
+// then at a 256-byte boundary the K ranges' fp32 partial outputs.  NHWC (nhwc true): x is [N][H][W][C], w is
 // [Cout][kh][kw][C] and y is [N][OH][OW][Cout]; the implicit GEMM reads x and
 // w in place (C a multiple of 8; the channels past C up to the K step's
 // multiple read as zero) and the workspace holds only the partial outputs.
@@ -488,10 +497,11 @@ static int32_t conv_impl(int64_t N, int64_t C, int64_t H, int64_t W, int64_t Cou
   const int64_t Cs = nhwc ? C : ws.Cp;      // channels per pixel (and per tap of a weight row) in memory
   const SplitK sk = split_k(Kc, splits, c.bk);
   const int64_t out_elems = N * Cout * OH * OW;
-  const int64_t part_offset = (layout_bytes + 255) / 256 * 256;
-  if (sk.n > 1 && (!workspace || (unsigned __int128)workspace_bytes <
-                                     (unsigned __int128)part_offset +
-                                         (unsigned __int128)sk.n * uint64_t(out_elems) * 4u))
+  const int64_t set_bytes = (layout_bytes + 255) / 256 * 256;  // one set of operand copies
+  const unsigned __int128 part_bytes = sk.n > 1 ? (unsigned __int128)sk.n * uint64_t(out_elems) * 4u : 0;
+  const bool two_sets = layout_bytes > 0 && (unsigned __int128)workspace_bytes >= 2 * (unsigned __int128)set_bytes + part_bytes;
+  const int64_t part_offset = two_sets ? 2 * set_bytes : set_bytes;
+  if (sk.n > 1 && (!workspace || (unsigned __int128)workspace_bytes < (unsigned __int128)part_offset + part_bytes))
     return TSS_E_ARG;
   float *partials = sk.n > 1 ? reinterpret_cast<float *>(static_cast<char *>(workspace) + part_offset) : nullptr;
 
@@ -499,8 +509,10 @@ static int32_t conv_impl(int64_t N, int64_t C, int64_t H, int64_t W, int64_t Cou
   const void *opA = w, *opB = x;
   if (!nhwc) {
     // 1. operands in (r, s, ci) order: channel-last input, reordered weights
-    uint16_t *xc = static_cast<uint16_t *>(workspace);
-    uint16_t *wr = reinterpret_cast<uint16_t *>(static_cast<char *>(workspace) + ws.wr_offset);
+    char *set = static_cast<char *>(workspace);
+    if (two_sets && (g_layout_flip.fetch_add(1, std::memory_order_relaxed) & 1u)) set += set_bytes;
+    uint16_t *xc = reinterpret_cast<uint16_t *>(set);
+    uint16_t *wr = reinterpret_cast<uint16_t *>(set + ws.wr_offset);
     LayoutArgs la{};
     la.x = static_cast<const uint16_t *>(x);
     la.xc = xc;
