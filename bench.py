@@ -233,7 +233,8 @@ def main():
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_F16_TFLOPS, 4),
                      "traffic": profiled_traffic(cfg_str)},
         "conv": {"workload": "conv_f16_n8c256h56_k3s2p1 (tileOh 8, fp32 out), NCHW x / OIHW w / NCHW y: "
-                             "layout pass + implicit GEMM", "us": round(conv_us, 2),
+                             "layout pass + implicit GEMM (a workspace of two operand sets, which consecutive calls alternate)",
+                             "us": round(conv_us, 2),
                  "tflops": round(conv_flops / (conv_us * 1e-6) / 1e12, 2),
                  "tile": f"{conv_cfg.bm}x{conv_cfg.bn}x{conv_cfg.bk}/s{conv_cfg.stages}/t{conv_cfg.threads}/"
                          f"{conv_cfg.instr}"},
